@@ -1,0 +1,219 @@
+"""Benchmark of the fused 8-bit AdamW step with a stochastically rounded bf16 write.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload gptneo-6.7b]
+
+One step = one opt8_adamw_step call over the whole parameter list (every
+tensor: dequantise, AdamW in fp32, stochastic bf16 param write, block absmax,
+requantise).  Inputs are synthetic and already resident in HBM when the timed
+region starts; a small pool of gradient sets gives each step fresh gradients
+without generating them inside the timed region.  Prints ONE JSON line.
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published peak
+METRIC = "Gparams/s per optimizer step and % of HBM peak BW, 1 MI355X"
+BLOCK = 2048
+STATE_BYTES = {0: 1, 1: 2, 2: 4}
+
+
+def algorithmic_bytes(mode: int, n: int) -> int:
+    """Bytes each element's step must move once: read grad, param, state; write param, state."""
+    if mode == 0:   # 8-bit: 2+2+1+1 in, 2+1+1 out, plus absmax r/w (2 x 4 B in, 2 x 4 B out) per block
+        return 10 * n + 16 * ((n + BLOCK - 1) // BLOCK)
+    if mode == 1:   # bf16 state: g 2 + p 2+2 + m, v 2+2 in / 2+2 out
+        return 14 * n
+    return 22 * n   # fp32 state: g 2 + p 2+2 + m, v 4+4 in / 4+4 out
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="gptneo-6.7b")
+    ap.add_argument("--grad-pool", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-elems", type=int, default=8 * 1024 * 1024)
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build measures one GPU only; run with --gpus 1",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from precision_optimizer_step_amd import opt8
+    from workloads import gen, shapes
+
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    opt8.opt8_init_codebooks()
+    w = shapes.get(args.workload)
+
+    def log(msg):
+        print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+    # ---------------------------------------------------------------- inputs in HBM
+    t0 = time.time()
+    pool = max(1, min(args.grad_pool, args.steps + args.warmup))
+    tensors = []
+    modes = {0: 0, 1: 0, 2: 0}
+    alg = {0: 0, 1: 0, 2: 0}
+    for tid, spec in enumerate(w.tensors):
+        n = spec.numel
+        mode = 1 if w.state_mode == "bf16" else opt8.opt8_default_mode(n)
+        P = torch.empty(n, dtype=torch.bfloat16, device=dev)
+        gen.param_init_device(spec, w, tid, P)
+        grads = []
+        for k in range(pool):
+            G = torch.empty(n, dtype=torch.bfloat16, device=dev)
+            gen.grad_init_device(spec, w, k + 1, tid, G)
+            grads.append(G)
+        AM = AV = None
+        if mode == 0:
+            M = torch.full((n,), 127, dtype=torch.uint8, device=dev)
+            V = torch.zeros(n, dtype=torch.uint8, device=dev)
+            nb = (n + BLOCK - 1) // BLOCK
+            AM = torch.zeros(nb, dtype=torch.float32, device=dev)
+            AV = torch.zeros(nb, dtype=torch.float32, device=dev)
+        elif mode == 1:
+            M = torch.zeros(n, dtype=torch.bfloat16, device=dev)
+            V = torch.zeros(n, dtype=torch.bfloat16, device=dev)
+        else:
+            M = torch.zeros(n, dtype=torch.float32, device=dev)
+            V = torch.zeros(n, dtype=torch.float32, device=dev)
+        tensors.append(dict(tid=tid, mode=mode, n=n, P=P, grads=grads, M=M, V=V, AM=AM, AV=AV))
+        modes[mode] += n
+        alg[mode] += algorithmic_bytes(mode, n)
+    torch.cuda.synchronize()
+    total = sum(t["n"] for t in tensors)
+    log(f"workload {w.name}: {len(tensors)} tensors, {total} params, inputs built in {time.time() - t0:.1f}s, "
+        f"{torch.cuda.memory_allocated() / 2**30:.1f} GiB allocated")
+
+    lists = [opt8.tensor_array(opt8.make_tensor(t["P"], t["grads"][k], t["M"], t["V"], t["AM"], t["AV"],
+                                                tensor_id=t["tid"], mode=t["mode"]) for t in tensors)
+             for k in range(pool)]
+
+    def step(t):
+        hp = opt8.make_hparams(w.lr, w.beta1, w.beta2, w.eps, w.weight_decay, step=t, seed=w.seed)
+        opt8.opt8_adamw_step(lists[(t - 1) % pool], hp)
+
+    # ---------------------------------------------------------------- timing
+    t_step = 1
+    for _ in range(args.warmup):
+        step(t_step)
+        t_step += 1
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    for k in range(args.steps):
+        starts[k].record()
+        step(t_step)
+        ends[k].record()
+        t_step += 1
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ev_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    ms_per_step = wall * 1000.0 / args.steps
+    ev_avg = sum(ev_ms) / len(ev_ms)
+    value = total / (ms_per_step / 1000.0) / 1e9
+    log(f"wall {ms_per_step:.3f} ms/step; events per step: avg {ev_avg:.3f} min {min(ev_ms):.3f} "
+        f"max {max(ev_ms):.3f} ms")
+
+    # dominant kernel: the largest share of algorithmic bytes
+    dom = max(alg, key=lambda k: alg[k])
+    only_dom = all(v == 0 for k, v in modes.items() if k != dom)
+    kernel_ms = ev_avg if only_dom else None
+    roof = None
+    if kernel_ms:
+        achieved = alg[dom] / (kernel_ms / 1000.0) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+                "kernel": {0: "step_kernel<8bit>", 1: "step_kernel<bf16>", 2: "step_kernel<fp32>"}[dom],
+                "algorithmic_bytes_per_launch": alg[dom], "avg_launch_ms": round(kernel_ms, 4)}
+
+    # attainable streaming bandwidth on this machine: a plain device copy of 4 GiB
+    src = torch.empty(1 << 31, dtype=torch.int16, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record()
+    for _ in range(5):
+        dst.copy_(src)
+    c1.record()
+    torch.cuda.synchronize()
+    copy_gbps = 2 * src.numel() * 2 * 5 / (c0.elapsed_time(c1) / 1000.0) / 1e9
+    del src, dst
+
+    # ---------------------------------------------------------------- CPU baseline (oracle)
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        big = max(tensors, key=lambda t: t["n"] if t["mode"] == dom else -1)
+        n = min(big["n"], args.cpu_sample_elems)
+        sd = {0: np.uint8, 1: np.uint16, 2: np.float32}[big["mode"]]
+
+        def host(t, dtype):
+            h = t[:n].detach().cpu()
+            if h.dtype == torch.bfloat16:
+                h = h.view(torch.int16)
+            return h.numpy().view(dtype).copy()
+        p, g = host(big["P"], np.uint16), host(big["grads"][0], np.uint16)
+        m, v = host(big["M"], sd), host(big["V"], sd)
+        am = big["AM"][: (n + BLOCK - 1) // BLOCK].cpu().numpy() if big["AM"] is not None else None
+        av = big["AV"][: (n + BLOCK - 1) // BLOCK].cpu().numpy() if big["AV"] is not None else None
+        hp = oracle.Hparams(lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps,
+                            weight_decay=w.weight_decay, step=t_step, seed=w.seed)
+        c0t = time.perf_counter()
+        oracle.step_tensor(big["mode"], p, g, m, v, am, av, hp, big["tid"])
+        cpu_s = time.perf_counter() - c0t
+        cpu = {"value": round(n / cpu_s / 1e9, 6), "unit": "Gparams/s", "cores": 1, "kind": "oracle",
+               "sample": f"one step of the first {n} elements of tensor {w.tensors[big['tid']].name} "
+                         f"({cpu_s:.1f} s, numpy single thread, of {os.cpu_count()} host cores)"}
+        log(f"oracle: {n} elements in {cpu_s:.2f}s")
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "Gparams/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "tensors": len(tensors), "params": total,
+                   "state": "bf16-sr" if w.state_mode == "bf16" else "8bit+fp32<4096",
+                   "grad_pool": pool, "hbm_pct_of_peak": round(100 * sum(alg.values()) / (ms_per_step / 1000.0)
+                                                              / 1e9 / HBM_PEAK_GBPS, 2),
+                   "attainable_copy_GBps": round(copy_gbps, 1)},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,150 @@
+/*
+ * opt8.h -- C ABI of the fused block-wise 8-bit AdamW step with a
+ * stochastically rounded bf16 parameter write, for AMD Instinct MI355X
+ * (gfx950).  Library: libopt8.so (precision_optimizer_step_amd/).
+ *
+ * What the step computes, per element i of a tensor (all arithmetic fp32,
+ * one rounding per operation, no fused multiply-add, IEEE sqrt and divide):
+ *
+ *   g = bf16 grad, p = bf16 param (both widened exactly)
+ *   m1, v1 = moments read from the state (8-bit: codebook[code] * block absmax)
+ *   m2 = beta1*m1 + (1-beta1)*g
+ *   v2 = beta2*v1 + (1-beta2)*(g*g)
+ *   den = sqrt(v2) * rbc2 + eps          rbc2 = 1/sqrt(1 - beta2^t)
+ *   p'  = (p - lrwd*p) - step_size*(m2/den)
+ *                                        step_size = lr/(1 - beta1^t), lrwd = lr*wd
+ *   param <- bf16(p') by stochastic rounding (or nearest-even on request)
+ *   state <- m2, v2 (8-bit: block absmax + nearest codebook entry; bf16:
+ *            stochastic rounding; fp32: stored as is)
+ *
+ * Passages defining it (page title, part of the page):
+ *  - "8-bit Optimizers via Block-wise Quantization", method bullets: 2048-
+ *    element blocks each normalised by its own absolute maximum; non-linear
+ *    8-bit codes found by binary search and decoded by a lookup table times the
+ *    block maximum; dequantise, update in 32-bit and requantise in registers;
+ *    the innovations list: dynamic tree quantisation extended to unipolar data.
+ *  - "Stochastic rounding support for 8-bit optimizers", feature request: the
+ *    update is computed in full precision and the bf16 parameter is rounded up
+ *    or down with a probability set by the rounding error; the scoping
+ *    comment: opt-in, non-paged AdamW with 8-bit state, no fp32 master copy, an
+ *    fp32-state fallback for small tensors, a weight-decay baseline to pick,
+ *    and work on the caller's stream.  The "Your contribution" paragraph: the
+ *    gradient transform and parameter update form one step outside Python.
+ *  - "[Feat]: Stochastic rounding of AdamW momentums": Adam arithmetic in
+ *    float32, the p + value*exp_avg/denom update with value = -step_size
+ *    done in fp32 before rounding, a state-precision flag, bf16 momenta cast
+ *    back with stochastic rounding each step.
+ *  - "Stochastic Rounding for LLM Training: Theory and Practice", TL;DR:
+ *    BF16-AdamW-SR and randomness shared across data-parallel replicas.
+ *
+ * Random bits: Philox4x32-10 (Salmon et al., SC'11) with
+ *   key = (lo32(seed), hi32(seed)),
+ *   counter = (lo32(j/8), hi32(j/8) | stream<<30, lo32(step), tensor_id),
+ *   j = index_base + i, element j taking 16-bit half (j%8)&1 (low first) of
+ *   output word (j%8)>>1; stream 0 = param, 1 = m, 2 = v.  The bits never
+ *   depend on a rank, a launch shape or a device, so replicas agree.
+ *
+ * Codebooks: the dynamic tree code read as a decimal exponent by leading
+ * zeros plus a linear fraction taking the upper end of its step; signed
+ * table (first moment) and unsigned table (second moment), 256 fp32 entries
+ * each, ascending, code == index; zero code 127 (signed) and 0 (unsigned).
+ * A value is rounded to the entry whose midpoint interval holds it, ties to
+ * the lower code.  A block whose new absmax is below 2^-126 stores the zero
+ * code everywhere (the absmax itself is stored as computed).
+ */
+#ifndef OPT8_H_
+#define OPT8_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define OPT8_BLOCK 2048                /* elements per quantisation block        */
+#define OPT8_FP32_STATE_THRESHOLD 4096 /* default policy: fp32 state below this  */
+#define OPT8_NUM_CODES 256
+
+typedef enum {
+  OPT8_OK = 0,
+  OPT8_E_NULL = -1,      /* a required pointer is NULL                               */
+  OPT8_E_ALIGN = -2,     /* param/grad/m/v not 16-byte aligned, absmax not 4-byte    */
+  OPT8_E_SIZE = -3,      /* n < 0, numel <= 0, bad index_base, size overflow         */
+  OPT8_E_MODE = -4,      /* unknown state mode or rounding mode                      */
+  OPT8_E_HPARAM = -5,    /* lr/betas/eps/weight_decay/step outside their ranges      */
+  OPT8_E_ALIAS = -6,     /* two buffers of the list overlap                          */
+  OPT8_E_DUPID = -7,     /* tensor_id repeated in one list                           */
+  OPT8_E_NOT_INIT = -8,  /* opt8_init_codebooks not called on the current device     */
+  OPT8_E_HIP = -9        /* a HIP runtime call or a kernel launch failed             */
+} opt8_status;
+
+typedef enum {
+  OPT8_STATE_8BIT = 0,    /* u8 codes + fp32 absmax per 2048-element block           */
+  OPT8_STATE_BF16_SR = 1, /* bf16 moments written with stochastic rounding           */
+  OPT8_STATE_FP32 = 2     /* fp32 moments                                            */
+} opt8_state_mode;
+
+typedef enum {
+  OPT8_ROUND_STOCHASTIC = 0, /* parameter written with stochastic rounding          */
+  OPT8_ROUND_NEAREST = 1     /* parameter written round-to-nearest-even             */
+} opt8_round_mode;
+
+/* One tensor of the list.  All pointers are DEVICE pointers on the current
+ * HIP device, owned by the caller, and must stay valid until the work queued
+ * on the stream has finished.  Tensors are flat (row-major) arrays.          */
+typedef struct opt8_tensor {
+  uint16_t* param;        /* bf16[numel], in/out, 16-byte aligned                      */
+  const uint16_t* grad;   /* bf16[numel], read only, 16-byte aligned                   */
+  void* m;                /* first moment [numel]: u8 (8-bit), bf16 or f32 by mode,    */
+  void* v;                /*   second moment likewise; in/out, 16-byte aligned         */
+  float* absmax_m;        /* f32[ceil(numel/2048)], in/out, 8-bit mode only (else     */
+  float* absmax_v;        /*   ignored and may be NULL); 4-byte aligned               */
+  int64_t numel;          /* > 0                                                       */
+  int64_t index_base;     /* global index of element 0 in the unsharded tensor (RNG   */
+                          /*   counter); >= 0 and a multiple of 2048; 0 if unsharded  */
+  uint32_t tensor_id;     /* RNG stream id; unique in the list, stable over steps     */
+  int32_t mode;           /* opt8_state_mode                                           */
+} opt8_tensor;
+
+typedef struct opt8_hparams {
+  double lr;              /* >= 0, finite                                              */
+  double beta1;           /* [0, 1)                                                    */
+  double beta2;           /* [0, 1)                                                    */
+  double eps;             /* > 0, finite                                               */
+  double weight_decay;    /* >= 0, finite; decoupled (AdamW)                           */
+  int64_t step;           /* 1-based step count t of this update, >= 1                 */
+  uint64_t seed;          /* Philox key                                                */
+  int32_t param_round;    /* opt8_round_mode                                           */
+  int32_t reserved;       /* must be 0                                                 */
+} opt8_hparams;
+
+/* Build the two 256-entry codebooks (and their 255 midpoints) on the host and
+ * upload them to the CURRENT device; idempotent, once per device.  If
+ * signed_out / unsigned_out are non-NULL the fp32 tables are also copied to
+ * those host arrays, before the upload, so a host without a GPU still gets
+ * them (the call then returns OPT8_E_HIP).  Returns OPT8_OK or OPT8_E_HIP.   */
+int opt8_init_codebooks(float* signed_out, float* unsigned_out);
+
+/* Default state mode for a tensor of numel elements: OPT8_STATE_FP32 below
+ * 4096 elements, OPT8_STATE_8BIT otherwise (the small-tensor fallback).      */
+int32_t opt8_default_mode(int64_t numel);
+
+/* One AdamW step over a list of n tensors, queued on hip_stream (a
+ * hipStream_t; NULL = the null stream) and asynchronous to the host.
+ * Every descriptor and hyperparameter is validated first; on any error
+ * nothing is queued and nothing is modified.  n == 0 is a no-op.  Tensors of
+ * different modes may be mixed.  Concurrent calls on different streams must
+ * use disjoint buffers.  Device faults surface at the caller's next
+ * synchronisation.  Returns OPT8_OK or a negative opt8_status.              */
+int opt8_adamw_step(const opt8_tensor* tensors, int32_t n, const opt8_hparams* hp,
+                    void* hip_stream);
+
+/* Message of the last failure on the calling thread ("" if none).  The
+ * string is owned by the library and valid until the thread's next call.    */
+const char* opt8_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* OPT8_H_ */

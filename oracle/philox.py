@@ -73,12 +73,20 @@ def sr_bits(seed: int, step: int, tensor_id: int, index, stream: int) -> np.ndar
     """uint32[n] of 16-bit random words (0..65535), one per global element index."""
     index = np.asarray(index, dtype=np.uint64).reshape(-1)
     group = index >> np.uint64(3)
-    lane = (index & np.uint64(7)).astype(np.int64)
-    c0 = group & np.uint64(_MASK)
-    c1 = (group >> np.uint64(32)) | np.uint64((stream & 3) << 30)
-    c2 = np.full(index.shape, step & _MASK, dtype=np.uint64)
-    c3 = np.full(index.shape, tensor_id & _MASK, dtype=np.uint64)
+    # one Philox call per distinct group of 8 consecutive indices
+    if index.size and np.array_equal(index, np.arange(int(index[0]), int(index[0]) + index.size,
+                                                      dtype=np.uint64)):
+        first = int(group[0])
+        groups = np.arange(first, int(group[-1]) + 1, dtype=np.uint64)
+        which = (group - np.uint64(first)).astype(np.int64)
+    else:
+        groups, which = np.unique(group, return_inverse=True)
+    c0 = groups & np.uint64(_MASK)
+    c1 = (groups >> np.uint64(32)) | np.uint64((stream & 3) << 30)
+    c2 = np.full(groups.shape, step & _MASK, dtype=np.uint64)
+    c3 = np.full(groups.shape, tensor_id & _MASK, dtype=np.uint64)
     words = np.stack(philox4x32_10(c0, c1, c2, c3, seed & _MASK, (seed >> 32) & _MASK))
-    word = np.take_along_axis(words, (lane >> 1)[None, :], axis=0)[0]
+    lane = (index & np.uint64(7)).astype(np.int64)
+    word = words[lane >> 1, which]
     shift = ((lane & 1) * 16).astype(np.uint32)
     return (word >> shift) & np.uint32(0xFFFF)

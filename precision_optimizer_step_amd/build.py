@@ -1,0 +1,49 @@
+"""Builds libopt8.so (host C++ + gfx950 HIP kernels) in this package directory.
+
+    python -m precision_optimizer_step_amd.build
+"""
+import os
+import shutil
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB = os.path.join(HERE, "libopt8.so")
+SOURCES = [os.path.join(HERE, "csrc", "opt8_host.cpp"), os.path.join(HERE, "csrc", "opt8_kernels.hip")]
+
+# fp32 arithmetic must round once per operation exactly as written: no
+# contraction into fused multiply-adds, IEEE sqrt/divide (hipcc's default),
+# denormals kept (hipcc's default), no fast-math.  Packed fp32 instructions
+# are switched off.
+FLAGS = [
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+    "-ffp-contract=off",
+    "-fno-fast-math",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall",
+]
+
+
+def hipcc() -> str:
+    for cand in (shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found: the ROCm toolchain is required to build libopt8.so")
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source into libopt8.so (always recompiles); returns its path."""
+    tmp = LIB + ".tmp"
+    cmd = [hipcc(), *FLAGS, "-o", tmp, *SOURCES]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    out = "\n".join(ln for ln in (res.stdout + res.stderr).splitlines() if "packed-fp32-ops" not in ln)
+    if res.returncode != 0:
+        raise RuntimeError("hipcc failed:\n" + " ".join(cmd) + "\n" + out)
+    if verbose and out.strip():
+        print(out, file=sys.stderr)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

@@ -1,0 +1,423 @@
+// Host side of libopt8: codebook construction, step scalars, argument
+// validation, the per-device descriptor cache and the C entry points.
+#include <algorithm>
+#include <cstdarg>
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "../../include/opt8.h"
+#include "opt8_internal.h"
+
+namespace opt8 {
+namespace {
+
+thread_local std::string t_error;
+
+int fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  t_error = buf;
+  return code;
+}
+
+// ----------------------------------------------------------------------------- codebooks
+// Nearest fp32 to num/den (num, den > 0), ties to even, in exact integer
+// arithmetic: scale so the quotient has 24 significant bits, round on the
+// remainder.
+float nearest_f32(uint64_t num, uint64_t den) {
+  if (num == 0) return 0.0f;
+  using u128 = unsigned __int128;
+  const u128 n = num, d = den;
+  int s = 0;                                   // value = q * 2^-s
+  while ((n << s) < (static_cast<u128>(d) << 23)) ++s;
+  while ((n << s) >= (static_cast<u128>(d) << 24)) --s;   // only for values >= 2^24 (never)
+  const u128 scaled = n << s;
+  u128 q = scaled / d;
+  const u128 rem = scaled % d;
+  if (2 * rem > d || (2 * rem == d && (q & 1))) ++q;
+  if (q == (static_cast<u128>(1) << 24)) { q >>= 1; --s; }
+  return std::ldexp(static_cast<float>(static_cast<uint64_t>(q)), -s);
+}
+
+uint64_t pow10u(int e) {
+  uint64_t r = 1;
+  while (e-- > 0) r *= 10;
+  return r;
+}
+
+// Dynamic tree code, read as: decade E of the magnitude (10^-(E+1), 10^-E] is
+// split into 2^F equal steps, F = magnitude_bits - 1 - E, and level k
+// (k = 0..2^F-1) is the upper end of step k:
+//   (2^F + 9 (k + 1)) / (10^(E+1) 2^F).
+// The signed code spends one bit on the sign (magnitude_bits 7) and the
+// unsigned code does not (magnitude_bits 8).  Source: "8-bit Optimizers via
+// Block-wise Quantization", innovations list (dynamic tree quantization
+// extended to unipolar data) and method bullets (non-linear 8-bit code).
+void tree_levels(int magnitude_bits, bool negative_too, std::vector<float>& out) {
+  for (int e = 0; e < magnitude_bits; ++e) {
+    const int f = magnitude_bits - 1 - e;
+    const uint64_t steps = 1ull << f;
+    for (uint64_t k = 0; k < steps; ++k) {
+      const float x = nearest_f32(steps + 9 * (k + 1), pow10u(e + 1) * steps);
+      out.push_back(x);
+      if (negative_too) out.push_back(-x);
+    }
+  }
+}
+
+struct Tables {
+  float words[kTableWords];
+};
+
+Tables build_tables() {
+  std::vector<float> s, u;
+  tree_levels(7, true, s);
+  s.push_back(0.0f);
+  s.push_back(nearest_f32(1, 10000000));   // the spare signed string: the 1e-7 level
+  tree_levels(8, false, u);
+  u.push_back(0.0f);
+  std::sort(s.begin(), s.end());
+  std::sort(u.begin(), u.end());
+  Tables t;
+  auto fill = [&](const std::vector<float>& c, float* tab, float* mid) {
+    for (int k = 0; k < kCodes; ++k) tab[k] = c[k];
+    for (int k = 0; k + 1 < kCodes; ++k)   // neighbours sum exactly in double
+      mid[k] = static_cast<float>((static_cast<double>(c[k]) + static_cast<double>(c[k + 1])) * 0.5);
+    mid[kCodes - 1] = INFINITY;
+  };
+  fill(s, t.words, t.words + kCodes);
+  fill(u, t.words + 2 * kCodes, t.words + 3 * kCodes);
+  return t;
+}
+
+const Tables& tables() {
+  static const Tables t = build_tables();
+  return t;
+}
+
+// ----------------------------------------------------------------------------- scalars
+// beta^t by repeated double multiplication (no pow), cached per beta pair so a
+// training run advances it incrementally; once both powers are below 2^-60,
+// 1 - beta^t is exactly 1.0 in double and further products cannot change it.
+struct PowCache {
+  double b1 = -1, b2 = -1, p1 = 1, p2 = 1;
+  int64_t t = 0;
+};
+
+void beta_powers(double b1, double b2, int64_t t, PowCache& c, double& p1, double& p2) {
+  if (c.b1 != b1 || c.b2 != b2 || c.t > t) c = PowCache{b1, b2, 1.0, 1.0, 0};
+  const double tiny = std::ldexp(1.0, -60);
+  while (c.t < t) {
+    if (c.p1 < tiny && c.p2 < tiny) { c.t = t; break; }
+    c.p1 *= b1;
+    c.p2 *= b2;
+    ++c.t;
+  }
+  p1 = c.p1;
+  p2 = c.p2;
+}
+
+StepScalars make_scalars(const opt8_hparams& hp, PowCache& cache) {
+  double b1t, b2t;
+  beta_powers(hp.beta1, hp.beta2, hp.step, cache, b1t, b2t);
+  const double bc1 = 1.0 - b1t;
+  const double bc2 = 1.0 - b2t;
+  StepScalars s;
+  s.beta1 = static_cast<float>(hp.beta1);
+  s.beta2 = static_cast<float>(hp.beta2);
+  s.w1 = static_cast<float>(1.0 - hp.beta1);
+  s.w2 = static_cast<float>(1.0 - hp.beta2);
+  s.eps = static_cast<float>(hp.eps);
+  s.step_size = static_cast<float>(hp.lr / bc1);
+  s.rbc2 = static_cast<float>(1.0 / std::sqrt(bc2));
+  s.lrwd = static_cast<float>(hp.lr * hp.weight_decay);
+  s.seed_lo = static_cast<uint32_t>(hp.seed);
+  s.seed_hi = static_cast<uint32_t>(hp.seed >> 32);
+  s.step_lo = static_cast<uint32_t>(hp.step);
+  s.param_round = hp.param_round;
+  return s;
+}
+
+// ----------------------------------------------------------------------------- validation
+size_t state_bytes(int mode) { return mode == OPT8_STATE_8BIT ? 1 : mode == OPT8_STATE_BF16_SR ? 2 : 4; }
+int64_t nblocks_of(int64_t numel) { return (numel + kBlock - 1) / kBlock; }
+
+int validate_hparams(const opt8_hparams& hp) {
+  if (!(std::isfinite(hp.lr) && hp.lr >= 0)) return fail(OPT8_E_HPARAM, "lr must be finite and >= 0 (got %g)", hp.lr);
+  if (!(hp.beta1 >= 0 && hp.beta1 < 1)) return fail(OPT8_E_HPARAM, "beta1 must be in [0, 1) (got %g)", hp.beta1);
+  if (!(hp.beta2 >= 0 && hp.beta2 < 1)) return fail(OPT8_E_HPARAM, "beta2 must be in [0, 1) (got %g)", hp.beta2);
+  if (!(std::isfinite(hp.eps) && hp.eps > 0)) return fail(OPT8_E_HPARAM, "eps must be finite and > 0 (got %g)", hp.eps);
+  if (!(std::isfinite(hp.weight_decay) && hp.weight_decay >= 0))
+    return fail(OPT8_E_HPARAM, "weight_decay must be finite and >= 0 (got %g)", hp.weight_decay);
+  if (hp.step < 1) return fail(OPT8_E_HPARAM, "step is 1-based (got %lld)", static_cast<long long>(hp.step));
+  if (hp.reserved != 0) return fail(OPT8_E_HPARAM, "reserved field must be 0");
+  if (hp.param_round != OPT8_ROUND_STOCHASTIC && hp.param_round != OPT8_ROUND_NEAREST)
+    return fail(OPT8_E_MODE, "unknown param_round %d", hp.param_round);
+  return OPT8_OK;
+}
+
+struct Range {
+  uintptr_t lo, hi;
+  int tensor;
+  const char* what;
+};
+
+int validate_tensors(const opt8_tensor* t, int32_t n) {
+  std::vector<Range> ranges;
+  std::vector<uint32_t> ids;
+  ranges.reserve(static_cast<size_t>(n) * 6);
+  ids.reserve(static_cast<size_t>(n));
+  for (int32_t i = 0; i < n; ++i) {
+    const opt8_tensor& x = t[i];
+    if (x.mode != OPT8_STATE_8BIT && x.mode != OPT8_STATE_BF16_SR && x.mode != OPT8_STATE_FP32)
+      return fail(OPT8_E_MODE, "tensor %d: unknown state mode %d", i, x.mode);
+    if (!x.param || !x.grad || !x.m || !x.v) return fail(OPT8_E_NULL, "tensor %d: NULL param/grad/m/v", i);
+    const bool q8 = x.mode == OPT8_STATE_8BIT;
+    if (q8 && (!x.absmax_m || !x.absmax_v)) return fail(OPT8_E_NULL, "tensor %d: 8-bit mode needs absmax_m/absmax_v", i);
+    if (x.numel <= 0) return fail(OPT8_E_SIZE, "tensor %d: numel must be > 0", i);
+    if (x.numel > (int64_t(1) << 46)) return fail(OPT8_E_SIZE, "tensor %d: numel too large", i);
+    if (x.index_base < 0 || x.index_base % kBlock != 0 || x.index_base > (int64_t(1) << 60))
+      return fail(OPT8_E_SIZE, "tensor %d: index_base must be >= 0 and a multiple of 2048", i);
+    auto al = [](const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; };
+    if (!al(x.param, 16) || !al(x.grad, 16) || !al(x.m, 16) || !al(x.v, 16))
+      return fail(OPT8_E_ALIGN, "tensor %d: param/grad/m/v must be 16-byte aligned", i);
+    if (q8 && (!al(x.absmax_m, 4) || !al(x.absmax_v, 4)))
+      return fail(OPT8_E_ALIGN, "tensor %d: absmax arrays must be 4-byte aligned", i);
+    const uintptr_t ne = static_cast<uintptr_t>(x.numel);
+    const uintptr_t sb = state_bytes(x.mode);
+    auto add = [&](const void* p, uintptr_t bytes, const char* what) {
+      const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+      ranges.push_back(Range{lo, lo + bytes, i, what});
+    };
+    add(x.param, 2 * ne, "param");
+    add(x.grad, 2 * ne, "grad");
+    add(x.m, sb * ne, "m");
+    add(x.v, sb * ne, "v");
+    if (q8) {
+      const uintptr_t ab = 4 * static_cast<uintptr_t>(nblocks_of(x.numel));
+      add(x.absmax_m, ab, "absmax_m");
+      add(x.absmax_v, ab, "absmax_v");
+    }
+    ids.push_back(x.tensor_id);
+  }
+  std::sort(ids.begin(), ids.end());
+  for (size_t k = 1; k < ids.size(); ++k)
+    if (ids[k] == ids[k - 1]) return fail(OPT8_E_DUPID, "tensor_id %u appears twice", ids[k]);
+  std::sort(ranges.begin(), ranges.end(), [](const Range& a, const Range& b) { return a.lo < b.lo; });
+  for (size_t k = 1; k < ranges.size(); ++k)
+    if (ranges[k].lo < ranges[k - 1].hi)
+      return fail(OPT8_E_ALIAS, "buffers overlap: tensor %d %s and tensor %d %s", ranges[k - 1].tensor,
+                  ranges[k - 1].what, ranges[k].tensor, ranges[k].what);
+  return OPT8_OK;
+}
+
+// ----------------------------------------------------------------------------- device state
+// Descriptor lists live in device memory, one slot per distinct list; a list
+// passed again (the usual training loop) is launched without a new upload.
+constexpr int kSlots = 4;
+constexpr int kMaxDevices = 64;
+
+struct Slot {
+  DevTensor* dev = nullptr;
+  DevTensor* host = nullptr;   // pinned staging buffer
+  size_t cap = 0;              // descriptors
+  std::vector<DevTensor> key;  // contents now on the device
+  hipEvent_t done = nullptr;   // recorded after the last launch that read it
+  hipStream_t last_stream = nullptr;
+  bool used = false;
+  uint64_t stamp = 0;
+};
+
+struct DeviceState {
+  bool init = false;
+  int num_cu = 0;
+  int occ[3] = {1, 1, 1};
+  Slot slots[kSlots];
+  uint64_t clock = 0;
+  PowCache pow;
+};
+
+std::mutex g_mu;
+DeviceState g_dev[kMaxDevices];
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(OPT8_E_HIP, "%s failed: %s", what, hipGetErrorString(e));
+}
+
+int current_device(int& dev) {
+  const hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(OPT8_E_HIP, "device index %d out of range", dev);
+  return OPT8_OK;
+}
+
+int ensure_capacity(Slot& s, size_t count) {
+  if (s.cap >= count) return OPT8_OK;
+  size_t cap = std::max<size_t>(count, 64);
+  cap = std::max(cap, s.cap * 2);
+  if (s.dev) (void)hipFree(s.dev);
+  if (s.host) (void)hipHostFree(s.host);
+  s.dev = nullptr;
+  s.host = nullptr;
+  s.cap = 0;
+  hipError_t e = hipMalloc(&s.dev, cap * sizeof(DevTensor));
+  if (e != hipSuccess) return hip_fail(e, "hipMalloc(descriptors)");
+  e = hipHostMalloc(&s.host, cap * sizeof(DevTensor), hipHostMallocDefault);
+  if (e != hipSuccess) return hip_fail(e, "hipHostMalloc(descriptors)");
+  s.cap = cap;
+  return OPT8_OK;
+}
+
+bool same_list(const std::vector<DevTensor>& a, const std::vector<DevTensor>& b) {
+  return a.size() == b.size() && std::memcmp(a.data(), b.data(), a.size() * sizeof(DevTensor)) == 0;
+}
+
+// Returns the slot holding `list` on the device, ordered before work queued
+// next on `stream`.
+int acquire_slot(DeviceState& ds, const std::vector<DevTensor>& list, hipStream_t stream, Slot*& out) {
+  ++ds.clock;
+  for (Slot& s : ds.slots) {
+    if (s.used && same_list(s.key, list)) {
+      if (s.last_stream != stream) {
+        const hipError_t e = hipStreamWaitEvent(stream, s.done, 0);
+        if (e != hipSuccess) return hip_fail(e, "hipStreamWaitEvent");
+      }
+      s.stamp = ds.clock;
+      out = &s;
+      return OPT8_OK;
+    }
+  }
+  Slot* victim = &ds.slots[0];
+  for (Slot& s : ds.slots) {
+    if (!s.used) { victim = &s; break; }
+    if (s.stamp < victim->stamp) victim = &s;
+  }
+  Slot& s = *victim;
+  if (s.used) {   // every launch that read it has finished before it is rewritten
+    const hipError_t e = hipEventSynchronize(s.done);
+    if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize");
+  }
+  s.used = false;
+  int rc = ensure_capacity(s, list.size());
+  if (rc != OPT8_OK) return rc;
+  std::memcpy(s.host, list.data(), list.size() * sizeof(DevTensor));
+  const hipError_t e = hipMemcpyAsync(s.dev, s.host, list.size() * sizeof(DevTensor),
+                                      hipMemcpyHostToDevice, stream);
+  if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync(descriptors)");
+  s.key = list;
+  s.used = true;
+  s.stamp = ds.clock;
+  out = &s;
+  return OPT8_OK;
+}
+
+}  // namespace
+}  // namespace opt8
+
+using namespace opt8;
+
+extern "C" int opt8_init_codebooks(float* signed_out, float* unsigned_out) {
+  std::lock_guard<std::mutex> lock(g_mu);
+  const Tables& t = tables();
+  if (signed_out) std::memcpy(signed_out, t.words, sizeof(float) * kCodes);
+  if (unsigned_out) std::memcpy(unsigned_out, t.words + 2 * kCodes, sizeof(float) * kCodes);
+  int dev = 0;
+  int rc = current_device(dev);
+  if (rc != OPT8_OK) return rc;
+  DeviceState& ds = g_dev[dev];
+  if (ds.init) return OPT8_OK;
+  hipError_t e = upload_tables(t.words);
+  if (e != hipSuccess) return hip_fail(e, "upload of codebooks");
+  e = hipDeviceGetAttribute(&ds.num_cu, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute(CU count)");
+  for (int k = 0; k < 3; ++k) ds.occ[k] = occupancy_per_cu(static_cast<Kind>(k));
+  for (Slot& s : ds.slots) {
+    if (!s.done) {
+      e = hipEventCreateWithFlags(&s.done, hipEventDisableTiming);
+      if (e != hipSuccess) return hip_fail(e, "hipEventCreateWithFlags");
+    }
+  }
+  e = hipDeviceSynchronize();
+  if (e != hipSuccess) return hip_fail(e, "hipDeviceSynchronize");
+  ds.init = true;
+  return OPT8_OK;
+}
+
+extern "C" int32_t opt8_default_mode(int64_t numel) {
+  return numel < OPT8_FP32_STATE_THRESHOLD ? OPT8_STATE_FP32 : OPT8_STATE_8BIT;
+}
+
+extern "C" const char* opt8_last_error(void) { return t_error.c_str(); }
+
+extern "C" int opt8_adamw_step(const opt8_tensor* tensors, int32_t n, const opt8_hparams* hp,
+                               void* hip_stream) {
+  t_error.clear();
+  if (!hp) return fail(OPT8_E_NULL, "hparams is NULL");
+  if (n < 0) return fail(OPT8_E_SIZE, "n must be >= 0 (got %d)", n);
+  if (n > 0 && !tensors) return fail(OPT8_E_NULL, "tensor list is NULL");
+  int rc = validate_hparams(*hp);
+  if (rc != OPT8_OK) return rc;
+  rc = validate_tensors(tensors, n);
+  if (rc != OPT8_OK) return rc;
+  if (n == 0) return OPT8_OK;
+
+  std::lock_guard<std::mutex> lock(g_mu);
+  int dev = 0;
+  rc = current_device(dev);
+  if (rc != OPT8_OK) return rc;
+  DeviceState& ds = g_dev[dev];
+  if (!ds.init) return fail(OPT8_E_NOT_INIT, "opt8_init_codebooks has not run on device %d", dev);
+
+  // one sub-list per state mode, each with its own block numbering
+  std::vector<DevTensor> list;
+  list.reserve(static_cast<size_t>(n));
+  int count[3] = {0, 0, 0};
+  int64_t blocks[3] = {0, 0, 0};
+  int first[3] = {0, 0, 0};
+  for (int kind = 0; kind < 3; ++kind) {
+    first[kind] = static_cast<int>(list.size());
+    for (int32_t i = 0; i < n; ++i) {
+      const opt8_tensor& x = tensors[i];
+      if (x.mode != kind) continue;
+      DevTensor d;
+      d.param = x.param;
+      d.grad = x.grad;
+      d.m = x.m;
+      d.v = x.v;
+      d.amax_m = kind == OPT8_STATE_8BIT ? x.absmax_m : nullptr;
+      d.amax_v = kind == OPT8_STATE_8BIT ? x.absmax_v : nullptr;
+      d.numel = x.numel;
+      d.index_base = x.index_base;
+      d.block_begin = blocks[kind];
+      d.tensor_id = x.tensor_id;
+      d.nblocks = static_cast<uint32_t>(nblocks_of(x.numel));
+      blocks[kind] += d.nblocks;
+      ++count[kind];
+      list.push_back(d);
+    }
+  }
+  const hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+  Slot* slot = nullptr;
+  rc = acquire_slot(ds, list, stream, slot);
+  if (rc != OPT8_OK) return rc;
+  const StepScalars sc = make_scalars(*hp, ds.pow);
+  for (int kind = 0; kind < 3; ++kind) {
+    if (!count[kind]) continue;
+    const int cap = ds.num_cu * ds.occ[kind];
+    const hipError_t e = launch_step(static_cast<Kind>(kind), slot->dev + first[kind], count[kind],
+                                     blocks[kind], sc, stream, cap);
+    if (e != hipSuccess) return hip_fail(e, "kernel launch");
+  }
+  const hipError_t e = hipEventRecord(slot->done, stream);
+  if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
+  slot->last_stream = stream;
+  return OPT8_OK;
+}

@@ -1,0 +1,456 @@
+// gfx950 kernels of the fused AdamW step (8-bit, bf16-SR and fp32 state).
+//
+// Work unit: one 2048-element quantisation block per wave64 ("8-bit Optimizers
+// via Block-wise Quantization", method bullets: 2048-element blocks normalised
+// by their own absolute maximum).  Lane l of the wave owns elements
+// r*512 + 8l .. r*512 + 8l + 7 for r = 0..3, so every global access of a wave
+// is one contiguous 1 KiB (bf16, 16 B per lane) or 512 B (codes, 8 B per lane)
+// segment, and one Philox call per lane and r yields the 8 random 16-bit words
+// of those 8 elements.  A block's absmax is a max, reduced across the wave
+// with cross-lane shuffles, so it is exact and independent of order.
+//
+// Waves of a persistent grid take contiguous runs of blocks over the whole
+// tensor list; each workgroup stages the codebooks and midpoints in LDS once.
+//
+// Arithmetic follows the step exactly as the oracle states it: fp32, one
+// rounding per operation (built with -ffp-contract=off), IEEE sqrt and divide,
+// denormals kept.
+#include "opt8_internal.h"
+
+namespace opt8 {
+namespace {
+
+constexpr int kWaves = 4;                 // waves per workgroup
+constexpr int kThreads = 64 * kWaves;
+constexpr int kGroups = kBlock / (64 * 8);  // 8-element groups per lane per block (4)
+
+__device__ float g_tables[kTableWords];
+
+// Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11): two 32x32->64 products per
+// round, the words permuted and xored with the round key, key bumped by the
+// Weyl constants.
+constexpr uint32_t kPhiloxM0 = 0xD2511F53u;
+constexpr uint32_t kPhiloxM1 = 0xCD9E8D57u;
+constexpr uint32_t kPhiloxW0 = 0x9E3779B9u;
+constexpr uint32_t kPhiloxW1 = 0xBB67AE85u;
+
+struct Rand4 {
+  uint32_t w[4];
+};
+
+__device__ __forceinline__ Rand4 philox10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3,
+                                          uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    const uint64_t p0 = static_cast<uint64_t>(kPhiloxM0) * c0;
+    const uint64_t p1 = static_cast<uint64_t>(kPhiloxM1) * c2;
+    const uint32_t n0 = static_cast<uint32_t>(p1 >> 32) ^ c1 ^ k0;
+    const uint32_t n2 = static_cast<uint32_t>(p0 >> 32) ^ c3 ^ k1;
+    c1 = static_cast<uint32_t>(p1);
+    c3 = static_cast<uint32_t>(p0);
+    c0 = n0;
+    c2 = n2;
+    k0 += kPhiloxW0;
+    k1 += kPhiloxW1;
+  }
+  return Rand4{{c0, c1, c2, c3}};
+}
+
+// Random words of the 8-element group `grp` (global element index / 8).
+__device__ __forceinline__ Rand4 group_bits(uint64_t grp, uint32_t stream, uint32_t tensor_id,
+                                            const StepScalars& sc) {
+  return philox10(static_cast<uint32_t>(grp), static_cast<uint32_t>(grp >> 32) | (stream << 30),
+                  sc.step_lo, tensor_id, sc.seed_lo, sc.seed_hi);
+}
+
+__device__ __forceinline__ uint32_t r16_of(const Rand4& r, int j) {
+  return (r.w[j >> 1] >> (16 * (j & 1))) & 0xFFFFu;
+}
+
+// fp32 -> bf16 bits: stochastic (add 16 random bits below the kept half, then
+// truncate) or nearest-even; NaN becomes the quiet NaN with its sign.
+__device__ __forceinline__ uint32_t to_bf16(float x, uint32_t r16, bool nearest) {
+  const uint32_t b = __float_as_uint(x);
+  if ((b & 0x7FFFFFFFu) > 0x7F800000u) return 0x7FC0u | ((b >> 16) & 0x8000u);
+  const uint32_t add = nearest ? (0x7FFFu + ((b >> 16) & 1u)) : r16;
+  return (b + add) >> 16;
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+__device__ __forceinline__ float bf16_at(const uint4& q, int j) {
+  const uint32_t w = (j < 2) ? q.x : (j < 4) ? q.y : (j < 6) ? q.z : q.w;
+  return (j & 1) ? bf16_hi(w) : bf16_lo(w);
+}
+__device__ __forceinline__ uint32_t byte_at(const uint2& q, int j) {
+  return (((j < 4) ? q.x : q.y) >> (8 * (j & 3))) & 0xFFu;
+}
+
+// AdamW on one element; returns the new fp32 parameter and the new moments.
+__device__ __forceinline__ float adamw(float p, float g, float m1, float v1, const StepScalars& sc,
+                                       float& m2, float& v2) {
+  m2 = sc.beta1 * m1 + sc.w1 * g;
+  v2 = sc.beta2 * v1 + sc.w2 * (g * g);
+  const float den = sqrtf(v2) * sc.rbc2 + sc.eps;
+  return (p - sc.lrwd * p) - sc.step_size * (m2 / den);
+}
+
+// Number of midpoints strictly below n (255 sorted midpoints): the nearest
+// codebook entry, ties to the lower code.  Branchless binary search.
+__device__ __forceinline__ uint32_t code_of(float n, const float* mid) {
+  uint32_t idx = 0;
+#pragma unroll
+  for (uint32_t s = 128; s >= 1; s >>= 1) idx += (mid[idx + s - 1] < n) ? s : 0u;
+  return idx;
+}
+
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
+  return x;
+}
+
+// ----------------------------------------------------------------------------- 8-bit state
+template <bool kFull>
+__device__ __forceinline__ void block_8bit(const DevTensor& d, int64_t blk, int lane, int valid,
+                                           const StepScalars& sc, const float* s_tab) {
+  const int64_t e0 = blk * kBlock;
+  const uint16_t* gp = d.grad + e0;
+  uint16_t* pp = d.param + e0;
+  uint8_t* mp = static_cast<uint8_t*>(d.m) + e0;
+  uint8_t* vp = static_cast<uint8_t*>(d.v) + e0;
+  const float am = d.amax_m[blk];
+  const float av = d.amax_v[blk];
+  const bool nearest = sc.param_round != 0;
+
+  uint4 G[kGroups], P[kGroups];
+  uint2 QM[kGroups], QV[kGroups];
+#pragma unroll
+  for (int r = 0; r < kGroups; ++r) {
+    const int off = r * 512 + lane * 8;
+    if (kFull) {
+      G[r] = *reinterpret_cast<const uint4*>(gp + off);
+      P[r] = *reinterpret_cast<const uint4*>(pp + off);
+      QM[r] = *reinterpret_cast<const uint2*>(mp + off);
+      QV[r] = *reinterpret_cast<const uint2*>(vp + off);
+    } else {
+      uint32_t g32[4] = {0, 0, 0, 0}, p32[4] = {0, 0, 0, 0}, m32[2] = {0, 0}, v32[2] = {0, 0};
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        if (off + j < valid) {
+          g32[j >> 1] |= static_cast<uint32_t>(gp[off + j]) << (16 * (j & 1));
+          p32[j >> 1] |= static_cast<uint32_t>(pp[off + j]) << (16 * (j & 1));
+          m32[j >> 2] |= static_cast<uint32_t>(mp[off + j]) << (8 * (j & 3));
+          v32[j >> 2] |= static_cast<uint32_t>(vp[off + j]) << (8 * (j & 3));
+        }
+      }
+      G[r] = make_uint4(g32[0], g32[1], g32[2], g32[3]);
+      P[r] = make_uint4(p32[0], p32[1], p32[2], p32[3]);
+      QM[r] = make_uint2(m32[0], m32[1]);
+      QV[r] = make_uint2(v32[0], v32[1]);
+    }
+  }
+
+  float M2[kGroups * 8], V2[kGroups * 8];
+  float mxm = 0.0f, mxv = 0.0f;
+  const uint64_t grp0 = static_cast<uint64_t>(d.index_base + e0) >> 3;
+#pragma unroll
+  for (int r = 0; r < kGroups; ++r) {
+    const int off = r * 512 + lane * 8;
+    Rand4 rnd{{0, 0, 0, 0}};
+    if (!nearest) rnd = group_bits(grp0 + (off >> 3), 0u, d.tensor_id, sc);
+    uint32_t outw[4] = {0, 0, 0, 0};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float g = bf16_at(G[r], j);
+      const float p = bf16_at(P[r], j);
+      const float m1 = s_tab[byte_at(QM[r], j)] * am;
+      const float v1 = s_tab[2 * kCodes + byte_at(QV[r], j)] * av;
+      float m2, v2;
+      const float pn = adamw(p, g, m1, v1, sc, m2, v2);
+      outw[j >> 1] |= to_bf16(pn, r16_of(rnd, j), nearest) << (16 * (j & 1));
+      const bool ok = kFull || (off + j < valid);
+      M2[r * 8 + j] = ok ? m2 : 0.0f;
+      V2[r * 8 + j] = ok ? v2 : 0.0f;
+      mxm = fmaxf(mxm, fabsf(M2[r * 8 + j]));
+      mxv = fmaxf(mxv, V2[r * 8 + j]);
+    }
+    if (kFull) {
+      *reinterpret_cast<uint4*>(pp + off) = make_uint4(outw[0], outw[1], outw[2], outw[3]);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (off + j < valid) pp[off + j] = static_cast<uint16_t>(outw[j >> 1] >> (16 * (j & 1)));
+    }
+  }
+
+  mxm = wave_max(mxm);
+  mxv = wave_max(mxv);
+  const float kMinNormal = 1.17549435e-38f;   // 2^-126
+  const bool live_m = mxm >= kMinNormal;
+  const bool live_v = mxv >= kMinNormal;
+  const float inv_m = live_m ? 1.0f / mxm : 0.0f;
+  const float inv_v = live_v ? 1.0f / mxv : 0.0f;
+  const float* mid_s = s_tab + kCodes;
+  const float* mid_u = s_tab + 3 * kCodes;
+#pragma unroll
+  for (int r = 0; r < kGroups; ++r) {
+    const int off = r * 512 + lane * 8;
+    uint32_t cm[2] = {0, 0}, cv[2] = {0, 0};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t qm = live_m ? code_of(M2[r * 8 + j] * inv_m, mid_s) : 127u;
+      const uint32_t qv = live_v ? code_of(V2[r * 8 + j] * inv_v, mid_u) : 0u;
+      cm[j >> 2] |= qm << (8 * (j & 3));
+      cv[j >> 2] |= qv << (8 * (j & 3));
+    }
+    if (kFull) {
+      *reinterpret_cast<uint2*>(mp + off) = make_uint2(cm[0], cm[1]);
+      *reinterpret_cast<uint2*>(vp + off) = make_uint2(cv[0], cv[1]);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        if (off + j < valid) {
+          mp[off + j] = static_cast<uint8_t>(cm[j >> 2] >> (8 * (j & 3)));
+          vp[off + j] = static_cast<uint8_t>(cv[j >> 2] >> (8 * (j & 3)));
+        }
+      }
+    }
+  }
+  if (lane == 0) {
+    d.amax_m[blk] = mxm;
+    d.amax_v[blk] = mxv;
+  }
+}
+
+// ----------------------------------------------------------------------------- bf16 state (SR)
+template <bool kFull>
+__device__ __forceinline__ void block_bf16(const DevTensor& d, int64_t blk, int lane, int valid,
+                                           const StepScalars& sc) {
+  const int64_t e0 = blk * kBlock;
+  const uint16_t* gp = d.grad + e0;
+  uint16_t* pp = d.param + e0;
+  uint16_t* mp = static_cast<uint16_t*>(d.m) + e0;
+  uint16_t* vp = static_cast<uint16_t*>(d.v) + e0;
+  const bool nearest = sc.param_round != 0;
+  const uint64_t grp0 = static_cast<uint64_t>(d.index_base + e0) >> 3;
+#pragma unroll
+  for (int r = 0; r < kGroups; ++r) {
+    const int off = r * 512 + lane * 8;
+    uint4 G, P, M, V;
+    if (kFull) {
+      G = *reinterpret_cast<const uint4*>(gp + off);
+      P = *reinterpret_cast<const uint4*>(pp + off);
+      M = *reinterpret_cast<const uint4*>(mp + off);
+      V = *reinterpret_cast<const uint4*>(vp + off);
+    } else {
+      uint32_t a[4] = {0, 0, 0, 0}, b[4] = {0, 0, 0, 0}, c[4] = {0, 0, 0, 0}, e[4] = {0, 0, 0, 0};
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        if (off + j < valid) {
+          const int s = 16 * (j & 1);
+          a[j >> 1] |= static_cast<uint32_t>(gp[off + j]) << s;
+          b[j >> 1] |= static_cast<uint32_t>(pp[off + j]) << s;
+          c[j >> 1] |= static_cast<uint32_t>(mp[off + j]) << s;
+          e[j >> 1] |= static_cast<uint32_t>(vp[off + j]) << s;
+        }
+      }
+      G = make_uint4(a[0], a[1], a[2], a[3]);
+      P = make_uint4(b[0], b[1], b[2], b[3]);
+      M = make_uint4(c[0], c[1], c[2], c[3]);
+      V = make_uint4(e[0], e[1], e[2], e[3]);
+    }
+    const uint64_t grp = grp0 + (off >> 3);
+    Rand4 rp{{0, 0, 0, 0}};
+    if (!nearest) rp = group_bits(grp, 0u, d.tensor_id, sc);
+    const Rand4 rm = group_bits(grp, 1u, d.tensor_id, sc);
+    const Rand4 rv = group_bits(grp, 2u, d.tensor_id, sc);
+    uint32_t po[4] = {0, 0, 0, 0}, mo[4] = {0, 0, 0, 0}, vo[4] = {0, 0, 0, 0};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      float m2, v2;
+      const float pn = adamw(bf16_at(P, j), bf16_at(G, j), bf16_at(M, j), bf16_at(V, j), sc, m2, v2);
+      const int s = 16 * (j & 1);
+      po[j >> 1] |= to_bf16(pn, r16_of(rp, j), nearest) << s;
+      mo[j >> 1] |= to_bf16(m2, r16_of(rm, j), false) << s;
+      vo[j >> 1] |= to_bf16(v2, r16_of(rv, j), false) << s;
+    }
+    if (kFull) {
+      *reinterpret_cast<uint4*>(pp + off) = make_uint4(po[0], po[1], po[2], po[3]);
+      *reinterpret_cast<uint4*>(mp + off) = make_uint4(mo[0], mo[1], mo[2], mo[3]);
+      *reinterpret_cast<uint4*>(vp + off) = make_uint4(vo[0], vo[1], vo[2], vo[3]);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        if (off + j < valid) {
+          const int s = 16 * (j & 1);
+          pp[off + j] = static_cast<uint16_t>(po[j >> 1] >> s);
+          mp[off + j] = static_cast<uint16_t>(mo[j >> 1] >> s);
+          vp[off + j] = static_cast<uint16_t>(vo[j >> 1] >> s);
+        }
+      }
+    }
+  }
+}
+
+// ----------------------------------------------------------------------------- fp32 state
+template <bool kFull>
+__device__ __forceinline__ void block_fp32(const DevTensor& d, int64_t blk, int lane, int valid,
+                                           const StepScalars& sc) {
+  const int64_t e0 = blk * kBlock;
+  const uint16_t* gp = d.grad + e0;
+  uint16_t* pp = d.param + e0;
+  float* mp = static_cast<float*>(d.m) + e0;
+  float* vp = static_cast<float*>(d.v) + e0;
+  const bool nearest = sc.param_round != 0;
+  const uint64_t grp0 = static_cast<uint64_t>(d.index_base + e0) >> 3;
+#pragma unroll
+  for (int r = 0; r < kGroups; ++r) {
+    const int off = r * 512 + lane * 8;
+    uint4 G = make_uint4(0, 0, 0, 0), P = make_uint4(0, 0, 0, 0);
+    float M[8], V[8];
+    if (kFull) {
+      G = *reinterpret_cast<const uint4*>(gp + off);
+      P = *reinterpret_cast<const uint4*>(pp + off);
+      const float4 m0 = *reinterpret_cast<const float4*>(mp + off);
+      const float4 m1 = *reinterpret_cast<const float4*>(mp + off + 4);
+      const float4 v0 = *reinterpret_cast<const float4*>(vp + off);
+      const float4 v1 = *reinterpret_cast<const float4*>(vp + off + 4);
+      M[0] = m0.x; M[1] = m0.y; M[2] = m0.z; M[3] = m0.w;
+      M[4] = m1.x; M[5] = m1.y; M[6] = m1.z; M[7] = m1.w;
+      V[0] = v0.x; V[1] = v0.y; V[2] = v0.z; V[3] = v0.w;
+      V[4] = v1.x; V[5] = v1.y; V[6] = v1.z; V[7] = v1.w;
+    } else {
+      uint32_t a[4] = {0, 0, 0, 0}, b[4] = {0, 0, 0, 0};
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const bool ok = off + j < valid;
+        if (ok) {
+          a[j >> 1] |= static_cast<uint32_t>(gp[off + j]) << (16 * (j & 1));
+          b[j >> 1] |= static_cast<uint32_t>(pp[off + j]) << (16 * (j & 1));
+        }
+        M[j] = ok ? mp[off + j] : 0.0f;
+        V[j] = ok ? vp[off + j] : 0.0f;
+      }
+      G = make_uint4(a[0], a[1], a[2], a[3]);
+      P = make_uint4(b[0], b[1], b[2], b[3]);
+    }
+    Rand4 rp{{0, 0, 0, 0}};
+    if (!nearest) rp = group_bits(grp0 + (off >> 3), 0u, d.tensor_id, sc);
+    uint32_t po[4] = {0, 0, 0, 0};
+    float M2[8], V2[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float pn = adamw(bf16_at(P, j), bf16_at(G, j), M[j], V[j], sc, M2[j], V2[j]);
+      po[j >> 1] |= to_bf16(pn, r16_of(rp, j), nearest) << (16 * (j & 1));
+    }
+    if (kFull) {
+      *reinterpret_cast<uint4*>(pp + off) = make_uint4(po[0], po[1], po[2], po[3]);
+      *reinterpret_cast<float4*>(mp + off) = make_float4(M2[0], M2[1], M2[2], M2[3]);
+      *reinterpret_cast<float4*>(mp + off + 4) = make_float4(M2[4], M2[5], M2[6], M2[7]);
+      *reinterpret_cast<float4*>(vp + off) = make_float4(V2[0], V2[1], V2[2], V2[3]);
+      *reinterpret_cast<float4*>(vp + off + 4) = make_float4(V2[4], V2[5], V2[6], V2[7]);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        if (off + j < valid) {
+          pp[off + j] = static_cast<uint16_t>(po[j >> 1] >> (16 * (j & 1)));
+          mp[off + j] = M2[j];
+          vp[off + j] = V2[j];
+        }
+      }
+    }
+  }
+}
+
+// ----------------------------------------------------------------------------- driver
+template <Kind K>
+__global__ void __launch_bounds__(kThreads)
+step_kernel(const DevTensor* __restrict__ list, int ntensors, int64_t total_blocks, StepScalars sc) {
+  __shared__ float s_tab[(K == Kind::k8bit) ? kTableWords : 1];
+  if constexpr (K == Kind::k8bit) {
+    for (int i = threadIdx.x; i < kTableWords; i += kThreads) s_tab[i] = g_tables[i];
+    __syncthreads();
+  }
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+  const int64_t gw = static_cast<int64_t>(blockIdx.x) * kWaves + wave;
+  const int64_t nw = static_cast<int64_t>(gridDim.x) * kWaves;
+  int64_t b = total_blocks * gw / nw;
+  const int64_t bend = total_blocks * (gw + 1) / nw;
+  if (b >= bend) return;
+
+  // the tensor holding block b: the last one whose first block is <= b
+  int lo = 0, hi = ntensors - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (list[mid].block_begin <= b) lo = mid; else hi = mid - 1;
+  }
+  int t = lo;
+  DevTensor d = list[t];
+  for (; b < bend; ++b) {
+    while (b >= d.block_begin + static_cast<int64_t>(d.nblocks)) d = list[++t];
+    const int64_t blk = b - d.block_begin;
+    const int64_t left = d.numel - blk * kBlock;
+    const bool full = left >= kBlock;
+    const int valid = full ? kBlock : static_cast<int>(left);
+    if constexpr (K == Kind::k8bit) {
+      if (full) block_8bit<true>(d, blk, lane, valid, sc, s_tab);
+      else block_8bit<false>(d, blk, lane, valid, sc, s_tab);
+    } else if constexpr (K == Kind::kBf16) {
+      if (full) block_bf16<true>(d, blk, lane, valid, sc);
+      else block_bf16<false>(d, blk, lane, valid, sc);
+    } else {
+      if (full) block_fp32<true>(d, blk, lane, valid, sc);
+      else block_fp32<false>(d, blk, lane, valid, sc);
+    }
+  }
+}
+
+template <Kind K>
+hipError_t launch_kind(const DevTensor* list, int n, int64_t total_blocks, const StepScalars& sc,
+                       hipStream_t stream, int grid_cap) {
+  int64_t grid = (total_blocks + kWaves - 1) / kWaves;
+  if (grid_cap > 0 && grid > grid_cap) grid = grid_cap;
+  if (grid < 1) grid = 1;
+  hipLaunchKernelGGL(step_kernel<K>, dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0, stream,
+                     list, n, total_blocks, sc);
+  return hipGetLastError();
+}
+
+template <Kind K>
+int occupancy_kind() {
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, step_kernel<K>, kThreads, 0) != hipSuccess)
+    return 1;
+  return n > 0 ? n : 1;
+}
+
+}  // namespace
+
+hipError_t upload_tables(const float* host_tables) {
+  return hipMemcpyToSymbol(HIP_SYMBOL(g_tables), host_tables, sizeof(float) * kTableWords, 0,
+                           hipMemcpyHostToDevice);
+}
+
+hipError_t launch_step(Kind kind, const DevTensor* list, int n, int64_t total_blocks,
+                       const StepScalars& sc, hipStream_t stream, int grid_cap) {
+  if (n <= 0 || total_blocks <= 0) return hipSuccess;
+  switch (kind) {
+    case Kind::k8bit: return launch_kind<Kind::k8bit>(list, n, total_blocks, sc, stream, grid_cap);
+    case Kind::kBf16: return launch_kind<Kind::kBf16>(list, n, total_blocks, sc, stream, grid_cap);
+    case Kind::kFp32: return launch_kind<Kind::kFp32>(list, n, total_blocks, sc, stream, grid_cap);
+  }
+  return hipErrorInvalidValue;
+}
+
+int occupancy_per_cu(Kind kind) {
+  switch (kind) {
+    case Kind::k8bit: return occupancy_kind<Kind::k8bit>();
+    case Kind::kBf16: return occupancy_kind<Kind::kBf16>();
+    case Kind::kFp32: return occupancy_kind<Kind::kFp32>();
+  }
+  return 1;
+}
+
+}  // namespace opt8

@@ -1,0 +1,181 @@
+"""ctypes binding of libopt8 (include/opt8.h): argument marshalling only.
+
+Every step of the optimizer runs in the library's HIP kernels; this module
+only converts Python/torch objects to the C structs and raises on errors.
+It fails loudly when libopt8.so is missing: there is no CPU fallback.
+"""
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libopt8.so")
+
+OPT8_BLOCK = 2048
+OPT8_FP32_STATE_THRESHOLD = 4096
+OPT8_NUM_CODES = 256
+
+OPT8_OK = 0
+OPT8_E_NULL = -1
+OPT8_E_ALIGN = -2
+OPT8_E_SIZE = -3
+OPT8_E_MODE = -4
+OPT8_E_HPARAM = -5
+OPT8_E_ALIAS = -6
+OPT8_E_DUPID = -7
+OPT8_E_NOT_INIT = -8
+OPT8_E_HIP = -9
+
+OPT8_STATE_8BIT = 0
+OPT8_STATE_BF16_SR = 1
+OPT8_STATE_FP32 = 2
+
+OPT8_ROUND_STOCHASTIC = 0
+OPT8_ROUND_NEAREST = 1
+
+STATUS_NAMES = {0: "OPT8_OK", -1: "OPT8_E_NULL", -2: "OPT8_E_ALIGN", -3: "OPT8_E_SIZE",
+                -4: "OPT8_E_MODE", -5: "OPT8_E_HPARAM", -6: "OPT8_E_ALIAS", -7: "OPT8_E_DUPID",
+                -8: "OPT8_E_NOT_INIT", -9: "OPT8_E_HIP"}
+
+
+class opt8_tensor(ctypes.Structure):
+    _fields_ = [
+        ("param", ctypes.c_void_p),
+        ("grad", ctypes.c_void_p),
+        ("m", ctypes.c_void_p),
+        ("v", ctypes.c_void_p),
+        ("absmax_m", ctypes.c_void_p),
+        ("absmax_v", ctypes.c_void_p),
+        ("numel", ctypes.c_int64),
+        ("index_base", ctypes.c_int64),
+        ("tensor_id", ctypes.c_uint32),
+        ("mode", ctypes.c_int32),
+    ]
+
+
+class opt8_hparams(ctypes.Structure):
+    _fields_ = [
+        ("lr", ctypes.c_double),
+        ("beta1", ctypes.c_double),
+        ("beta2", ctypes.c_double),
+        ("eps", ctypes.c_double),
+        ("weight_decay", ctypes.c_double),
+        ("step", ctypes.c_int64),
+        ("seed", ctypes.c_uint64),
+        ("param_round", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
+    ]
+
+
+class Opt8Error(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libopt8.so; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with "
+                              "`python -m precision_optimizer_step_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        L.opt8_init_codebooks.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        L.opt8_init_codebooks.restype = ctypes.c_int
+        L.opt8_default_mode.argtypes = [ctypes.c_int64]
+        L.opt8_default_mode.restype = ctypes.c_int32
+        L.opt8_adamw_step.argtypes = [ctypes.POINTER(opt8_tensor), ctypes.c_int32,
+                                      ctypes.POINTER(opt8_hparams), ctypes.c_void_p]
+        L.opt8_adamw_step.restype = ctypes.c_int
+        L.opt8_last_error.argtypes = []
+        L.opt8_last_error.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def opt8_last_error() -> str:
+    return lib().opt8_last_error().decode()
+
+
+def _check(status: int) -> int:
+    if status != OPT8_OK:
+        raise Opt8Error(status, opt8_last_error())
+    return status
+
+
+def opt8_init_codebooks(signed_out=None, unsigned_out=None, check: bool = True) -> int:
+    """Upload the codebooks to the current device; optional float32[256] host outputs
+    (numpy arrays or anything exposing a writable buffer)."""
+    def ptr(a):
+        if a is None:
+            return None
+        if hasattr(a, "ctypes"):
+            assert a.dtype.name == "float32" and a.size == OPT8_NUM_CODES and a.flags["C_CONTIGUOUS"]
+            return a.ctypes.data
+        return ctypes.addressof(a)
+    rc = lib().opt8_init_codebooks(ptr(signed_out), ptr(unsigned_out))
+    return _check(rc) if check else rc
+
+
+def opt8_default_mode(numel: int) -> int:
+    return int(lib().opt8_default_mode(int(numel)))
+
+
+def make_hparams(lr, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.0, step=1, seed=0,
+                 param_round=OPT8_ROUND_STOCHASTIC) -> opt8_hparams:
+    return opt8_hparams(float(lr), float(beta1), float(beta2), float(eps), float(weight_decay),
+                        int(step), int(seed) & 0xFFFFFFFFFFFFFFFF, int(param_round), 0)
+
+
+def _addr(x):
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def make_tensor(param, grad, m, v, absmax_m=None, absmax_v=None, tensor_id=0,
+                mode=OPT8_STATE_8BIT, index_base=0, numel=None) -> opt8_tensor:
+    """Descriptor from torch tensors (or raw device addresses given as ints)."""
+    if numel is None:
+        numel = param.numel()
+    return opt8_tensor(_addr(param), _addr(grad), _addr(m), _addr(v), _addr(absmax_m),
+                       _addr(absmax_v), int(numel), int(index_base), int(tensor_id), int(mode))
+
+
+def tensor_array(descs) -> ctypes.Array:
+    """A C array of opt8_tensor, reusable across steps while the buffers live."""
+    descs = list(descs)
+    arr = (opt8_tensor * max(1, len(descs)))()
+    for i, d in enumerate(descs):
+        arr[i] = d
+    arr._n = len(descs)
+    return arr
+
+
+def opt8_adamw_step(tensors, hp: opt8_hparams, stream=None, n=None, check: bool = True) -> int:
+    """One fused step over a descriptor list (a list of opt8_tensor or tensor_array()).
+
+    stream: a torch.cuda.Stream, a raw hipStream_t int, or None for the current
+    torch stream (the null stream if torch is not in use).
+    """
+    if not isinstance(tensors, ctypes.Array):
+        tensors = tensor_array(tensors)
+    count = getattr(tensors, "_n", len(tensors)) if n is None else int(n)
+    if stream is None:
+        try:
+            import torch
+            handle = torch.cuda.current_stream().cuda_stream if torch.cuda.is_available() else 0
+        except ImportError:
+            handle = 0
+    elif isinstance(stream, int):
+        handle = stream
+    else:
+        handle = stream.cuda_stream
+    rc = lib().opt8_adamw_step(tensors, count, ctypes.byref(hp), ctypes.c_void_p(handle or None))
+    return _check(rc) if check else rc

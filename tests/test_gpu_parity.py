@@ -1,0 +1,275 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle, element by element.
+
+Sizes are chosen so the oracle finishes in seconds while spanning many blocks
+and ragged tails; the full-size 6.7B-shaped list is covered by sampled blocks
+in test_gpu_fullsize.py.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_helpers import DevTensorSet, compare_state, gpu_step, log, oracle_step, to_dev
+from precision_optimizer_step_amd import opt8
+from workloads import gen, shapes
+
+pytestmark = pytest.mark.gpu
+
+M8, MB, MF = oracle.MODE_8BIT, oracle.MODE_BF16_SR, oracle.MODE_FP32
+
+
+@pytest.fixture(scope="module", autouse=True)
+def device():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a visible AMD GPU")
+    torch.cuda.set_device(0)
+    opt8.opt8_init_codebooks()
+    log(f"device: {torch.cuda.get_device_name(0)}")
+
+
+def _rand_bf16(rng, n, sigma):
+    return gen.to_bf16_bits((rng.standard_normal(n) * sigma).astype(np.float32))
+
+
+def _zero_state(mode, n):
+    nb = (n + 2047) // 2048
+    if mode == M8:
+        return np.full(n, 127, np.uint8), np.zeros(n, np.uint8), np.zeros(nb, np.float32), np.zeros(nb, np.float32)
+    if mode == MB:
+        return np.zeros(n, np.uint16), np.zeros(n, np.uint16), None, None
+    return np.zeros(n, np.float32), np.zeros(n, np.float32), None, None
+
+
+def _rand_state(mode, n, seed, tid):
+    if mode == M8:
+        return gen.random_state_8bit(seed, tid, n)
+    if mode == MB:
+        return (*gen.random_state_bf16(seed, tid, n), None, None)
+    return (*gen.random_state_f32(seed, tid, n), None, None)
+
+
+def _run_and_compare(sets, states, hp, label, stats=None):
+    """One GPU step over the list vs the oracle per tensor; returns the oracle's states."""
+    gpu_step(sets, hp)
+    nxt = []
+    for s, st in zip(sets, states):
+        want = oracle_step(s, st, hp)
+        compare_state(f"{label}/t{s.tensor_id}", s.read(), want, s.mode, stats)
+        nxt.append(want)
+    return nxt
+
+
+def _force(sets, states):
+    """Overwrite the device state with the oracle's (keeps steps independent)."""
+    for s, (p, m, v, am, av) in zip(sets, states):
+        s.P.copy_(to_dev(p))
+        s.M.copy_(to_dev(m))
+        s.V.copy_(to_dev(v))
+        if s.AM is not None:
+            s.AM.copy_(to_dev(am))
+            s.AV.copy_(to_dev(av))
+
+
+# ----------------------------------------------------------------------------- workloads
+def test_single_tensor_1m_ten_steps():
+    """1,048,576 elements (512 blocks), zero state, fresh grads with 0.1% x100 outliers, 10 steps."""
+    w = shapes.single_tensor()
+    p = gen.param_init(w, 0)
+    m, v, am, av = _zero_state(M8, p.size)
+    s = DevTensorSet(M8, p, gen.grad_init(w, 1, 0), m, v, am, av, tensor_id=0)
+    state = [p, m, v, am, av]
+    stats = {}
+    for t in range(1, w.steps + 1):
+        s.set_grad(gen.grad_init(w, t, 0))
+        hp = oracle.Hparams(lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps,
+                            weight_decay=w.weight_decay, step=t, seed=w.seed)
+        state = _run_and_compare([s], [state], hp, f"single-1M step {t}", stats)[0]
+        log(f"single-1M step {t}: mismatches so far {sum(stats.values())}")
+    # the free-running trajectories also agree: nothing was forced above
+    assert sum(stats.values()) == 0, stats
+
+
+@pytest.mark.parametrize("param_round", [oracle.ROUND_STOCHASTIC, oracle.ROUND_NEAREST])
+def test_mixed_list_ragged_sizes(param_round):
+    """Tiny, ragged and multi-block tensors of all three modes in one list, random state."""
+    rng = np.random.default_rng(5 + param_round)
+    sizes = [1, 7, 8, 100, 2047, 2048, 2049, 4095, 4096, 6149, 20000, 3 * 2048 + 1024]
+    sets, states = [], []
+    tid = 0
+    for n in sizes:
+        for mode in (opt8.opt8_default_mode(n), M8, MB):
+            if mode == MF and n >= 4096:
+                continue
+            p = _rand_bf16(rng, n, 0.02)
+            g = _rand_bf16(rng, n, 1e-3)
+            m, v, am, av = _rand_state(mode, n, 9, tid)
+            base = 2048 * int(rng.integers(0, 1000)) if tid % 3 == 0 else 0
+            sets.append(DevTensorSet(mode, p, g, m, v, am, av, tensor_id=1000 + tid, index_base=base))
+            states.append([p, m, v, am, av])
+            tid += 1
+    log(f"mixed list: {len(sets)} tensors")
+    stats = {}
+    for t in (1, 2, 7):
+        for s in sets:
+            s.set_grad(_rand_bf16(rng, s.host[0].size, 1e-3))
+        hp = oracle.Hparams(lr=1e-3, weight_decay=0.1, step=t, seed=0xABCDEF0123456789,
+                            param_round=param_round)
+        states = _run_and_compare(sets, states, hp, f"mixed step {t}", stats)
+        _force(sets, states)
+    log(f"mixed list mismatches: {sum(stats.values())}")
+
+
+def test_gpt2_350m_first_last_layers_three_steps():
+    """GPT-2 350M list: wpe, every tensor of layers 0 and 23 and ln_f (fp32 state under 4096)."""
+    w = shapes.gpt2_350m()
+    keep = [i for i in shapes.subset_for_sampling(w) if w.tensors[i].name != "wte"]
+    sets, states = [], []
+    for tid in keep:
+        spec = w.tensors[tid]
+        mode = opt8.opt8_default_mode(spec.numel)
+        p = gen.param_init(w, tid)
+        m, v, am, av = _zero_state(mode, spec.numel)
+        sets.append(DevTensorSet(mode, p, gen.grad_init(w, 1, tid), m, v, am, av, tensor_id=tid))
+        states.append([p, m, v, am, av])
+    log(f"gpt2-350m subset: {len(sets)} tensors, {sum(s.host[0].size for s in sets)} elements")
+    stats = {}
+    for t in range(1, w.steps + 1):
+        for s in sets:
+            s.set_grad(gen.grad_init(w, t, s.tensor_id))
+        hp = oracle.Hparams(lr=w.lr, weight_decay=w.weight_decay, step=t, seed=w.seed)
+        states = _run_and_compare(sets, states, hp, f"gpt2 step {t}", stats)
+    log(f"gpt2 subset mismatches: {sum(stats.values())}")
+
+
+def test_lm_1p5b_nonuniform_grads():
+    """1.5B-shaped layer-0 tensors + a 2,000-row slice of the embedding with the sparse-row recipe."""
+    w = shapes.lm_1p5b()
+    sets, states = [], []
+    for tid, spec in enumerate(w.tensors):
+        if not spec.name.startswith("h0.") and spec.name not in ("ln_f.w", "ln_f.b"):
+            continue
+        mode = opt8.opt8_default_mode(spec.numel)
+        p = gen.param_init(w, tid)
+        m, v, am, av = _zero_state(mode, spec.numel)
+        sets.append(DevTensorSet(mode, p, gen.grad_init(w, 1, tid), m, v, am, av, tensor_id=tid))
+        states.append([p, m, v, am, av])
+    # sparse embedding rows: 5% of rows carry N(0, 1e-2) grads, the rest are exactly zero
+    rows, width = 2000, 1600
+    rng = np.random.default_rng(77)
+    emb = _rand_bf16(rng, rows * width, 0.02)
+    m, v, am, av = _zero_state(M8, rows * width)
+    sets.append(DevTensorSet(M8, emb, np.zeros(rows * width, np.uint16), m, v, am, av, tensor_id=0))
+    states.append([emb, m, v, am, av])
+    stats = {}
+    for t in range(1, w.steps + 1):
+        for s in sets[:-1]:
+            s.set_grad(gen.grad_init(w, t, s.tensor_id))
+        g = np.zeros((rows, width), np.float32)
+        pick = rng.choice(rows, 100, replace=False)
+        g[pick] = rng.standard_normal((100, width)).astype(np.float32) * np.float32(1e-2)
+        sets[-1].set_grad(gen.to_bf16_bits(g.reshape(-1)))
+        hp = oracle.Hparams(lr=w.lr, weight_decay=w.weight_decay, step=t, seed=w.seed)
+        states = _run_and_compare(sets, states, hp, f"lm-1.5b step {t}", stats)
+    log(f"lm-1.5b subset mismatches: {sum(stats.values())}")
+
+
+def test_gptneo_2p7b_bf16_state_mode():
+    """BF16-AdamW-SR: every tensor in bf16 state (layer 0 of the 2.7B list), 3 steps."""
+    w = shapes.gptneo_2p7b("bf16")
+    sets, states = [], []
+    for tid, spec in enumerate(w.tensors):
+        if not spec.name.startswith("h0."):
+            continue
+        p = gen.param_init(w, tid)
+        m, v, am, av = _zero_state(MB, spec.numel)
+        sets.append(DevTensorSet(MB, p, gen.grad_init(w, 1, tid), m, v, am, av, tensor_id=tid))
+        states.append([p, m, v, am, av])
+    stats = {}
+    for t in range(1, w.steps + 1):
+        for s in sets:
+            s.set_grad(gen.grad_init(w, t, s.tensor_id))
+        hp = oracle.Hparams(lr=w.lr, weight_decay=w.weight_decay, step=t, seed=w.seed)
+        states = _run_and_compare(sets, states, hp, f"bf16 step {t}", stats)
+    log(f"bf16-state mismatches: {sum(stats.values())}")
+
+
+# ----------------------------------------------------------------------------- edge cases
+def test_degenerate_blocks():
+    """All-zero grads and state, subnormal and huge grads, zero lr/wd, a lone element."""
+    rng = np.random.default_rng(3)
+    n = 2048 * 2 + 33
+    cases = []
+    p = _rand_bf16(rng, n, 0.02)
+    cases.append(("zero grads, zero state", p, np.zeros(n, np.uint16), _zero_state(M8, n)))
+    sub = (rng.integers(1, 0x7F, n) | (rng.integers(0, 2, n) << 15)).astype(np.uint16)  # bf16 subnormals
+    cases.append(("subnormal grads", p, sub, _zero_state(M8, n)))
+    big = _rand_bf16(rng, n, 1e3)
+    cases.append(("huge grads", p, big, _rand_state(M8, n, 3, 1)))
+    tiny_state = list(_rand_state(M8, n, 4, 2))
+    tiny_state[2] = np.full_like(tiny_state[2], 1e-39)        # subnormal absmax
+    cases.append(("subnormal absmax", p, _rand_bf16(rng, n, 1e-30), tuple(tiny_state)))
+    cases.append(("lone element", _rand_bf16(rng, 1, 0.5), _rand_bf16(rng, 1, 1e-3), _zero_state(M8, 1)))
+    for k, (label, pp, gg, st) in enumerate(cases):
+        s = DevTensorSet(M8, pp, gg, *st, tensor_id=k)
+        for hp in (oracle.Hparams(lr=1e-3, weight_decay=0.1, step=1, seed=1),
+                   oracle.Hparams(lr=0.0, weight_decay=0.0, step=4, seed=1)):
+            want = oracle_step(s, [pp, *st], hp)
+            s2 = DevTensorSet(M8, pp, gg, *st, tensor_id=k)
+            gpu_step([s2], hp)
+            compare_state(label, s2.read(), want, M8)
+            if hp.lr == 0.0:
+                assert np.array_equal(s2.read()[0], pp), "zero lr and wd must leave params untouched"
+        log(f"degenerate case ok: {label}")
+
+
+def test_determinism_list_independence_and_resume():
+    rng = np.random.default_rng(8)
+    n = 2048 * 5 + 77
+    p = _rand_bf16(rng, n, 0.02)
+    grads = [_rand_bf16(rng, n, 1e-3) for _ in range(4)]
+    st = _zero_state(M8, n)
+    other_p = _rand_bf16(rng, 3000, 0.02)
+
+    def run(with_other, split):
+        s = DevTensorSet(M8, p, grads[0], *st, tensor_id=3)
+        o = DevTensorSet(MF, other_p, _rand_bf16(np.random.default_rng(1), 3000, 1e-3),
+                         *_zero_state(MF, 3000), tensor_id=4)
+        for t in range(1, 5):
+            s.set_grad(grads[t - 1])
+            hp = oracle.Hparams(lr=1e-3, weight_decay=0.01, step=t, seed=99)
+            gpu_step([s, o] if with_other else [s], hp)
+            if split and t == 2:          # checkpoint: state to host and back into fresh buffers
+                cur = s.read()
+                s = DevTensorSet(M8, cur[0], grads[t - 1], cur[1], cur[2], cur[3], cur[4], tensor_id=3)
+        return s.read()
+
+    a = run(False, False)
+    b = run(False, False)
+    c = run(True, False)
+    d = run(False, True)
+    for x in (b, c, d):
+        for u, w in zip(a, x):
+            assert np.array_equal(u, w)
+
+
+def test_index_base_equals_shard_of_a_larger_tensor():
+    """A shard stepped with its global index base equals that slice of the whole tensor."""
+    rng = np.random.default_rng(12)
+    n = 2048 * 8 + 500
+    p = _rand_bf16(rng, n, 0.02)
+    g = _rand_bf16(rng, n, 1e-3)
+    st = _rand_state(M8, n, 5, 5)
+    hp = oracle.Hparams(lr=1e-3, weight_decay=0.01, step=3, seed=5)
+    whole = DevTensorSet(M8, p, g, *st, tensor_id=11)
+    gpu_step([whole], hp)
+    cut = 2048 * 3
+    qm, qv, am, av = st
+    shard = DevTensorSet(M8, p[cut:], g[cut:], qm[cut:], qv[cut:], am[3:], av[3:],
+                         tensor_id=11, index_base=cut)
+    gpu_step([shard], hp)
+    w = whole.read()
+    s = shard.read()
+    assert np.array_equal(w[0][cut:], s[0])
+    assert np.array_equal(w[1][cut:], s[1]) and np.array_equal(w[2][cut:], s[2])
+    assert np.array_equal(w[3][3:], s[3]) and np.array_equal(w[4][3:], s[4])
