@@ -41,7 +41,7 @@ def parse():
     ap.add_argument("--workload", default="gptneo-6.7b")
     ap.add_argument("--grad-pool", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-elems", type=int, default=8 * 1024 * 1024)
+    ap.add_argument("--cpu-sample-elems", type=int, default=96 * 1024 * 1024)
     return ap.parse_args()
 
 

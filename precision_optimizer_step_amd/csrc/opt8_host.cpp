@@ -74,8 +74,50 @@ void tree_levels(int magnitude_bits, bool negative_too, std::vector<float>& out)
 }
 
 struct Tables {
-  float words[kTableWords];
+  alignas(16) uint8_t bytes[kTableBytes];
+  const float* cb_s() const { return reinterpret_cast<const float*>(bytes + kOffCbS); }
+  const float* cb_u() const { return reinterpret_cast<const float*>(bytes + kOffCbU); }
+  bool ok = false;
 };
+
+// #{k : mid[k] < x} over the 255 midpoints.
+int count_below(const float* mid, float x) {
+  int c = 0;
+  while (c < kCodes - 1 && mid[c] < x) ++c;
+  return c;
+}
+
+float bits_f32(uint32_t b) {
+  float f;
+  std::memcpy(&f, &b, 4);
+  return f;
+}
+
+// Code LUTs: the fp32 values sharing the top 16 bits (sign, exponent, 7
+// mantissa bits) of a key form a bucket; magnitudes below 2^-27 join the
+// lowest bucket.  Each entry is the code of the bucket's smallest value; a
+// bucket may contain at most one midpoint (checked here), so a value's code is
+// the entry plus one exactly when it lies above the midpoint the entry indexes.
+bool build_luts(uint8_t* bytes) {
+  const float* mid_s = reinterpret_cast<const float*>(bytes + kOffMidS);
+  const float* mid_u = reinterpret_cast<const float*>(bytes + kOffMidU);
+  for (uint32_t key = kKeyLo; key <= kKeyHi; ++key) {
+    const float lo = key == kKeyLo ? 0.0f : bits_f32(key << 16);
+    const float hi = bits_f32((key << 16) | 0xFFFFu);
+    struct { const float* mid; float least, most; int at; } cases[3] = {
+        {mid_u, lo, hi, static_cast<int>(key)},                            // unsigned, n >= 0
+        {mid_s, lo, hi, static_cast<int>(key) + kLutN},                    // signed, n >= 0
+        {mid_s, -hi, -lo, static_cast<int>(key) + 2 * kLutN}};             // signed, n < 0
+    for (const auto& c : cases) {
+      const int base = count_below(c.mid, c.least);
+      // the largest count in the bucket is reached at its largest value
+      const int top = count_below(c.mid, c.most);
+      if (top - base > 1) return false;
+      bytes[kOffLutU - static_cast<int>(kKeyLo) + c.at] = static_cast<uint8_t>(base);
+    }
+  }
+  return true;
+}
 
 Tables build_tables() {
   std::vector<float> s, u;
@@ -87,14 +129,19 @@ Tables build_tables() {
   std::sort(s.begin(), s.end());
   std::sort(u.begin(), u.end());
   Tables t;
-  auto fill = [&](const std::vector<float>& c, float* tab, float* mid) {
+  std::memset(t.bytes, 0, sizeof t.bytes);
+  auto fill = [&](const std::vector<float>& c, int off_tab, int off_mid) {
+    float tab[kCodes], mid[kCodes];
     for (int k = 0; k < kCodes; ++k) tab[k] = c[k];
     for (int k = 0; k + 1 < kCodes; ++k)   // neighbours sum exactly in double
       mid[k] = static_cast<float>((static_cast<double>(c[k]) + static_cast<double>(c[k + 1])) * 0.5);
     mid[kCodes - 1] = INFINITY;
+    std::memcpy(t.bytes + off_tab, tab, sizeof tab);
+    std::memcpy(t.bytes + off_mid, mid, sizeof mid);
   };
-  fill(s, t.words, t.words + kCodes);
-  fill(u, t.words + 2 * kCodes, t.words + 3 * kCodes);
+  fill(s, kOffCbS, kOffMidS);
+  fill(u, kOffCbU, kOffMidU);
+  t.ok = s.size() == kCodes && u.size() == kCodes && build_luts(t.bytes);
   return t;
 }
 
@@ -224,6 +271,7 @@ int validate_tensors(const opt8_tensor* t, int32_t n) {
 // passed again (the usual training loop) is launched without a new upload.
 constexpr int kSlots = 4;
 constexpr int kMaxDevices = 64;
+constexpr int kKinds = 4;
 
 struct Slot {
   DevTensor* dev = nullptr;
@@ -239,7 +287,7 @@ struct Slot {
 struct DeviceState {
   bool init = false;
   int num_cu = 0;
-  int occ[3] = {1, 1, 1};
+  int occ[kKinds] = {1, 1, 1, 1};
   Slot slots[kSlots];
   uint64_t clock = 0;
   PowCache pow;
@@ -327,18 +375,19 @@ using namespace opt8;
 extern "C" int opt8_init_codebooks(float* signed_out, float* unsigned_out) {
   std::lock_guard<std::mutex> lock(g_mu);
   const Tables& t = tables();
-  if (signed_out) std::memcpy(signed_out, t.words, sizeof(float) * kCodes);
-  if (unsigned_out) std::memcpy(unsigned_out, t.words + 2 * kCodes, sizeof(float) * kCodes);
+  if (signed_out) std::memcpy(signed_out, t.cb_s(), sizeof(float) * kCodes);
+  if (unsigned_out) std::memcpy(unsigned_out, t.cb_u(), sizeof(float) * kCodes);
+  if (!t.ok) return fail(OPT8_E_HIP, "internal error: code lookup tables failed their construction check");
   int dev = 0;
   int rc = current_device(dev);
   if (rc != OPT8_OK) return rc;
   DeviceState& ds = g_dev[dev];
   if (ds.init) return OPT8_OK;
-  hipError_t e = upload_tables(t.words);
+  hipError_t e = upload_tables(t.bytes);
   if (e != hipSuccess) return hip_fail(e, "upload of codebooks");
   e = hipDeviceGetAttribute(&ds.num_cu, hipDeviceAttributeMultiprocessorCount, dev);
   if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute(CU count)");
-  for (int k = 0; k < 3; ++k) ds.occ[k] = occupancy_per_cu(static_cast<Kind>(k));
+  for (int k = 0; k < kKinds; ++k) ds.occ[k] = occupancy_per_cu(static_cast<Kind>(k));
   for (Slot& s : ds.slots) {
     if (!s.done) {
       e = hipEventCreateWithFlags(&s.done, hipEventDisableTiming);
@@ -376,30 +425,37 @@ extern "C" int opt8_adamw_step(const opt8_tensor* tensors, int32_t n, const opt8
   DeviceState& ds = g_dev[dev];
   if (!ds.init) return fail(OPT8_E_NOT_INIT, "opt8_init_codebooks has not run on device %d", dev);
 
-  // one sub-list per state mode, each with its own block numbering
+  // one sub-list per kernel, each with its own block numbering: full blocks of
+  // 8-bit tensors, bf16-state tensors, fp32-state tensors, and the partial last
+  // block of 8-bit tensors
   std::vector<DevTensor> list;
-  list.reserve(static_cast<size_t>(n));
-  int count[3] = {0, 0, 0};
-  int64_t blocks[3] = {0, 0, 0};
-  int first[3] = {0, 0, 0};
-  for (int kind = 0; kind < 3; ++kind) {
+  list.reserve(static_cast<size_t>(n) * 2);
+  int count[kKinds] = {0, 0, 0, 0};
+  int64_t blocks[kKinds] = {0, 0, 0, 0};
+  int first[kKinds] = {0, 0, 0, 0};
+  for (int kind = 0; kind < kKinds; ++kind) {
     first[kind] = static_cast<int>(list.size());
+    const int mode = kind == static_cast<int>(Kind::k8bitTail) ? OPT8_STATE_8BIT : kind;
     for (int32_t i = 0; i < n; ++i) {
       const opt8_tensor& x = tensors[i];
-      if (x.mode != kind) continue;
+      if (x.mode != mode) continue;
+      int64_t nb = nblocks_of(x.numel);
+      if (kind == static_cast<int>(Kind::k8bit)) nb = x.numel / kBlock;
+      if (kind == static_cast<int>(Kind::k8bitTail)) nb = (x.numel % kBlock) ? 1 : 0;
+      if (nb == 0) continue;
       DevTensor d;
       d.param = x.param;
       d.grad = x.grad;
       d.m = x.m;
       d.v = x.v;
-      d.amax_m = kind == OPT8_STATE_8BIT ? x.absmax_m : nullptr;
-      d.amax_v = kind == OPT8_STATE_8BIT ? x.absmax_v : nullptr;
+      d.amax_m = mode == OPT8_STATE_8BIT ? x.absmax_m : nullptr;
+      d.amax_v = mode == OPT8_STATE_8BIT ? x.absmax_v : nullptr;
       d.numel = x.numel;
       d.index_base = x.index_base;
       d.block_begin = blocks[kind];
       d.tensor_id = x.tensor_id;
-      d.nblocks = static_cast<uint32_t>(nblocks_of(x.numel));
-      blocks[kind] += d.nblocks;
+      d.nblocks = static_cast<uint32_t>(nb);
+      blocks[kind] += nb;
       ++count[kind];
       list.push_back(d);
     }
@@ -409,7 +465,7 @@ extern "C" int opt8_adamw_step(const opt8_tensor* tensors, int32_t n, const opt8
   rc = acquire_slot(ds, list, stream, slot);
   if (rc != OPT8_OK) return rc;
   const StepScalars sc = make_scalars(*hp, ds.pow);
-  for (int kind = 0; kind < 3; ++kind) {
+  for (int kind = 0; kind < kKinds; ++kind) {
     if (!count[kind]) continue;
     const int cap = ds.num_cu * ds.occ[kind];
     const hipError_t e = launch_step(static_cast<Kind>(kind), slot->dev + first[kind], count[kind],

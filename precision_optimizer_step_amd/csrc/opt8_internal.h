@@ -35,15 +35,32 @@ struct StepScalars {
   int32_t param_round;   // 0 stochastic, 1 nearest-even
 };
 
-// Host-built lookup tables uploaded once per device.  Layout (fp32 words):
-// [0,256) signed codebook, [256,512) signed midpoints (255 + padding),
-// [512,768) unsigned codebook, [768,1024) unsigned midpoints.
-constexpr int kTableWords = 4 * kCodes;
+// Host-built lookup tables, uploaded once per device and staged by every
+// workgroup into LDS with the same byte layout:
+//   [0, 1024)      signed codebook (fp32[256], ascending)
+//   [1024, 2048)   signed midpoints (fp32[255], then +inf)
+//   [2048, 3072)   unsigned codebook
+//   [3072, 4096)   unsigned midpoints (fp32[255], then +inf)
+//   [4096, 12288)  per-wave scratch in LDS only (block-scaled codebooks)
+//   [12800, ...)   code LUTs (u8): for a non-negative fp32 n with top-16-bit key
+//                  k = max(bits(n) >> 16, kKeyLo), the number of midpoints below
+//                  the smallest value of that key's bucket; unsigned table at
+//                  byte k, signed table at byte k + kLutN (n >= 0) or
+//                  k + 2*kLutN (n < 0, bucket of |n|).  Every bucket holds at
+//                  most one midpoint, so code = lut + (mid[lut] < n) exactly.
+constexpr uint32_t kKeyLo = 100u << 7;      // |n| < 2^-27 share the lowest bucket
+constexpr uint32_t kKeyHi = 0x3F80u;        // bucket of [1, 1 + 2^-7): |n| <= 1 + 2^-22
+constexpr int kLutN = static_cast<int>(kKeyHi - kKeyLo + 1);
+constexpr int kOffCbS = 0, kOffMidS = 1024, kOffCbU = 2048, kOffMidU = 3072;
+constexpr int kOffWave = 4096;
+constexpr int kWaveScratch = 2048;          // Tm[256], Tv[256] fp32
+constexpr int kOffLutU = static_cast<int>(kKeyLo);
+constexpr int kTableBytes = ((kOffLutU + 3 * kLutN) + 15) / 16 * 16;
 
-enum class Kind : int { k8bit = 0, kBf16 = 1, kFp32 = 2 };
+enum class Kind : int { k8bit = 0, kBf16 = 1, kFp32 = 2, k8bitTail = 3 };
 
 // Kernel side (opt8_kernels.hip).
-hipError_t upload_tables(const float* host_tables);   // to the current device
+hipError_t upload_tables(const uint8_t* host_tables);   // kTableBytes, to the current device
 hipError_t launch_step(Kind kind, const DevTensor* dev_list, int ntensors, int64_t total_blocks,
                        const StepScalars& sc, hipStream_t stream, int grid_cap);
 // Workgroups per CU that the kernel of this kind can keep resident.

@@ -7,24 +7,29 @@
 // is one contiguous 1 KiB (bf16, 16 B per lane) or 512 B (codes, 8 B per lane)
 // segment, and one Philox call per lane and r yields the 8 random 16-bit words
 // of those 8 elements.  A block's absmax is a max, reduced across the wave
-// with cross-lane shuffles, so it is exact and independent of order.
+// with cross-lane shuffles, so it is exact and independent of order; no
+// workgroup barrier is needed inside the block loop.
 //
 // Waves of a persistent grid take contiguous runs of blocks over the whole
-// tensor list; each workgroup stages the codebooks and midpoints in LDS once.
+// tensor list; each workgroup stages the codebooks, midpoints and code LUTs in
+// LDS once.
 //
-// Arithmetic follows the step exactly as the oracle states it: fp32, one
-// rounding per operation (built with -ffp-contract=off), IEEE sqrt and divide,
-// denormals kept.
+// Arithmetic is the step exactly as the oracle states it: fp32, one rounding
+// per operation (built with -ffp-contract=off), IEEE sqrt and divide,
+// denormals kept.  The fast 8-bit path reaches the same bits with cheaper
+// instruction sequences whose exactness holds inside a range the block is
+// checked against; a block outside it takes the plain path.
 #include "opt8_internal.h"
 
 namespace opt8 {
 namespace {
 
-constexpr int kWaves = 4;                 // waves per workgroup
+constexpr int kWaves = 4;                   // waves per workgroup
 constexpr int kThreads = 64 * kWaves;
 constexpr int kGroups = kBlock / (64 * 8);  // 8-element groups per lane per block (4)
+constexpr float kMinNormal = 1.17549435e-38f;  // 2^-126
 
-__device__ float g_tables[kTableWords];
+__device__ uint4 g_tables[kTableBytes / 16];
 
 // Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11): two 32x32->64 products per
 // round, the words permuted and xored with the round key, key bumped by the
@@ -38,14 +43,19 @@ struct Rand4 {
   uint32_t w[4];
 };
 
+// The key is uniform across the wave: it lives in scalar registers and is
+// bumped on the scalar unit round by round (the empty asm keeps the compiler
+// from precomputing all twenty round keys, which would spill).
 __device__ __forceinline__ Rand4 philox10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3,
                                           uint32_t k0, uint32_t k1) {
 #pragma unroll
   for (int r = 0; r < 10; ++r) {
+    asm volatile("" : "+s"(k0), "+s"(k1));
     const uint64_t p0 = static_cast<uint64_t>(kPhiloxM0) * c0;
     const uint64_t p1 = static_cast<uint64_t>(kPhiloxM1) * c2;
-    const uint32_t n0 = static_cast<uint32_t>(p1 >> 32) ^ c1 ^ k0;
-    const uint32_t n2 = static_cast<uint32_t>(p0 >> 32) ^ c3 ^ k1;
+    // three-input xor in one instruction (truth table 0x96)
+    const uint32_t n0 = __builtin_amdgcn_bitop3_b32(static_cast<uint32_t>(p1 >> 32), c1, k0, 0x96);
+    const uint32_t n2 = __builtin_amdgcn_bitop3_b32(static_cast<uint32_t>(p0 >> 32), c3, k1, 0x96);
     c1 = static_cast<uint32_t>(p1);
     c3 = static_cast<uint32_t>(p0);
     c0 = n0;
@@ -71,22 +81,31 @@ __device__ __forceinline__ uint32_t r16_of(const Rand4& r, int j) {
 // truncate) or nearest-even; NaN becomes the quiet NaN with its sign.
 __device__ __forceinline__ uint32_t to_bf16(float x, uint32_t r16, bool nearest) {
   const uint32_t b = __float_as_uint(x);
-  if ((b & 0x7FFFFFFFu) > 0x7F800000u) return 0x7FC0u | ((b >> 16) & 0x8000u);
   const uint32_t add = nearest ? (0x7FFFu + ((b >> 16) & 1u)) : r16;
-  return (b + add) >> 16;
+  const uint32_t rounded = (b + add) >> 16;
+  const uint32_t qnan = 0x7FC0u | ((b >> 16) & 0x8000u);
+  return (x != x) ? qnan : rounded;
 }
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+__device__ __forceinline__ uint32_t word_of(const uint4& q, int k) {
+  return (k == 0) ? q.x : (k == 1) ? q.y : (k == 2) ? q.z : q.w;
+}
 __device__ __forceinline__ float bf16_at(const uint4& q, int j) {
-  const uint32_t w = (j < 2) ? q.x : (j < 4) ? q.y : (j < 6) ? q.z : q.w;
+  const uint32_t w = word_of(q, j >> 1);
   return (j & 1) ? bf16_hi(w) : bf16_lo(w);
 }
 __device__ __forceinline__ uint32_t byte_at(const uint2& q, int j) {
   return (((j < 4) ? q.x : q.y) >> (8 * (j & 3))) & 0xFFu;
 }
 
-// AdamW on one element; returns the new fp32 parameter and the new moments.
+// Max that keeps NaN once seen (the oracle's numpy max propagates NaN).
+__device__ __forceinline__ float nan_max(float acc, float x) {
+  return (x > acc || x != x) ? x : acc;
+}
+
+// AdamW on one element with IEEE sqrt and divide; returns the new fp32 parameter.
 __device__ __forceinline__ float adamw(float p, float g, float m1, float v1, const StepScalars& sc,
                                        float& m2, float& v2) {
   m2 = sc.beta1 * m1 + sc.w1 * g;
@@ -95,13 +114,42 @@ __device__ __forceinline__ float adamw(float p, float g, float m1, float v1, con
   return (p - sc.lrwd * p) - sc.step_size * (m2 / den);
 }
 
+// Correctly rounded sqrt for x == +0 or 2^-96 <= x < inf: the hardware square
+// root corrected by the sign of the residuals of its two neighbours.  Outside
+// that range (where the residuals could underflow) the plain sqrtf is used.
+__device__ __forceinline__ float sqrt_rn(float x) {
+  const float s = __builtin_amdgcn_sqrtf(x);
+  const float sm = __uint_as_float(__float_as_uint(s) - 1u);
+  const float sp = __uint_as_float(__float_as_uint(s) + 1u);
+  const float rm = __builtin_fmaf(-sm, s, x);
+  const float rp = __builtin_fmaf(-sp, s, x);
+  float r = (rm <= 0.0f) ? sm : s;
+  r = (rp > 0.0f) ? sp : r;
+  return r;
+}
+
+// Correctly rounded a / d by a refined reciprocal and two residual
+// corrections, valid when a == +-0 or 2^-100 < |a/d| and |a| and d are normal
+// and far from overflow (no operand or residual leaves the normal range).
+// Residuals are kept negated so a zero quotient keeps the sign of a.
+__device__ __forceinline__ float div_rn(float a, float d) {
+  const float r0 = __builtin_amdgcn_rcpf(d);
+  const float e = __builtin_fmaf(-d, r0, 1.0f);
+  const float r = __builtin_fmaf(e, r0, r0);
+  const float q0 = a * r;
+  const float t0 = __builtin_fmaf(d, q0, -a);
+  const float q1 = __builtin_fmaf(-t0, r, q0);
+  const float t1 = __builtin_fmaf(d, q1, -a);
+  return __builtin_fmaf(-t1, r, q1);
+}
+
 // Number of midpoints strictly below n (255 sorted midpoints): the nearest
-// codebook entry, ties to the lower code.  Branchless binary search.
-__device__ __forceinline__ uint32_t code_of(float n, const float* mid) {
+// codebook entry, ties to the lower code; NaN sorts above everything.
+__device__ __forceinline__ uint32_t code_search(float n, const float* mid) {
   uint32_t idx = 0;
 #pragma unroll
   for (uint32_t s = 128; s >= 1; s >>= 1) idx += (mid[idx + s - 1] < n) ? s : 0u;
-  return idx;
+  return (n != n) ? 255u : idx;
 }
 
 __device__ __forceinline__ float wave_max(float x) {
@@ -110,10 +158,23 @@ __device__ __forceinline__ float wave_max(float x) {
   return x;
 }
 
-// ----------------------------------------------------------------------------- 8-bit state
+__device__ __forceinline__ float wave_nan_max(float x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x = nan_max(x, __shfl_xor(x, o, 64));
+  return x;
+}
+
+// ----------------------------------------------------------------------------- 8-bit, plain path
+// Every block whose values leave the fast path's range, every partial block,
+// and every non-finite case: IEEE operations, binary search over the
+// midpoints, NaN-propagating block max.
 template <bool kFull>
-__device__ __forceinline__ void block_8bit(const DevTensor& d, int64_t blk, int lane, int valid,
-                                           const StepScalars& sc, const float* s_tab) {
+__device__ __forceinline__ void block_8bit_plain(const DevTensor& d, int64_t blk, int lane, int valid,
+                                              const StepScalars& sc, const uint8_t* lds) {
+  const float* cb_s = reinterpret_cast<const float*>(lds + kOffCbS);
+  const float* mid_s = reinterpret_cast<const float*>(lds + kOffMidS);
+  const float* cb_u = reinterpret_cast<const float*>(lds + kOffCbU);
+  const float* mid_u = reinterpret_cast<const float*>(lds + kOffMidU);
   const int64_t e0 = blk * kBlock;
   const uint16_t* gp = d.grad + e0;
   uint16_t* pp = d.param + e0;
@@ -123,16 +184,19 @@ __device__ __forceinline__ void block_8bit(const DevTensor& d, int64_t blk, int 
   const float av = d.amax_v[blk];
   const bool nearest = sc.param_round != 0;
 
-  uint4 G[kGroups], P[kGroups];
-  uint2 QM[kGroups], QV[kGroups];
+  float M2[kGroups * 8], V2[kGroups * 8];
+  float mxm = 0.0f, mxv = 0.0f;
+  const uint64_t grp0 = static_cast<uint64_t>(d.index_base + e0) >> 3;
 #pragma unroll
   for (int r = 0; r < kGroups; ++r) {
     const int off = r * 512 + lane * 8;
+    uint4 G, P;
+    uint2 QM, QV;
     if (kFull) {
-      G[r] = *reinterpret_cast<const uint4*>(gp + off);
-      P[r] = *reinterpret_cast<const uint4*>(pp + off);
-      QM[r] = *reinterpret_cast<const uint2*>(mp + off);
-      QV[r] = *reinterpret_cast<const uint2*>(vp + off);
+      G = *reinterpret_cast<const uint4*>(gp + off);
+      P = *reinterpret_cast<const uint4*>(pp + off);
+      QM = *reinterpret_cast<const uint2*>(mp + off);
+      QV = *reinterpret_cast<const uint2*>(vp + off);
     } else {
       uint32_t g32[4] = {0, 0, 0, 0}, p32[4] = {0, 0, 0, 0}, m32[2] = {0, 0}, v32[2] = {0, 0};
 #pragma unroll
@@ -144,36 +208,26 @@ __device__ __forceinline__ void block_8bit(const DevTensor& d, int64_t blk, int 
           v32[j >> 2] |= static_cast<uint32_t>(vp[off + j]) << (8 * (j & 3));
         }
       }
-      G[r] = make_uint4(g32[0], g32[1], g32[2], g32[3]);
-      P[r] = make_uint4(p32[0], p32[1], p32[2], p32[3]);
-      QM[r] = make_uint2(m32[0], m32[1]);
-      QV[r] = make_uint2(v32[0], v32[1]);
+      G = make_uint4(g32[0], g32[1], g32[2], g32[3]);
+      P = make_uint4(p32[0], p32[1], p32[2], p32[3]);
+      QM = make_uint2(m32[0], m32[1]);
+      QV = make_uint2(v32[0], v32[1]);
     }
-  }
-
-  float M2[kGroups * 8], V2[kGroups * 8];
-  float mxm = 0.0f, mxv = 0.0f;
-  const uint64_t grp0 = static_cast<uint64_t>(d.index_base + e0) >> 3;
-#pragma unroll
-  for (int r = 0; r < kGroups; ++r) {
-    const int off = r * 512 + lane * 8;
     Rand4 rnd{{0, 0, 0, 0}};
     if (!nearest) rnd = group_bits(grp0 + (off >> 3), 0u, d.tensor_id, sc);
     uint32_t outw[4] = {0, 0, 0, 0};
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const float g = bf16_at(G[r], j);
-      const float p = bf16_at(P[r], j);
-      const float m1 = s_tab[byte_at(QM[r], j)] * am;
-      const float v1 = s_tab[2 * kCodes + byte_at(QV[r], j)] * av;
+      const float m1 = cb_s[byte_at(QM, j)] * am;
+      const float v1 = cb_u[byte_at(QV, j)] * av;
       float m2, v2;
-      const float pn = adamw(p, g, m1, v1, sc, m2, v2);
+      const float pn = adamw(bf16_at(P, j), bf16_at(G, j), m1, v1, sc, m2, v2);
       outw[j >> 1] |= to_bf16(pn, r16_of(rnd, j), nearest) << (16 * (j & 1));
       const bool ok = kFull || (off + j < valid);
       M2[r * 8 + j] = ok ? m2 : 0.0f;
       V2[r * 8 + j] = ok ? v2 : 0.0f;
-      mxm = fmaxf(mxm, fabsf(M2[r * 8 + j]));
-      mxv = fmaxf(mxv, V2[r * 8 + j]);
+      mxm = nan_max(mxm, fabsf(M2[r * 8 + j]));
+      mxv = nan_max(mxv, V2[r * 8 + j]);
     }
     if (kFull) {
       *reinterpret_cast<uint4*>(pp + off) = make_uint4(outw[0], outw[1], outw[2], outw[3]);
@@ -184,23 +238,20 @@ __device__ __forceinline__ void block_8bit(const DevTensor& d, int64_t blk, int 
     }
   }
 
-  mxm = wave_max(mxm);
-  mxv = wave_max(mxv);
-  const float kMinNormal = 1.17549435e-38f;   // 2^-126
+  mxm = wave_nan_max(mxm);
+  mxv = wave_nan_max(mxv);
   const bool live_m = mxm >= kMinNormal;
   const bool live_v = mxv >= kMinNormal;
   const float inv_m = live_m ? 1.0f / mxm : 0.0f;
   const float inv_v = live_v ? 1.0f / mxv : 0.0f;
-  const float* mid_s = s_tab + kCodes;
-  const float* mid_u = s_tab + 3 * kCodes;
 #pragma unroll
   for (int r = 0; r < kGroups; ++r) {
     const int off = r * 512 + lane * 8;
     uint32_t cm[2] = {0, 0}, cv[2] = {0, 0};
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const uint32_t qm = live_m ? code_of(M2[r * 8 + j] * inv_m, mid_s) : 127u;
-      const uint32_t qv = live_v ? code_of(V2[r * 8 + j] * inv_v, mid_u) : 0u;
+      const uint32_t qm = live_m ? code_search(M2[r * 8 + j] * inv_m, mid_s) : 127u;
+      const uint32_t qv = live_v ? code_search(V2[r * 8 + j] * inv_v, mid_u) : 0u;
       cm[j >> 2] |= qm << (8 * (j & 3));
       cv[j >> 2] |= qv << (8 * (j & 3));
     }
@@ -221,6 +272,146 @@ __device__ __forceinline__ void block_8bit(const DevTensor& d, int64_t blk, int 
     d.amax_m[blk] = mxm;
     d.amax_v[blk] = mxv;
   }
+}
+
+// ----------------------------------------------------------------------------- 8-bit, fast path
+// Codes through the bucket LUTs: code = lut[key] + (mid[lut[key]] < n).
+__device__ __forceinline__ uint32_t code_u(float n, const uint8_t* lds, const float* mid) {
+  const uint32_t b = __float_as_uint(n);
+  const uint32_t key = max(b >> 16, kKeyLo);              // n >= 0
+  const uint32_t c = lds[key];                             // kOffLutU + key - kKeyLo == key
+  return c + ((mid[c] < n) ? 1u : 0u);
+}
+
+__device__ __forceinline__ uint32_t code_s(float n, const uint8_t* lds, const float* mid) {
+  const uint32_t b = __float_as_uint(n);
+  const uint32_t key = max((b >> 16) & 0x7FFFu, kKeyLo);
+  const uint32_t c = lds[key + static_cast<uint32_t>(kLutN) * (1u + (b >> 31))];
+  return c + ((mid[c] < n) ? 1u : 0u);
+}
+
+// A full block; returns false (having written nothing) when the block must
+// take the plain path instead.
+template <bool kNearest>
+__device__ __forceinline__ bool block_8bit_fast(const DevTensor& d, int64_t blk, int lane,
+                                                const StepScalars& sc, const uint8_t* lds,
+                                                bool range_ok) {
+  const float* cb_s = reinterpret_cast<const float*>(lds + kOffCbS);
+  const float* cb_u = reinterpret_cast<const float*>(lds + kOffCbU);
+  const int64_t e0 = blk * kBlock;
+  const uint16_t* gp = d.grad + e0;
+  uint16_t* pp = d.param + e0;
+  uint8_t* mp = static_cast<uint8_t*>(d.m) + e0;
+  uint8_t* vp = static_cast<uint8_t*>(d.v) + e0;
+  const float am = d.amax_m[blk];
+  const float av = d.amax_v[blk];
+
+  uint4 G[kGroups], P[kGroups];
+  uint2 QM[kGroups], QV[kGroups];
+#pragma unroll
+  for (int r = 0; r < kGroups; ++r) {
+    const int off = r * 512 + lane * 8;
+    G[r] = *reinterpret_cast<const uint4*>(gp + off);
+    P[r] = *reinterpret_cast<const uint4*>(pp + off);
+    QM[r] = *reinterpret_cast<const uint2*>(mp + off);
+    QV[r] = *reinterpret_cast<const uint2*>(vp + off);
+  }
+
+  // pass 1: moments, block maxima, smallest exponents
+  float M2[kGroups * 8], V2[kGroups * 8];
+  float mxm = 0.0f, mxv = 0.0f;
+  int em = 0, ev = 0;
+#pragma unroll
+  for (int r = 0; r < kGroups; ++r) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float g = bf16_at(G[r], j);
+      const float m1 = cb_s[byte_at(QM[r], j)] * am;
+      const float v1 = cb_u[byte_at(QV[r], j)] * av;
+      const float m2 = sc.beta1 * m1 + sc.w1 * g;
+      const float v2 = sc.beta2 * v1 + sc.w2 * (g * g);
+      M2[r * 8 + j] = m2;
+      V2[r * 8 + j] = v2;
+      mxm = fmaxf(mxm, fabsf(m2));
+      mxv = fmaxf(mxv, v2);
+      em = min(em, __builtin_amdgcn_frexp_expf(m2));   // 0 for zero
+      ev = min(ev, __builtin_amdgcn_frexp_expf(v2));
+    }
+  }
+  mxm = wave_max(mxm);
+  mxv = wave_max(mxv);
+
+  // range check for sqrt_rn / div_rn (uniform): finite maxima, v2 == 0 or
+  // >= 2^-89, and every non-zero m2 / den quotient far above 2^-126
+  const bool finite = (mxm <= 3.0e38f) && (mxv <= 3.0e38f);
+  const int e_den = __builtin_amdgcn_frexp_expf(sqrtf(mxv) * sc.rbc2 + sc.eps);
+  const int e_mmax = __builtin_amdgcn_frexp_expf(mxm);
+  const int e_eps = __builtin_amdgcn_frexp_expf(sc.eps);
+  const int floor_m = max(-88, e_den - 98);
+  const bool lane_bad = (em < floor_m) || (ev < -88);
+  if (!range_ok || !finite || e_den > 100 || e_mmax - e_eps > 100 ||
+      __builtin_amdgcn_ballot_w64(lane_bad) != 0)
+    return false;
+
+  // pass 2: parameter update and its rounding (stores deferred)
+  const uint64_t grp0 = static_cast<uint64_t>(d.index_base + e0) >> 3;
+  uint64_t nan_lanes = 0;
+#pragma unroll
+  for (int r = 0; r < kGroups; ++r) {
+    const int off = r * 512 + lane * 8;
+    Rand4 rnd{{0, 0, 0, 0}};
+    if (!kNearest) rnd = group_bits(grp0 + (off >> 3), 0u, d.tensor_id, sc);
+    uint32_t sums[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float p = bf16_at(P[r], j);
+      const float den = sqrt_rn(V2[r * 8 + j]) * sc.rbc2 + sc.eps;
+      const float u = div_rn(M2[r * 8 + j], den);
+      const float pn = (p - sc.lrwd * p) - sc.step_size * u;
+      nan_lanes |= __builtin_amdgcn_ballot_w64(pn != pn);
+      const uint32_t b = __float_as_uint(pn);
+      sums[j] = b + (kNearest ? (0x7FFFu + ((b >> 16) & 1u)) : r16_of(rnd, j));
+    }
+    // keep the upper halves: bf16 pairs (element 2k in the low half)
+    P[r] = make_uint4(__builtin_amdgcn_perm(sums[1], sums[0], 0x07060302u),
+                      __builtin_amdgcn_perm(sums[3], sums[2], 0x07060302u),
+                      __builtin_amdgcn_perm(sums[5], sums[4], 0x07060302u),
+                      __builtin_amdgcn_perm(sums[7], sums[6], 0x07060302u));
+  }
+  if (nan_lanes != 0) return false;
+#pragma unroll
+  for (int r = 0; r < kGroups; ++r)
+    *reinterpret_cast<uint4*>(pp + r * 512 + lane * 8) = P[r];
+
+  // pass 3: requantise (a block with absmax below 2^-126 stores the zero code;
+  // its codes are computed from n = 0 and then replaced)
+  const float* mid_s = reinterpret_cast<const float*>(lds + kOffMidS);
+  const float* mid_u = reinterpret_cast<const float*>(lds + kOffMidU);
+  const bool live_m = mxm >= kMinNormal;
+  const bool live_v = mxv >= kMinNormal;
+  const float inv_m = live_m ? 1.0f / mxm : 0.0f;
+  const float inv_v = live_v ? 1.0f / mxv : 0.0f;
+#pragma unroll
+  for (int r = 0; r < kGroups; ++r) {
+    const int off = r * 512 + lane * 8;
+    uint32_t cm[2] = {0, 0}, cv[2] = {0, 0};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t qm = code_s(M2[r * 8 + j] * inv_m, lds, mid_s);
+      const uint32_t qv = code_u(V2[r * 8 + j] * inv_v, lds, mid_u);
+      cm[j >> 2] |= qm << (8 * (j & 3));
+      cv[j >> 2] |= qv << (8 * (j & 3));
+    }
+    if (!live_m) cm[0] = cm[1] = 0x7F7F7F7Fu;
+    if (!live_v) cv[0] = cv[1] = 0u;
+    *reinterpret_cast<uint2*>(mp + off) = make_uint2(cm[0], cm[1]);
+    *reinterpret_cast<uint2*>(vp + off) = make_uint2(cv[0], cv[1]);
+  }
+  if (lane == 0) {
+    d.amax_m[blk] = mxm;
+    d.amax_v[blk] = mxv;
+  }
+  return true;
 }
 
 // ----------------------------------------------------------------------------- bf16 state (SR)
@@ -364,14 +555,21 @@ __device__ __forceinline__ void block_fp32(const DevTensor& d, int64_t blk, int 
 }
 
 // ----------------------------------------------------------------------------- driver
+__device__ __forceinline__ void stage_tables(uint8_t* lds) {
+  uint4* dst = reinterpret_cast<uint4*>(lds);
+  // codebooks and midpoints, then the LUTs (the per-wave scratch is not copied)
+  for (int i = threadIdx.x; i < kOffWave / 16; i += kThreads) dst[i] = g_tables[i];
+  for (int i = kOffLutU / 16 + threadIdx.x; i < kTableBytes / 16; i += kThreads) dst[i] = g_tables[i];
+  __syncthreads();
+}
+
 template <Kind K>
 __global__ void __launch_bounds__(kThreads)
-step_kernel(const DevTensor* __restrict__ list, int ntensors, int64_t total_blocks, StepScalars sc) {
-  __shared__ float s_tab[(K == Kind::k8bit) ? kTableWords : 1];
-  if constexpr (K == Kind::k8bit) {
-    for (int i = threadIdx.x; i < kTableWords; i += kThreads) s_tab[i] = g_tables[i];
-    __syncthreads();
-  }
+step_kernel(const DevTensor* __restrict__ list, int ntensors, int64_t total_blocks, StepScalars sc,
+            int range_ok) {
+  constexpr bool kQ8 = (K == Kind::k8bit || K == Kind::k8bitTail);
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kQ8 ? kTableBytes : 16];
+  if constexpr (kQ8) stage_tables(lds);
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
   const int64_t gw = static_cast<int64_t>(blockIdx.x) * kWaves + wave;
@@ -391,30 +589,38 @@ step_kernel(const DevTensor* __restrict__ list, int ntensors, int64_t total_bloc
   for (; b < bend; ++b) {
     while (b >= d.block_begin + static_cast<int64_t>(d.nblocks)) d = list[++t];
     const int64_t blk = b - d.block_begin;
-    const int64_t left = d.numel - blk * kBlock;
-    const bool full = left >= kBlock;
-    const int valid = full ? kBlock : static_cast<int>(left);
     if constexpr (K == Kind::k8bit) {
-      if (full) block_8bit<true>(d, blk, lane, valid, sc, s_tab);
-      else block_8bit<false>(d, blk, lane, valid, sc, s_tab);
-    } else if constexpr (K == Kind::kBf16) {
-      if (full) block_bf16<true>(d, blk, lane, valid, sc);
-      else block_bf16<false>(d, blk, lane, valid, sc);
+      // this list holds the full blocks of 8-bit tensors only
+      const bool done = sc.param_round ? block_8bit_fast<true>(d, blk, lane, sc, lds, range_ok != 0)
+                                       : block_8bit_fast<false>(d, blk, lane, sc, lds, range_ok != 0);
+      if (!done) block_8bit_plain<true>(d, blk, lane, kBlock, sc, lds);
+    } else if constexpr (K == Kind::k8bitTail) {
+      // this list holds the last, partial block of 8-bit tensors (one per entry)
+      const int64_t tail = (d.numel - 1) / kBlock;
+      block_8bit_plain<false>(d, tail, lane, static_cast<int>(d.numel - tail * kBlock), sc, lds);
     } else {
-      if (full) block_fp32<true>(d, blk, lane, valid, sc);
-      else block_fp32<false>(d, blk, lane, valid, sc);
+      const int64_t left = d.numel - blk * kBlock;
+      const bool full = left >= kBlock;
+      const int valid = full ? kBlock : static_cast<int>(left);
+      if constexpr (K == Kind::kBf16) {
+        if (full) block_bf16<true>(d, blk, lane, valid, sc);
+        else block_bf16<false>(d, blk, lane, valid, sc);
+      } else {
+        if (full) block_fp32<true>(d, blk, lane, valid, sc);
+        else block_fp32<false>(d, blk, lane, valid, sc);
+      }
     }
   }
 }
 
 template <Kind K>
 hipError_t launch_kind(const DevTensor* list, int n, int64_t total_blocks, const StepScalars& sc,
-                       hipStream_t stream, int grid_cap) {
+                       hipStream_t stream, int grid_cap, int range_ok) {
   int64_t grid = (total_blocks + kWaves - 1) / kWaves;
   if (grid_cap > 0 && grid > grid_cap) grid = grid_cap;
   if (grid < 1) grid = 1;
   hipLaunchKernelGGL(step_kernel<K>, dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0, stream,
-                     list, n, total_blocks, sc);
+                     list, n, total_blocks, sc, range_ok);
   return hipGetLastError();
 }
 
@@ -428,18 +634,22 @@ int occupancy_kind() {
 
 }  // namespace
 
-hipError_t upload_tables(const float* host_tables) {
-  return hipMemcpyToSymbol(HIP_SYMBOL(g_tables), host_tables, sizeof(float) * kTableWords, 0,
-                           hipMemcpyHostToDevice);
+hipError_t upload_tables(const uint8_t* host_tables) {
+  return hipMemcpyToSymbol(HIP_SYMBOL(g_tables), host_tables, kTableBytes, 0, hipMemcpyHostToDevice);
 }
 
 hipError_t launch_step(Kind kind, const DevTensor* list, int n, int64_t total_blocks,
                        const StepScalars& sc, hipStream_t stream, int grid_cap) {
   if (n <= 0 || total_blocks <= 0) return hipSuccess;
+  // the fast 8-bit path needs eps well inside the normal range and a bounded
+  // second-moment correction (it then checks each block's own values)
+  const int range_ok = (sc.eps >= 0x1p-60f && sc.eps <= 0x1p+60f && sc.rbc2 <= 0x1p+20f) ? 1 : 0;
   switch (kind) {
-    case Kind::k8bit: return launch_kind<Kind::k8bit>(list, n, total_blocks, sc, stream, grid_cap);
-    case Kind::kBf16: return launch_kind<Kind::kBf16>(list, n, total_blocks, sc, stream, grid_cap);
-    case Kind::kFp32: return launch_kind<Kind::kFp32>(list, n, total_blocks, sc, stream, grid_cap);
+    case Kind::k8bit: return launch_kind<Kind::k8bit>(list, n, total_blocks, sc, stream, grid_cap, range_ok);
+    case Kind::k8bitTail:
+      return launch_kind<Kind::k8bitTail>(list, n, total_blocks, sc, stream, grid_cap, range_ok);
+    case Kind::kBf16: return launch_kind<Kind::kBf16>(list, n, total_blocks, sc, stream, grid_cap, range_ok);
+    case Kind::kFp32: return launch_kind<Kind::kFp32>(list, n, total_blocks, sc, stream, grid_cap, range_ok);
   }
   return hipErrorInvalidValue;
 }
@@ -447,6 +657,7 @@ hipError_t launch_step(Kind kind, const DevTensor* list, int n, int64_t total_bl
 int occupancy_per_cu(Kind kind) {
   switch (kind) {
     case Kind::k8bit: return occupancy_kind<Kind::k8bit>();
+    case Kind::k8bitTail: return occupancy_kind<Kind::k8bitTail>();
     case Kind::kBf16: return occupancy_kind<Kind::kBf16>();
     case Kind::kFp32: return occupancy_kind<Kind::kFp32>();
   }

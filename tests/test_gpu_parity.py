@@ -273,3 +273,35 @@ def test_index_base_equals_shard_of_a_larger_tensor():
     assert np.array_equal(w[0][cut:], s[0])
     assert np.array_equal(w[1][cut:], s[1]) and np.array_equal(w[2][cut:], s[2])
     assert np.array_equal(w[3][3:], s[3]) and np.array_equal(w[4][3:], s[4])
+
+
+def test_non_finite_inputs():
+    """NaN and infinite gradients: the parameter becomes NaN where the oracle's does, the
+    block absmax follows NaN propagation, codes match.  (The sign of a NaN produced by an
+    invalid operation differs between the CPU and the GPU, so NaN is compared as NaN.)"""
+    rng = np.random.default_rng(21)
+    n = 2048 * 3
+    p = _rand_bf16(rng, n, 0.02)
+    g = _rand_bf16(rng, n, 1e-3)
+    g[5] = 0x7FC0            # NaN in block 0
+    g[2048 + 9] = 0x7F80     # +inf in block 1
+    g[2048 + 700] = 0xFF80   # -inf in block 1
+    st = _rand_state(M8, n, 6, 6)
+    hp = oracle.Hparams(lr=1e-3, weight_decay=0.01, step=2, seed=3)
+    want = oracle_step(DevTensorSet(M8, p, g, *st, tensor_id=1), [p, *st], hp)
+    s = DevTensorSet(M8, p, g, *st, tensor_id=1)
+    gpu_step([s], hp)
+    got = s.read()
+    wp = oracle.rounding.bf16_to_f32(want[0])
+    gp_ = oracle.rounding.bf16_to_f32(got[0])
+    assert np.array_equal(np.isnan(wp), np.isnan(gp_))
+    fin = ~np.isnan(wp)
+    assert np.array_equal(got[0][fin], want[0][fin])
+    for k in (1, 2):
+        assert np.array_equal(got[k], want[k])
+    for k in (3, 4):
+        assert np.array_equal(np.isnan(got[k]), np.isnan(want[k]))
+        ok = ~np.isnan(want[k])
+        assert np.array_equal(got[k][ok], want[k][ok])
+    # the third block is untouched by the bad values and matches bit for bit
+    assert np.array_equal(got[0][4096:], want[0][4096:])
