@@ -93,28 +93,34 @@ float bits_f32(uint32_t b) {
   return f;
 }
 
-// Code LUTs: the fp32 values sharing the top 16 bits (sign, exponent, 7
-// mantissa bits) of a key form a bucket; magnitudes below 2^-27 join the
-// lowest bucket.  Each entry is the code of the bucket's smallest value; a
-// bucket may contain at most one midpoint (checked here), so a value's code is
-// the entry plus one exactly when it lies above the midpoint the entry indexes.
+// Inverse of the monotone map fp32 -> uint32 that flips the sign bit of
+// non-negative values and every bit of negative ones.
+float unsortable(uint32_t u) { return bits_f32((u >> 31) ? (u & 0x7FFFFFFFu) : ~u); }
+
+// #{k : mid[k] < x} is constant on a bucket except at most one step; the LUT
+// entry is its value at the bucket's smallest member.  Returns false if a
+// bucket holds two midpoints (the lookup would then be wrong).
+bool lut_entry(const float* mid, float least, float most, uint8_t& out) {
+  const int base = count_below(mid, least);
+  const int top = count_below(mid, most);   // the largest count is at the largest member
+  out = static_cast<uint8_t>(base);
+  return top - base <= 1;
+}
+
+// Code LUTs for the signed table (keys of sortable(n) >> 17) and the unsigned
+// table (keys of bits(n) >> 16, clamped below at kKeyLo).
 bool build_luts(uint8_t* bytes) {
   const float* mid_s = reinterpret_cast<const float*>(bytes + kOffMidS);
   const float* mid_u = reinterpret_cast<const float*>(bytes + kOffMidU);
+  for (uint32_t key = kKeySLo; key <= kKeySHi; ++key) {
+    const float least = unsortable(key << 17);
+    const float most = unsortable((key << 17) | 0x1FFFFu);
+    if (!lut_entry(mid_s, least, most, bytes[key])) return false;
+  }
   for (uint32_t key = kKeyLo; key <= kKeyHi; ++key) {
-    const float lo = key == kKeyLo ? 0.0f : bits_f32(key << 16);
-    const float hi = bits_f32((key << 16) | 0xFFFFu);
-    struct { const float* mid; float least, most; int at; } cases[3] = {
-        {mid_u, lo, hi, static_cast<int>(key)},                            // unsigned, n >= 0
-        {mid_s, lo, hi, static_cast<int>(key) + kLutN},                    // signed, n >= 0
-        {mid_s, -hi, -lo, static_cast<int>(key) + 2 * kLutN}};             // signed, n < 0
-    for (const auto& c : cases) {
-      const int base = count_below(c.mid, c.least);
-      // the largest count in the bucket is reached at its largest value
-      const int top = count_below(c.mid, c.most);
-      if (top - base > 1) return false;
-      bytes[kOffLutU - static_cast<int>(kKeyLo) + c.at] = static_cast<uint8_t>(base);
-    }
+    const float least = key == kKeyLo ? 0.0f : bits_f32(key << 16);
+    const float most = bits_f32((key << 16) | 0xFFFFu);
+    if (!lut_entry(mid_u, least, most, bytes[key + kOffLutU])) return false;
   }
   return true;
 }

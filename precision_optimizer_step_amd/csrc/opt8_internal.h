@@ -41,21 +41,27 @@ struct StepScalars {
 //   [1024, 2048)   signed midpoints (fp32[255], then +inf)
 //   [2048, 3072)   unsigned codebook
 //   [3072, 4096)   unsigned midpoints (fp32[255], then +inf)
-//   [4096, 12288)  per-wave scratch in LDS only (block-scaled codebooks)
-//   [12800, ...)   code LUTs (u8): for a non-negative fp32 n with top-16-bit key
-//                  k = max(bits(n) >> 16, kKeyLo), the number of midpoints below
-//                  the smallest value of that key's bucket; unsigned table at
-//                  byte k, signed table at byte k + kLutN (n >= 0) or
-//                  k + 2*kLutN (n < 0, bucket of |n|).  Every bucket holds at
-//                  most one midpoint, so code = lut + (mid[lut] < n) exactly.
+//   signed code LUT (u8) at byte k for the key k = sortable(n) >> 17, where
+//                  sortable(n) flips the sign bit of n >= 0 and every bit of
+//                  n < 0, so keys grow with n; keys of |n| < 2 span
+//                  [kKeySLo, kKeySHi].
+//   unsigned code LUT (u8) at byte k + kOffLutU for the key
+//                  k = max(bits(n) >> 16, kKeyLo) of n >= 0 (magnitudes below
+//                  2^-27 share the lowest bucket); keys of n < 2 end at kKeyHi.
+// Each entry is the code of the smallest value of its bucket (the values
+// sharing a key).  No bucket holds more than one midpoint (checked when the
+// tables are built), so code = lut + (mid[lut] < n) exactly.
+constexpr uint32_t kKeySLo = 0x1FFFu;       // sortable(-2) >> 17
+constexpr uint32_t kKeySHi = 0x6000u;       // sortable(+2) >> 17
 constexpr uint32_t kKeyLo = 100u << 7;      // |n| < 2^-27 share the lowest bucket
-constexpr uint32_t kKeyHi = 0x3F80u;        // bucket of [1, 1 + 2^-7): |n| <= 1 + 2^-22
+constexpr uint32_t kKeyHi = 0x3FFFu;        // last key below 2.0
+constexpr int kLutSN = static_cast<int>(kKeySHi - kKeySLo + 1);
 constexpr int kLutN = static_cast<int>(kKeyHi - kKeyLo + 1);
 constexpr int kOffCbS = 0, kOffMidS = 1024, kOffCbU = 2048, kOffMidU = 3072;
-constexpr int kOffWave = 4096;
-constexpr int kWaveScratch = 2048;          // Tm[256], Tv[256] fp32
-constexpr int kOffLutU = static_cast<int>(kKeyLo);
-constexpr int kTableBytes = ((kOffLutU + 3 * kLutN) + 15) / 16 * 16;
+constexpr int kOffLutSBytes = static_cast<int>(kKeySLo);   // first byte of the signed LUT
+constexpr int kOffLutUBytes = (kOffLutSBytes + kLutSN + 15) / 16 * 16;
+constexpr int kOffLutU = kOffLutUBytes - static_cast<int>(kKeyLo);   // address = key + kOffLutU
+constexpr int kTableBytes = (kOffLutUBytes + kLutN + 15) / 16 * 16;
 
 enum class Kind : int { k8bit = 0, kBf16 = 1, kFp32 = 2, k8bitTail = 3 };
 

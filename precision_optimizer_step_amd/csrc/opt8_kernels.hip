@@ -277,17 +277,39 @@ __device__ __forceinline__ void block_8bit_plain(const DevTensor& d, int64_t blk
 // ----------------------------------------------------------------------------- 8-bit, fast path
 // Codes through the bucket LUTs: code = lut[key] + (mid[lut[key]] < n).
 __device__ __forceinline__ uint32_t code_u(float n, const uint8_t* lds, const float* mid) {
-  const uint32_t b = __float_as_uint(n);
-  const uint32_t key = max(b >> 16, kKeyLo);              // n >= 0
-  const uint32_t c = lds[key];                             // kOffLutU + key - kKeyLo == key
+  const uint32_t key = max(__float_as_uint(n) >> 16, kKeyLo);    // 0 <= n < 2
+  const uint32_t c = lds[key + kOffLutU];
   return c + ((mid[c] < n) ? 1u : 0u);
 }
 
 __device__ __forceinline__ uint32_t code_s(float n, const uint8_t* lds, const float* mid) {
-  const uint32_t b = __float_as_uint(n);
-  const uint32_t key = max((b >> 16) & 0x7FFFu, kKeyLo);
-  const uint32_t c = lds[key + static_cast<uint32_t>(kLutN) * (1u + (b >> 31))];
+  const uint32_t b = __float_as_uint(n);                          // -2 < n < 2
+  const uint32_t neg = static_cast<uint32_t>(static_cast<int32_t>(b) >> 31);
+  const uint32_t key = (b ^ (neg | 0x80000000u)) >> 17;          // sortable(n) >> 17
+  const uint32_t c = lds[key];
   return c + ((mid[c] < n) ? 1u : 0u);
+}
+
+// Philox for four 8-element groups at once, round by round, so each round key
+// is computed once on the scalar unit and used by all four.
+__device__ __forceinline__ void philox10_x4(uint32_t (&c0)[4], uint32_t (&c1)[4], uint32_t (&c2)[4],
+                                            uint32_t (&c3)[4], uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const uint64_t p0 = static_cast<uint64_t>(kPhiloxM0) * c0[g];
+      const uint64_t p1 = static_cast<uint64_t>(kPhiloxM1) * c2[g];
+      const uint32_t n0 = __builtin_amdgcn_bitop3_b32(static_cast<uint32_t>(p1 >> 32), c1[g], k0, 0x96);
+      const uint32_t n2 = __builtin_amdgcn_bitop3_b32(static_cast<uint32_t>(p0 >> 32), c3[g], k1, 0x96);
+      c1[g] = static_cast<uint32_t>(p1);
+      c3[g] = static_cast<uint32_t>(p0);
+      c0[g] = n0;
+      c2[g] = n2;
+    }
+    k0 += kPhiloxW0;
+    k1 += kPhiloxW1;
+  }
 }
 
 // A full block; returns false (having written nothing) when the block must
@@ -320,7 +342,7 @@ __device__ __forceinline__ bool block_8bit_fast(const DevTensor& d, int64_t blk,
   // pass 1: moments, block maxima, smallest exponents
   float M2[kGroups * 8], V2[kGroups * 8];
   float mxm = 0.0f, mxv = 0.0f;
-  int em = 0, ev = 0;
+  int emin = 0;
 #pragma unroll
   for (int r = 0; r < kGroups; ++r) {
 #pragma unroll
@@ -334,33 +356,43 @@ __device__ __forceinline__ bool block_8bit_fast(const DevTensor& d, int64_t blk,
       V2[r * 8 + j] = v2;
       mxm = fmaxf(mxm, fabsf(m2));
       mxv = fmaxf(mxv, v2);
-      em = min(em, __builtin_amdgcn_frexp_expf(m2));   // 0 for zero
-      ev = min(ev, __builtin_amdgcn_frexp_expf(v2));
+      // smallest exponent of any non-zero m2 or v2 (frexp gives 0 for zero)
+      emin = min(emin, min(__builtin_amdgcn_frexp_expf(m2), __builtin_amdgcn_frexp_expf(v2)));
     }
   }
   mxm = wave_max(mxm);
   mxv = wave_max(mxv);
 
-  // range check for sqrt_rn / div_rn (uniform): finite maxima, v2 == 0 or
-  // >= 2^-89, and every non-zero m2 / den quotient far above 2^-126
+  // range check for sqrt_rn / div_rn (uniform): finite maxima, every non-zero
+  // v2 >= 2^-89, every non-zero m2 / den quotient far above 2^-126
   const bool finite = (mxm <= 3.0e38f) && (mxv <= 3.0e38f);
   const int e_den = __builtin_amdgcn_frexp_expf(sqrtf(mxv) * sc.rbc2 + sc.eps);
   const int e_mmax = __builtin_amdgcn_frexp_expf(mxm);
   const int e_eps = __builtin_amdgcn_frexp_expf(sc.eps);
-  const int floor_m = max(-88, e_den - 98);
-  const bool lane_bad = (em < floor_m) || (ev < -88);
+  const int floor_e = max(-88, e_den - 98);
+  const bool lane_bad = emin < floor_e;
   if (!range_ok || !finite || e_den > 100 || e_mmax - e_eps > 100 ||
       __builtin_amdgcn_ballot_w64(lane_bad) != 0)
     return false;
 
   // pass 2: parameter update and its rounding (stores deferred)
-  const uint64_t grp0 = static_cast<uint64_t>(d.index_base + e0) >> 3;
+  uint32_t c0[4] = {0, 0, 0, 0}, c1[4] = {0, 0, 0, 0}, c2[4] = {0, 0, 0, 0}, c3[4] = {0, 0, 0, 0};
+  if (!kNearest) {
+    const uint64_t grp0 = (static_cast<uint64_t>(d.index_base + e0) >> 3) + static_cast<uint64_t>(lane);
+#pragma unroll
+    for (int r = 0; r < kGroups; ++r) {
+      const uint64_t grp = grp0 + static_cast<uint64_t>(r * 64);
+      c0[r] = static_cast<uint32_t>(grp);
+      c1[r] = static_cast<uint32_t>(grp >> 32);   // stream 0
+      c2[r] = sc.step_lo;
+      c3[r] = d.tensor_id;
+    }
+    philox10_x4(c0, c1, c2, c3, sc.seed_lo, sc.seed_hi);
+  }
   uint64_t nan_lanes = 0;
 #pragma unroll
   for (int r = 0; r < kGroups; ++r) {
-    const int off = r * 512 + lane * 8;
-    Rand4 rnd{{0, 0, 0, 0}};
-    if (!kNearest) rnd = group_bits(grp0 + (off >> 3), 0u, d.tensor_id, sc);
+    const Rand4 rnd{{c0[r], c1[r], c2[r], c3[r]}};
     uint32_t sums[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
@@ -558,8 +590,8 @@ __device__ __forceinline__ void block_fp32(const DevTensor& d, int64_t blk, int 
 __device__ __forceinline__ void stage_tables(uint8_t* lds) {
   uint4* dst = reinterpret_cast<uint4*>(lds);
   // codebooks and midpoints, then the LUTs (the per-wave scratch is not copied)
-  for (int i = threadIdx.x; i < kOffWave / 16; i += kThreads) dst[i] = g_tables[i];
-  for (int i = kOffLutU / 16 + threadIdx.x; i < kTableBytes / 16; i += kThreads) dst[i] = g_tables[i];
+  for (int i = threadIdx.x; i < kOffMidU / 16 + 64; i += kThreads) dst[i] = g_tables[i];
+  for (int i = kOffLutSBytes / 16 + threadIdx.x; i < kTableBytes / 16; i += kThreads) dst[i] = g_tables[i];
   __syncthreads();
 }
 
