@@ -33,6 +33,22 @@ def algorithmic_bytes(mode: int, n: int) -> int:
     return 22 * n   # fp32 state: g 2 + p 2+2 + m, v 4+4 in / 4+4 out
 
 
+def profiled_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from a committed rocprofv3 summary of this exact kernel build, or None."""
+    import glob
+    from precision_optimizer_step_amd.build import kernel_fingerprint
+    fp = kernel_fingerprint()
+    for path in glob.glob(os.path.join(ROOT, "profiles", "*.md")):
+        text = open(path).read()
+        if "bench-traffic" not in text:
+            continue
+        block = text.split("bench-traffic", 1)[1].split("```", 1)[0]
+        kv = dict(ln.split(": ", 1) for ln in block.strip().splitlines() if ": " in ln)
+        if kv.get("kernel") == kernel and kv.get("workload") == workload and kv.get("fingerprint") == fp:
+            return int(float(kv["traffic_bytes"]))
+    return None
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -145,9 +161,10 @@ def main():
     roof = None
     if kernel_ms:
         achieved = alg[dom] / (kernel_ms / 1000.0) / 1e9
+        kname = {0: "step_kernel<8bit>", 1: "step_kernel<bf16>", 2: "step_kernel<fp32>"}[dom]
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
-                "kernel": {0: "step_kernel<8bit>", 1: "step_kernel<bf16>", 2: "step_kernel<fp32>"}[dom],
+                "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": profiled_traffic(kname, w.name),
+                "kernel": kname,
                 "algorithmic_bytes_per_launch": alg[dom], "avg_launch_ms": round(kernel_ms, 4)}
 
     # attainable streaming bandwidth on this machine: a plain device copy of 4 GiB

@@ -24,6 +24,17 @@ FLAGS = [
 ]
 
 
+def kernel_fingerprint() -> str:
+    """sha256 over the kernel sources and the device compile flags (names a kernel build)."""
+    import hashlib
+    h = hashlib.sha256()
+    for name in ("opt8_kernels.hip", "opt8_internal.h"):
+        with open(os.path.join(HERE, "csrc", name), "rb") as f:
+            h.update(f.read())
+    h.update(" ".join(FLAGS).encode())
+    return h.hexdigest()
+
+
 def hipcc() -> str:
     for cand in (shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
         if cand and os.path.exists(cand):
