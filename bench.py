@@ -49,6 +49,43 @@ def profiled_traffic(kernel: str, workload: str):
     return None
 
 
+def probe_bandwidth(dev, words=1 << 27, reps=5):
+    """Best GB/s of the streaming probe over three grid sizes: 1 read + 1 write stream, and
+    3 read + 2 write streams (the 8-bit step's 6 B read : 4 B written per element)."""
+    import ctypes
+    import torch
+    path = os.path.join(ROOT, "precision_optimizer_step_amd", "libopt8_probe.so")
+    if not os.path.exists(path):
+        return {}
+    lib = ctypes.CDLL(path)
+    lib.opt8_probe_stream.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int,
+                                      ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    inp = torch.empty(3 * words * 16, dtype=torch.uint8, device=dev).random_(0, 255)
+    out = torch.empty(2 * words * 16, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream().cuda_stream
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    res = {}
+    for name, nin, nout in (("copy", 1, 1), ("mix", 3, 2)):
+        best = 0.0
+        for grid in (cus * 8, cus * 16, cus * 32):
+            def run():
+                assert lib.opt8_probe_stream(inp.data_ptr(), out.data_ptr(), words, nin, nout, grid,
+                                             stream) == 0
+            run()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                run()
+            e1.record()
+            torch.cuda.synchronize()
+            best = max(best, (nin + nout) * words * 16 * reps / (e0.elapsed_time(e1) / 1000.0) / 1e9)
+        res[name] = round(best, 1)
+    del inp, out
+    torch.cuda.empty_cache()
+    return res
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -167,19 +204,9 @@ def main():
                 "kernel": kname,
                 "algorithmic_bytes_per_launch": alg[dom], "avg_launch_ms": round(kernel_ms, 4)}
 
-    # attainable streaming bandwidth on this machine: a plain device copy of 4 GiB
-    src = torch.empty(1 << 31, dtype=torch.int16, device=dev)
-    dst = torch.empty_like(src)
-    dst.copy_(src)
-    torch.cuda.synchronize()
-    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    c0.record()
-    for _ in range(5):
-        dst.copy_(src)
-    c1.record()
-    torch.cuda.synchronize()
-    copy_gbps = 2 * src.numel() * 2 * 5 / (c0.elapsed_time(c1) / 1000.0) / 1e9
-    del src, dst
+    # attainable streaming bandwidth on this machine: the probe kernels (libopt8_probe.so) with a
+    # plain 1:1 copy and with the step's own 3:2 read:write mix, 16-byte accesses
+    attain = probe_bandwidth(dev)
 
     # ---------------------------------------------------------------- CPU baseline (oracle)
     cpu = None
@@ -225,7 +252,8 @@ def main():
                    "state": "bf16-sr" if w.state_mode == "bf16" else "8bit+fp32<4096",
                    "grad_pool": pool, "hbm_pct_of_peak": round(100 * sum(alg.values()) / (ms_per_step / 1000.0)
                                                               / 1e9 / HBM_PEAK_GBPS, 2),
-                   "attainable_copy_GBps": round(copy_gbps, 1)},
+                   "attainable_copy_GBps": attain.get("copy"),
+                   "attainable_3r2w_GBps": attain.get("mix")},
         "roofline": roof,
         "cpu_baseline": cpu,
     }

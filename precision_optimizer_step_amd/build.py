@@ -10,6 +10,9 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB = os.path.join(HERE, "libopt8.so")
 SOURCES = [os.path.join(HERE, "csrc", "opt8_host.cpp"), os.path.join(HERE, "csrc", "opt8_kernels.hip")]
+# bandwidth probe used by bench.py for the attainable-bandwidth context figure
+PROBE_LIB = os.path.join(HERE, "libopt8_probe.so")
+PROBE_SOURCES = [os.path.join(HERE, "csrc", "bw_probe.hip")]
 
 # fp32 arithmetic must round once per operation exactly as written: no
 # contraction into fused multiply-adds, IEEE sqrt/divide (hipcc's default),
@@ -42,18 +45,23 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found: the ROCm toolchain is required to build libopt8.so")
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source into libopt8.so (always recompiles); returns its path."""
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), *FLAGS, "-o", tmp, *SOURCES]
+def _compile(target: str, sources, verbose: bool) -> str:
+    tmp = target + ".tmp"
+    cmd = [hipcc(), *FLAGS, "-o", tmp, *sources]
     res = subprocess.run(cmd, capture_output=True, text=True)
     out = "\n".join(ln for ln in (res.stdout + res.stderr).splitlines() if "packed-fp32-ops" not in ln)
     if res.returncode != 0:
         raise RuntimeError("hipcc failed:\n" + " ".join(cmd) + "\n" + out)
     if verbose and out.strip():
         print(out, file=sys.stderr)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, target)
+    return target
+
+
+def build(verbose: bool = False) -> str:
+    """Compile libopt8.so and the bandwidth probe (always recompiles); returns libopt8's path."""
+    _compile(PROBE_LIB, PROBE_SOURCES, verbose)
+    return _compile(LIB, SOURCES, verbose)
 
 
 if __name__ == "__main__":

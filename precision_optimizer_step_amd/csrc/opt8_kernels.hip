@@ -87,6 +87,29 @@ __device__ __forceinline__ uint32_t to_bf16(float x, uint32_t r16, bool nearest)
   return (x != x) ? qnan : rounded;
 }
 
+// Streaming global accesses: every byte of the step is read once and written
+// once, so loads and stores are non-temporal (no reuse to keep in the caches).
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint4 ld_stream16(const void* p) {
+  const u32x4_t v = __builtin_nontemporal_load(static_cast<const u32x4_t*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint2 ld_stream8(const void* p) {
+  const u32x2_t v = __builtin_nontemporal_load(static_cast<const u32x2_t*>(p));
+  return make_uint2(v.x, v.y);
+}
+__device__ __forceinline__ void st_stream16(void* p, const uint4& q) {
+  u32x4_t v;
+  v.x = q.x; v.y = q.y; v.z = q.z; v.w = q.w;
+  __builtin_nontemporal_store(v, static_cast<u32x4_t*>(p));
+}
+__device__ __forceinline__ void st_stream8(void* p, const uint2& q) {
+  u32x2_t v;
+  v.x = q.x; v.y = q.y;
+  __builtin_nontemporal_store(v, static_cast<u32x2_t*>(p));
+}
+
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 __device__ __forceinline__ uint32_t word_of(const uint4& q, int k) {
@@ -333,11 +356,15 @@ __device__ __forceinline__ bool block_8bit_fast(const DevTensor& d, int64_t blk,
 #pragma unroll
   for (int r = 0; r < kGroups; ++r) {
     const int off = r * 512 + lane * 8;
-    G[r] = *reinterpret_cast<const uint4*>(gp + off);
-    P[r] = *reinterpret_cast<const uint4*>(pp + off);
-    QM[r] = *reinterpret_cast<const uint2*>(mp + off);
-    QV[r] = *reinterpret_cast<const uint2*>(vp + off);
+    G[r] = ld_stream16(gp + off);
+    QM[r] = ld_stream8(mp + off);
+    QV[r] = ld_stream8(vp + off);
   }
+  // the parameters are needed from pass 2 on; loading them here keeps their
+  // registers free during pass 1 while the wave's other loads are in flight
+#pragma unroll
+  for (int r = 0; r < kGroups; ++r)
+    P[r] = ld_stream16(pp + r * 512 + lane * 8);
 
   // pass 1: moments, block maxima, smallest exponents
   float M2[kGroups * 8], V2[kGroups * 8];
@@ -357,7 +384,7 @@ __device__ __forceinline__ bool block_8bit_fast(const DevTensor& d, int64_t blk,
       mxm = fmaxf(mxm, fabsf(m2));
       mxv = fmaxf(mxv, v2);
       // smallest exponent of any non-zero m2 or v2 (frexp gives 0 for zero)
-      emin = min(emin, min(__builtin_amdgcn_frexp_expf(m2), __builtin_amdgcn_frexp_expf(v2)));
+      emin = min(min(emin, __builtin_amdgcn_frexp_expf(m2)), __builtin_amdgcn_frexp_expf(v2));
     }
   }
   mxm = wave_max(mxm);
@@ -412,8 +439,7 @@ __device__ __forceinline__ bool block_8bit_fast(const DevTensor& d, int64_t blk,
   }
   if (nan_lanes != 0) return false;
 #pragma unroll
-  for (int r = 0; r < kGroups; ++r)
-    *reinterpret_cast<uint4*>(pp + r * 512 + lane * 8) = P[r];
+  for (int r = 0; r < kGroups; ++r) st_stream16(pp + r * 512 + lane * 8, P[r]);
 
   // pass 3: requantise (a block with absmax below 2^-126 stores the zero code;
   // its codes are computed from n = 0 and then replaced)
@@ -436,8 +462,8 @@ __device__ __forceinline__ bool block_8bit_fast(const DevTensor& d, int64_t blk,
     }
     if (!live_m) cm[0] = cm[1] = 0x7F7F7F7Fu;
     if (!live_v) cv[0] = cv[1] = 0u;
-    *reinterpret_cast<uint2*>(mp + off) = make_uint2(cm[0], cm[1]);
-    *reinterpret_cast<uint2*>(vp + off) = make_uint2(cv[0], cv[1]);
+    st_stream8(mp + off, make_uint2(cm[0], cm[1]));
+    st_stream8(vp + off, make_uint2(cv[0], cv[1]));
   }
   if (lane == 0) {
     d.amax_m[blk] = mxm;
@@ -462,10 +488,10 @@ __device__ __forceinline__ void block_bf16(const DevTensor& d, int64_t blk, int 
     const int off = r * 512 + lane * 8;
     uint4 G, P, M, V;
     if (kFull) {
-      G = *reinterpret_cast<const uint4*>(gp + off);
-      P = *reinterpret_cast<const uint4*>(pp + off);
-      M = *reinterpret_cast<const uint4*>(mp + off);
-      V = *reinterpret_cast<const uint4*>(vp + off);
+      G = ld_stream16(gp + off);
+      P = ld_stream16(pp + off);
+      M = ld_stream16(mp + off);
+      V = ld_stream16(vp + off);
     } else {
       uint32_t a[4] = {0, 0, 0, 0}, b[4] = {0, 0, 0, 0}, c[4] = {0, 0, 0, 0}, e[4] = {0, 0, 0, 0};
 #pragma unroll
@@ -499,9 +525,9 @@ __device__ __forceinline__ void block_bf16(const DevTensor& d, int64_t blk, int 
       vo[j >> 1] |= to_bf16(v2, r16_of(rv, j), false) << s;
     }
     if (kFull) {
-      *reinterpret_cast<uint4*>(pp + off) = make_uint4(po[0], po[1], po[2], po[3]);
-      *reinterpret_cast<uint4*>(mp + off) = make_uint4(mo[0], mo[1], mo[2], mo[3]);
-      *reinterpret_cast<uint4*>(vp + off) = make_uint4(vo[0], vo[1], vo[2], vo[3]);
+      st_stream16(pp + off, make_uint4(po[0], po[1], po[2], po[3]));
+      st_stream16(mp + off, make_uint4(mo[0], mo[1], mo[2], mo[3]));
+      st_stream16(vp + off, make_uint4(vo[0], vo[1], vo[2], vo[3]));
     } else {
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
