@@ -33,8 +33,9 @@ def algorithmic_bytes(mode: int, n: int) -> int:
     return 22 * n   # fp32 state: g 2 + p 2+2 + m, v 4+4 in / 4+4 out
 
 
-def profiled_traffic(kernel: str, workload: str):
-    """HBM bytes per launch from a committed rocprofv3 summary of this exact kernel build, or None."""
+def profiled_traffic(kernel: str, workload: str, key: str = "traffic_bytes"):
+    """A figure (default: HBM bytes per launch) from a committed rocprofv3 summary of this
+    exact kernel build and workload, or None."""
     import glob
     from precision_optimizer_step_amd.build import kernel_fingerprint
     fp = kernel_fingerprint()
@@ -45,7 +46,7 @@ def profiled_traffic(kernel: str, workload: str):
         block = text.split("bench-traffic", 1)[1].split("```", 1)[0]
         kv = dict(ln.split(": ", 1) for ln in block.strip().splitlines() if ": " in ln)
         if kv.get("kernel") == kernel and kv.get("workload") == workload and kv.get("fingerprint") == fp:
-            return int(float(kv["traffic_bytes"]))
+            return float(kv[key]) if key in kv else None
     return None
 
 
@@ -199,14 +200,19 @@ def main():
     if kernel_ms:
         achieved = alg[dom] / (kernel_ms / 1000.0) / 1e9
         kname = {0: "step_kernel<8bit>", 1: "step_kernel<bf16>", 2: "step_kernel<fp32>"}[dom]
+        traffic = profiled_traffic(kname, w.name)
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": profiled_traffic(kname, w.name),
+                "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": int(traffic) if traffic else None,
+                "valu_issue_frac": profiled_traffic(kname, w.name, "valu_issue_frac"),
+                "frac_of_attainable": None,
                 "kernel": kname,
                 "algorithmic_bytes_per_launch": alg[dom], "avg_launch_ms": round(kernel_ms, 4)}
 
     # attainable streaming bandwidth on this machine: the probe kernels (libopt8_probe.so) with a
     # plain 1:1 copy and with the step's own 3:2 read:write mix, 16-byte accesses
     attain = probe_bandwidth(dev)
+    if roof and attain.get("mix"):
+        roof["frac_of_attainable"] = round(roof["achieved"] / attain["mix"], 4)
 
     # ---------------------------------------------------------------- CPU baseline (oracle)
     cpu = None
