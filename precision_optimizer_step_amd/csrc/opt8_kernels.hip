@@ -473,9 +473,127 @@ __device__ __forceinline__ bool block_8bit_fast(const DevTensor& d, int64_t blk,
 }
 
 // ----------------------------------------------------------------------------- bf16 state (SR)
-template <bool kFull>
-__device__ __forceinline__ void block_bf16(const DevTensor& d, int64_t blk, int lane, int valid,
-                                           const StepScalars& sc) {
+// Plain path: IEEE operations, every rounding with its NaN rule.  Used for the
+// partial last block of a tensor and for any 8-element group of a full block
+// whose values leave the fast path's range.
+__device__ __forceinline__ void group_bf16_plain(const uint4& G, const uint4& P, const uint4& M,
+                                                 const uint4& V, const Rand4& rp, const Rand4& rm,
+                                                 const Rand4& rv, bool nearest, const StepScalars& sc,
+                                                 uint32_t (&po)[4], uint32_t (&mo)[4], uint32_t (&vo)[4]) {
+#pragma unroll
+  for (int k = 0; k < 4; ++k) po[k] = mo[k] = vo[k] = 0;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    float m2, v2;
+    const float pn = adamw(bf16_at(P, j), bf16_at(G, j), bf16_at(M, j), bf16_at(V, j), sc, m2, v2);
+    const int s = 16 * (j & 1);
+    po[j >> 1] |= to_bf16(pn, r16_of(rp, j), nearest) << s;
+    mo[j >> 1] |= to_bf16(m2, r16_of(rm, j), false) << s;
+    vo[j >> 1] |= to_bf16(v2, r16_of(rv, j), false) << s;
+  }
+}
+
+// Philox for the three streams (param, m, v) of one 8-element group, round by
+// round so each round key is computed once.
+__device__ __forceinline__ void philox10_x3(uint32_t (&c0)[3], uint32_t (&c1)[3], uint32_t (&c2)[3],
+                                            uint32_t (&c3)[3], uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+#pragma unroll
+    for (int g = 0; g < 3; ++g) {
+      const uint64_t p0 = static_cast<uint64_t>(kPhiloxM0) * c0[g];
+      const uint64_t p1 = static_cast<uint64_t>(kPhiloxM1) * c2[g];
+      const uint32_t n0 = __builtin_amdgcn_bitop3_b32(static_cast<uint32_t>(p1 >> 32), c1[g], k0, 0x96);
+      const uint32_t n2 = __builtin_amdgcn_bitop3_b32(static_cast<uint32_t>(p0 >> 32), c3[g], k1, 0x96);
+      c1[g] = static_cast<uint32_t>(p1);
+      c3[g] = static_cast<uint32_t>(p0);
+      c0[g] = n0;
+      c2[g] = n2;
+    }
+    k0 += kPhiloxW0;
+    k1 += kPhiloxW1;
+  }
+}
+
+// Upper halves of two 32-bit sums as one bf16 pair (element 2k in the low half).
+__device__ __forceinline__ uint32_t hi_pair(uint32_t even, uint32_t odd) {
+  return __builtin_amdgcn_perm(odd, even, 0x07060302u);
+}
+
+// A full block.  Each group takes the fast sequences (sqrt_rn, div_rn, the
+// plain add-and-truncate rounding) when every element of the wave's group is
+// in their range -- no NaN result, and non-zero m2, v2 and m2/den all at or
+// above 2^-88 -- and otherwise recomputes the group on the plain path.
+template <bool kNearest>
+__device__ __forceinline__ void block_bf16_full(const DevTensor& d, int64_t blk, int lane,
+                                                const StepScalars& sc, bool range_ok) {
+  const int64_t e0 = blk * kBlock;
+  const uint16_t* gp = d.grad + e0;
+  uint16_t* pp = d.param + e0;
+  uint16_t* mp = static_cast<uint16_t*>(d.m) + e0;
+  uint16_t* vp = static_cast<uint16_t*>(d.v) + e0;
+  const uint64_t grp0 = (static_cast<uint64_t>(d.index_base + e0) >> 3) + static_cast<uint64_t>(lane);
+#pragma unroll 1
+  for (int r = 0; r < kGroups; ++r) {
+    const int off = r * 512 + lane * 8;
+    const uint4 G = ld_stream16(gp + off);
+    const uint4 P = ld_stream16(pp + off);
+    const uint4 M = ld_stream16(mp + off);
+    const uint4 V = ld_stream16(vp + off);
+    const uint64_t grp = grp0 + static_cast<uint64_t>(r * 64);
+    uint32_t c0[3], c1[3], c2[3], c3[3];
+#pragma unroll
+    for (int s = 0; s < 3; ++s) {
+      c0[s] = static_cast<uint32_t>(grp);
+      c1[s] = static_cast<uint32_t>(grp >> 32) | (static_cast<uint32_t>(s) << 30);
+      c2[s] = sc.step_lo;
+      c3[s] = d.tensor_id;
+    }
+    philox10_x3(c0, c1, c2, c3, sc.seed_lo, sc.seed_hi);
+    const Rand4 rp{{c0[0], c1[0], c2[0], c3[0]}};
+    const Rand4 rm{{c0[1], c1[1], c2[1], c3[1]}};
+    const Rand4 rv{{c0[2], c1[2], c2[2], c3[2]}};
+
+    uint32_t ps[8], ms[8], vs[8];
+    int emin = 0;
+    bool nan = false;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float g = bf16_at(G, j);
+      const float p = bf16_at(P, j);
+      const float m2 = sc.beta1 * bf16_at(M, j) + sc.w1 * g;
+      const float v2 = sc.beta2 * bf16_at(V, j) + sc.w2 * (g * g);
+      const float den = sqrt_rn(v2) * sc.rbc2 + sc.eps;
+      const float u = div_rn(m2, den);
+      const float pn = (p - sc.lrwd * p) - sc.step_size * u;
+      nan |= (pn != pn);
+      emin = min(min(emin, __builtin_amdgcn_frexp_expf(u)),
+                 min(__builtin_amdgcn_frexp_expf(m2), __builtin_amdgcn_frexp_expf(v2)));
+      const uint32_t b = __float_as_uint(pn);
+      ps[j] = b + (kNearest ? (0x7FFFu + ((b >> 16) & 1u)) : r16_of(rp, j));
+      ms[j] = __float_as_uint(m2) + r16_of(rm, j);
+      vs[j] = __float_as_uint(v2) + r16_of(rv, j);
+    }
+    uint32_t po[4], mo[4], vo[4];
+    if (range_ok && __builtin_amdgcn_ballot_w64(nan || emin < -88) == 0) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        po[k] = hi_pair(ps[2 * k], ps[2 * k + 1]);
+        mo[k] = hi_pair(ms[2 * k], ms[2 * k + 1]);
+        vo[k] = hi_pair(vs[2 * k], vs[2 * k + 1]);
+      }
+    } else {
+      group_bf16_plain(G, P, M, V, rp, rm, rv, kNearest, sc, po, mo, vo);
+    }
+    st_stream16(pp + off, make_uint4(po[0], po[1], po[2], po[3]));
+    st_stream16(mp + off, make_uint4(mo[0], mo[1], mo[2], mo[3]));
+    st_stream16(vp + off, make_uint4(vo[0], vo[1], vo[2], vo[3]));
+  }
+}
+
+// The partial last block of a tensor.
+__device__ __forceinline__ void block_bf16_tail(const DevTensor& d, int64_t blk, int lane, int valid,
+                                                const StepScalars& sc) {
   const int64_t e0 = blk * kBlock;
   const uint16_t* gp = d.grad + e0;
   uint16_t* pp = d.param + e0;
@@ -483,60 +601,36 @@ __device__ __forceinline__ void block_bf16(const DevTensor& d, int64_t blk, int 
   uint16_t* vp = static_cast<uint16_t*>(d.v) + e0;
   const bool nearest = sc.param_round != 0;
   const uint64_t grp0 = static_cast<uint64_t>(d.index_base + e0) >> 3;
-#pragma unroll
+#pragma unroll 1
   for (int r = 0; r < kGroups; ++r) {
     const int off = r * 512 + lane * 8;
-    uint4 G, P, M, V;
-    if (kFull) {
-      G = ld_stream16(gp + off);
-      P = ld_stream16(pp + off);
-      M = ld_stream16(mp + off);
-      V = ld_stream16(vp + off);
-    } else {
-      uint32_t a[4] = {0, 0, 0, 0}, b[4] = {0, 0, 0, 0}, c[4] = {0, 0, 0, 0}, e[4] = {0, 0, 0, 0};
+    uint32_t a[4] = {0, 0, 0, 0}, b[4] = {0, 0, 0, 0}, c[4] = {0, 0, 0, 0}, e[4] = {0, 0, 0, 0};
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        if (off + j < valid) {
-          const int s = 16 * (j & 1);
-          a[j >> 1] |= static_cast<uint32_t>(gp[off + j]) << s;
-          b[j >> 1] |= static_cast<uint32_t>(pp[off + j]) << s;
-          c[j >> 1] |= static_cast<uint32_t>(mp[off + j]) << s;
-          e[j >> 1] |= static_cast<uint32_t>(vp[off + j]) << s;
-        }
+    for (int j = 0; j < 8; ++j) {
+      if (off + j < valid) {
+        const int s = 16 * (j & 1);
+        a[j >> 1] |= static_cast<uint32_t>(gp[off + j]) << s;
+        b[j >> 1] |= static_cast<uint32_t>(pp[off + j]) << s;
+        c[j >> 1] |= static_cast<uint32_t>(mp[off + j]) << s;
+        e[j >> 1] |= static_cast<uint32_t>(vp[off + j]) << s;
       }
-      G = make_uint4(a[0], a[1], a[2], a[3]);
-      P = make_uint4(b[0], b[1], b[2], b[3]);
-      M = make_uint4(c[0], c[1], c[2], c[3]);
-      V = make_uint4(e[0], e[1], e[2], e[3]);
     }
     const uint64_t grp = grp0 + (off >> 3);
     Rand4 rp{{0, 0, 0, 0}};
     if (!nearest) rp = group_bits(grp, 0u, d.tensor_id, sc);
     const Rand4 rm = group_bits(grp, 1u, d.tensor_id, sc);
     const Rand4 rv = group_bits(grp, 2u, d.tensor_id, sc);
-    uint32_t po[4] = {0, 0, 0, 0}, mo[4] = {0, 0, 0, 0}, vo[4] = {0, 0, 0, 0};
+    uint32_t po[4], mo[4], vo[4];
+    group_bf16_plain(make_uint4(a[0], a[1], a[2], a[3]), make_uint4(b[0], b[1], b[2], b[3]),
+                     make_uint4(c[0], c[1], c[2], c[3]), make_uint4(e[0], e[1], e[2], e[3]),
+                     rp, rm, rv, nearest, sc, po, mo, vo);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      float m2, v2;
-      const float pn = adamw(bf16_at(P, j), bf16_at(G, j), bf16_at(M, j), bf16_at(V, j), sc, m2, v2);
-      const int s = 16 * (j & 1);
-      po[j >> 1] |= to_bf16(pn, r16_of(rp, j), nearest) << s;
-      mo[j >> 1] |= to_bf16(m2, r16_of(rm, j), false) << s;
-      vo[j >> 1] |= to_bf16(v2, r16_of(rv, j), false) << s;
-    }
-    if (kFull) {
-      st_stream16(pp + off, make_uint4(po[0], po[1], po[2], po[3]));
-      st_stream16(mp + off, make_uint4(mo[0], mo[1], mo[2], mo[3]));
-      st_stream16(vp + off, make_uint4(vo[0], vo[1], vo[2], vo[3]));
-    } else {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        if (off + j < valid) {
-          const int s = 16 * (j & 1);
-          pp[off + j] = static_cast<uint16_t>(po[j >> 1] >> s);
-          mp[off + j] = static_cast<uint16_t>(mo[j >> 1] >> s);
-          vp[off + j] = static_cast<uint16_t>(vo[j >> 1] >> s);
-        }
+      if (off + j < valid) {
+        const int s = 16 * (j & 1);
+        pp[off + j] = static_cast<uint16_t>(po[j >> 1] >> s);
+        mp[off + j] = static_cast<uint16_t>(mo[j >> 1] >> s);
+        vp[off + j] = static_cast<uint16_t>(vo[j >> 1] >> s);
       }
     }
   }
@@ -661,8 +755,9 @@ step_kernel(const DevTensor* __restrict__ list, int ntensors, int64_t total_bloc
       const bool full = left >= kBlock;
       const int valid = full ? kBlock : static_cast<int>(left);
       if constexpr (K == Kind::kBf16) {
-        if (full) block_bf16<true>(d, blk, lane, valid, sc);
-        else block_bf16<false>(d, blk, lane, valid, sc);
+        if (!full) block_bf16_tail(d, blk, lane, valid, sc);
+        else if (sc.param_round) block_bf16_full<true>(d, blk, lane, sc, range_ok != 0);
+        else block_bf16_full<false>(d, blk, lane, sc, range_ok != 0);
       } else {
         if (full) block_fp32<true>(d, blk, lane, valid, sc);
         else block_fp32<false>(d, blk, lane, valid, sc);
