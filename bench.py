@@ -95,6 +95,8 @@ def parse():
     ap.add_argument("--workload", default="gptneo-6.7b")
     ap.add_argument("--grad-pool", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--round", choices=("stochastic", "nearest"), default="stochastic",
+                    help="parameter rounding (nearest: the deterministic baseline, for the SR overhead)")
     ap.add_argument("--cpu-sample-elems", type=int, default=96 * 1024 * 1024)
     return ap.parse_args()
 
@@ -164,8 +166,11 @@ def main():
                                                 tensor_id=t["tid"], mode=t["mode"]) for t in tensors)
              for k in range(pool)]
 
+    rnd = opt8.OPT8_ROUND_NEAREST if args.round == "nearest" else opt8.OPT8_ROUND_STOCHASTIC
+
     def step(t):
-        hp = opt8.make_hparams(w.lr, w.beta1, w.beta2, w.eps, w.weight_decay, step=t, seed=w.seed)
+        hp = opt8.make_hparams(w.lr, w.beta1, w.beta2, w.eps, w.weight_decay, step=t, seed=w.seed,
+                               param_round=rnd)
         opt8.opt8_adamw_step(lists[(t - 1) % pool], hp)
 
     # ---------------------------------------------------------------- timing
@@ -256,6 +261,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "tensors": len(tensors), "params": total,
                    "state": "bf16-sr" if w.state_mode == "bf16" else "8bit+fp32<4096",
+                   "param_round": args.round,
                    "grad_pool": pool, "hbm_pct_of_peak": round(100 * sum(alg.values()) / (ms_per_step / 1000.0)
                                                               / 1e9 / HBM_PEAK_GBPS, 2),
                    "attainable_copy_GBps": attain.get("copy"),
