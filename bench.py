@@ -1,12 +1,14 @@
 """Benchmark of the fused 8-bit AdamW step with a stochastically rounded bf16 write.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload gptneo-6.7b]
+                    [--algo adamw|lion|momentum]
 
 One step = one opt8_adamw_step call over the whole parameter list (every
 tensor: dequantise, AdamW in fp32, stochastic bf16 param write, block absmax,
-requantise).  Inputs are synthetic and already resident in HBM when the timed
-region starts; a small pool of gradient sets gives each step fresh gradients
-without generating them inside the timed region.  Prints ONE JSON line.
+requantise); --algo lion / momentum time the one-state rules on the same list.
+Inputs are synthetic and already resident in HBM when the timed region starts;
+a small pool of gradient sets gives each step fresh gradients without
+generating them inside the timed region.  Prints ONE JSON line.
 """
 
 import argparse
@@ -24,8 +26,12 @@ BLOCK = 2048
 STATE_BYTES = {0: 1, 1: 2, 2: 4}
 
 
-def algorithmic_bytes(mode: int, n: int) -> int:
+def algorithmic_bytes(mode: int, n: int, one_state: bool = False) -> int:
     """Bytes each element's step must move once: read grad, param, state; write param, state."""
+    if one_state:   # m only: g 2 + p 2+2 + m r/w (8-bit 1+1 and 8 B absmax per block, bf16 2+2, fp32 4+4)
+        if mode == 0:
+            return 8 * n + 8 * ((n + BLOCK - 1) // BLOCK)
+        return 10 * n if mode == 1 else 14 * n
     if mode == 0:   # 8-bit: 2+2+1+1 in, 2+1+1 out, plus absmax r/w (2 x 4 B in, 2 x 4 B out) per block
         return 10 * n + 16 * ((n + BLOCK - 1) // BLOCK)
     if mode == 1:   # bf16 state: g 2 + p 2+2 + m, v 2+2 in / 2+2 out
@@ -98,6 +104,8 @@ def parse():
     ap.add_argument("--round", choices=("stochastic", "nearest"), default="stochastic",
                     help="parameter rounding (nearest: the deterministic baseline, for the SR overhead)")
     ap.add_argument("--cpu-sample-elems", type=int, default=96 * 1024 * 1024)
+    ap.add_argument("--algo", choices=("adamw", "lion", "momentum"), default="adamw",
+                    help="update rule (lion / momentum: one 8-bit state, the same machinery)")
     return ap.parse_args()
 
 
@@ -121,6 +129,14 @@ def main():
     torch.cuda.set_device(dev)
     opt8.opt8_init_codebooks()
     w = shapes.get(args.workload)
+    one_state = args.algo != "adamw"
+    algo_id = {"adamw": 0, "lion": 1, "momentum": 2}[args.algo]
+    step_fn = {"adamw": opt8.opt8_adamw_step, "lion": opt8.opt8_lion_step,
+               "momentum": opt8.opt8_momentum_step}[args.algo]
+    # hyperparameters: the workload's for AdamW; Lion at a tenth of its lr with beta2 0.99
+    # (the usual Lion setting), momentum 0.9 at the workload's lr
+    lr = w.lr / 10 if args.algo == "lion" else w.lr
+    beta2 = 0.99 if args.algo == "lion" else w.beta2
 
     def log(msg):
         print(f"[bench] {msg}", file=sys.stderr, flush=True)
@@ -154,9 +170,11 @@ def main():
         else:
             M = torch.zeros(n, dtype=torch.float32, device=dev)
             V = torch.zeros(n, dtype=torch.float32, device=dev)
+        if one_state:
+            V = AV = None
         tensors.append(dict(tid=tid, mode=mode, n=n, P=P, grads=grads, M=M, V=V, AM=AM, AV=AV))
         modes[mode] += n
-        alg[mode] += algorithmic_bytes(mode, n)
+        alg[mode] += algorithmic_bytes(mode, n, one_state)
     torch.cuda.synchronize()
     total = sum(t["n"] for t in tensors)
     log(f"workload {w.name}: {len(tensors)} tensors, {total} params, inputs built in {time.time() - t0:.1f}s, "
@@ -169,9 +187,9 @@ def main():
     rnd = opt8.OPT8_ROUND_NEAREST if args.round == "nearest" else opt8.OPT8_ROUND_STOCHASTIC
 
     def step(t):
-        hp = opt8.make_hparams(w.lr, w.beta1, w.beta2, w.eps, w.weight_decay, step=t, seed=w.seed,
+        hp = opt8.make_hparams(lr, w.beta1, beta2, w.eps, w.weight_decay, step=t, seed=w.seed,
                                param_round=rnd)
-        opt8.opt8_adamw_step(lists[(t - 1) % pool], hp)
+        step_fn(lists[(t - 1) % pool], hp)
 
     # ---------------------------------------------------------------- timing
     t_step = 1
@@ -205,6 +223,8 @@ def main():
     if kernel_ms:
         achieved = alg[dom] / (kernel_ms / 1000.0) / 1e9
         kname = {0: "step_kernel<8bit>", 1: "step_kernel<bf16>", 2: "step_kernel<fp32>"}[dom]
+        if one_state:
+            kname = kname[:-1] + f",{args.algo}>"
         traffic = profiled_traffic(kname, w.name)
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": int(traffic) if traffic else None,
@@ -233,13 +253,17 @@ def main():
                 h = h.view(torch.int16)
             return h.numpy().view(dtype).copy()
         p, g = host(big["P"], np.uint16), host(big["grads"][0], np.uint16)
-        m, v = host(big["M"], sd), host(big["V"], sd)
+        m = host(big["M"], sd)
+        v = host(big["V"], sd) if big["V"] is not None else None
         am = big["AM"][: (n + BLOCK - 1) // BLOCK].cpu().numpy() if big["AM"] is not None else None
         av = big["AV"][: (n + BLOCK - 1) // BLOCK].cpu().numpy() if big["AV"] is not None else None
-        hp = oracle.Hparams(lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps,
+        hp = oracle.Hparams(lr=lr, beta1=w.beta1, beta2=beta2, eps=w.eps,
                             weight_decay=w.weight_decay, step=t_step, seed=w.seed)
         c0t = time.perf_counter()
-        oracle.step_tensor(big["mode"], p, g, m, v, am, av, hp, big["tid"])
+        if one_state:
+            oracle.step_tensor_1state(algo_id, big["mode"], p, g, m, am, hp, big["tid"])
+        else:
+            oracle.step_tensor(big["mode"], p, g, m, v, am, av, hp, big["tid"])
         cpu_s = time.perf_counter() - c0t
         cpu = {"value": round(n / cpu_s / 1e9, 6), "unit": "Gparams/s", "cores": 1, "kind": "oracle",
                "sample": f"one step of the first {n} elements of tensor {w.tensors[big['tid']].name} "
@@ -261,7 +285,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "tensors": len(tensors), "params": total,
                    "state": "bf16-sr" if w.state_mode == "bf16" else "8bit+fp32<4096",
-                   "param_round": args.round,
+                   "param_round": args.round, "algo": args.algo,
                    "grad_pool": pool, "hbm_pct_of_peak": round(100 * sum(alg.values()) / (ms_per_step / 1000.0)
                                                               / 1e9 / HBM_PEAK_GBPS, 2),
                    "attainable_copy_GBps": attain.get("copy"),

@@ -139,6 +139,32 @@ int32_t opt8_default_mode(int64_t numel);
 int opt8_adamw_step(const opt8_tensor* tensors, int32_t n, const opt8_hparams* hp,
                     void* hip_stream);
 
+/* One-state update rules on the same state machinery (codebook, block absmax,
+ * state modes, rounding, Random bits; the SIGNED codebook holds the state in
+ * 8-bit mode).  The pages name both without defining them ("8-bit Optimizers
+ * via Block-wise Quantization", introduction: the state of Adam and of
+ * Momentum; "Stochastic rounding support for 8-bit optimizers", motivation:
+ * more memory saved with 8-bit Lion); the readings below follow the papers
+ * that introduced them, with weight decay decoupled as in the AdamW step.
+ * v and absmax_v are ignored (may be NULL) and eps is neither validated nor
+ * used; step is still validated (>= 1) and keys the random bits; there is
+ * no bias correction.
+ * Validation, error behaviour, streams and ownership as for opt8_adamw_step.
+ *
+ * Lion (Chen et al., "Symbolic Discovery of Optimization Algorithms"):
+ *   c  = beta1*m1 + (1-beta1)*g          (the direction uses the old moment)
+ *   m2 = beta2*m1 + (1-beta2)*g
+ *   p' = (p - lrwd*p) - lr*sign(c)       sign(+-0) = 0, sign(NaN) = NaN     */
+int opt8_lion_step(const opt8_tensor* tensors, int32_t n, const opt8_hparams* hp,
+                   void* hip_stream);
+
+/* SGD with momentum (heavy ball, dampening 0; beta1 is the momentum, beta2
+ * is validated but unused):
+ *   m2 = beta1*m1 + g
+ *   p' = (p - lrwd*p) - lr*m2                                                */
+int opt8_momentum_step(const opt8_tensor* tensors, int32_t n, const opt8_hparams* hp,
+                       void* hip_stream);
+
 /* Message of the last failure on the calling thread ("" if none).  The
  * string is owned by the library and valid until the thread's next call.    */
 const char* opt8_last_error(void);

@@ -19,12 +19,13 @@ Modules
   codebook  dynamic-tree signed/unsigned 256-entry codebooks and midpoints
   philox    Philox4x32-10 counter-based generator (Salmon et al., SC'11)
   rounding  bf16 decode, stochastic rounding and round-to-nearest-even
-  adamw     host scalars, block quantiser and the per-tensor step
+  adamw     host scalars, block quantiser and the per-tensor AdamW step
+  onestate  Lion and SGD with momentum on the same state machinery
 
 Parity status of each function is stated in its module header.
 """
 
-from . import codebook, philox, rounding, adamw  # noqa: F401
+from . import codebook, philox, rounding, adamw, onestate  # noqa: F401
 from .adamw import (  # noqa: F401
     Hparams,
     Scalars,
@@ -42,3 +43,4 @@ from .adamw import (  # noqa: F401
     FP32_STATE_THRESHOLD,
     default_mode,
 )
+from .onestate import ALGO_LION, ALGO_MOMENTUM, step_tensor_1state  # noqa: F401

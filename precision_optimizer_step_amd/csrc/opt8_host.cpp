@@ -178,9 +178,10 @@ void beta_powers(double b1, double b2, int64_t t, PowCache& c, double& p1, doubl
   p2 = c.p2;
 }
 
-StepScalars make_scalars(const opt8_hparams& hp, PowCache& cache) {
-  double b1t, b2t;
-  beta_powers(hp.beta1, hp.beta2, hp.step, cache, b1t, b2t);
+StepScalars make_scalars(const opt8_hparams& hp, int algo, PowCache& cache) {
+  // Lion and momentum have no bias correction
+  double b1t = 0.0, b2t = 0.0;
+  if (algo == kAdamW) beta_powers(hp.beta1, hp.beta2, hp.step, cache, b1t, b2t);
   const double bc1 = 1.0 - b1t;
   const double bc2 = 1.0 - b2t;
   StepScalars s;
@@ -192,6 +193,7 @@ StepScalars make_scalars(const opt8_hparams& hp, PowCache& cache) {
   s.step_size = static_cast<float>(hp.lr / bc1);
   s.rbc2 = static_cast<float>(1.0 / std::sqrt(bc2));
   s.lrwd = static_cast<float>(hp.lr * hp.weight_decay);
+  s.lr = static_cast<float>(hp.lr);
   s.seed_lo = static_cast<uint32_t>(hp.seed);
   s.seed_hi = static_cast<uint32_t>(hp.seed >> 32);
   s.step_lo = static_cast<uint32_t>(hp.step);
@@ -203,11 +205,12 @@ StepScalars make_scalars(const opt8_hparams& hp, PowCache& cache) {
 size_t state_bytes(int mode) { return mode == OPT8_STATE_8BIT ? 1 : mode == OPT8_STATE_BF16_SR ? 2 : 4; }
 int64_t nblocks_of(int64_t numel) { return (numel + kBlock - 1) / kBlock; }
 
-int validate_hparams(const opt8_hparams& hp) {
+int validate_hparams(const opt8_hparams& hp, int algo) {
   if (!(std::isfinite(hp.lr) && hp.lr >= 0)) return fail(OPT8_E_HPARAM, "lr must be finite and >= 0 (got %g)", hp.lr);
   if (!(hp.beta1 >= 0 && hp.beta1 < 1)) return fail(OPT8_E_HPARAM, "beta1 must be in [0, 1) (got %g)", hp.beta1);
   if (!(hp.beta2 >= 0 && hp.beta2 < 1)) return fail(OPT8_E_HPARAM, "beta2 must be in [0, 1) (got %g)", hp.beta2);
-  if (!(std::isfinite(hp.eps) && hp.eps > 0)) return fail(OPT8_E_HPARAM, "eps must be finite and > 0 (got %g)", hp.eps);
+  if (algo == kAdamW && !(std::isfinite(hp.eps) && hp.eps > 0))
+    return fail(OPT8_E_HPARAM, "eps must be finite and > 0 (got %g)", hp.eps);
   if (!(std::isfinite(hp.weight_decay) && hp.weight_decay >= 0))
     return fail(OPT8_E_HPARAM, "weight_decay must be finite and >= 0 (got %g)", hp.weight_decay);
   if (hp.step < 1) return fail(OPT8_E_HPARAM, "step is 1-based (got %lld)", static_cast<long long>(hp.step));
@@ -223,7 +226,8 @@ struct Range {
   const char* what;
 };
 
-int validate_tensors(const opt8_tensor* t, int32_t n) {
+// Two-state rules (AdamW) use v and absmax_v; one-state rules ignore them.
+int validate_tensors(const opt8_tensor* t, int32_t n, bool two_state) {
   std::vector<Range> ranges;
   std::vector<uint32_t> ids;
   ranges.reserve(static_cast<size_t>(n) * 6);
@@ -232,17 +236,20 @@ int validate_tensors(const opt8_tensor* t, int32_t n) {
     const opt8_tensor& x = t[i];
     if (x.mode != OPT8_STATE_8BIT && x.mode != OPT8_STATE_BF16_SR && x.mode != OPT8_STATE_FP32)
       return fail(OPT8_E_MODE, "tensor %d: unknown state mode %d", i, x.mode);
-    if (!x.param || !x.grad || !x.m || !x.v) return fail(OPT8_E_NULL, "tensor %d: NULL param/grad/m/v", i);
+    if (!x.param || !x.grad || !x.m || (two_state && !x.v))
+      return fail(OPT8_E_NULL, two_state ? "tensor %d: NULL param/grad/m/v" : "tensor %d: NULL param/grad/m", i);
     const bool q8 = x.mode == OPT8_STATE_8BIT;
-    if (q8 && (!x.absmax_m || !x.absmax_v)) return fail(OPT8_E_NULL, "tensor %d: 8-bit mode needs absmax_m/absmax_v", i);
+    if (q8 && (!x.absmax_m || (two_state && !x.absmax_v)))
+      return fail(OPT8_E_NULL, two_state ? "tensor %d: 8-bit mode needs absmax_m/absmax_v"
+                                         : "tensor %d: 8-bit mode needs absmax_m", i);
     if (x.numel <= 0) return fail(OPT8_E_SIZE, "tensor %d: numel must be > 0", i);
     if (x.numel > (int64_t(1) << 46)) return fail(OPT8_E_SIZE, "tensor %d: numel too large", i);
     if (x.index_base < 0 || x.index_base % kBlock != 0 || x.index_base > (int64_t(1) << 60))
       return fail(OPT8_E_SIZE, "tensor %d: index_base must be >= 0 and a multiple of 2048", i);
     auto al = [](const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; };
-    if (!al(x.param, 16) || !al(x.grad, 16) || !al(x.m, 16) || !al(x.v, 16))
-      return fail(OPT8_E_ALIGN, "tensor %d: param/grad/m/v must be 16-byte aligned", i);
-    if (q8 && (!al(x.absmax_m, 4) || !al(x.absmax_v, 4)))
+    if (!al(x.param, 16) || !al(x.grad, 16) || !al(x.m, 16) || (two_state && !al(x.v, 16)))
+      return fail(OPT8_E_ALIGN, "tensor %d: param/grad/state buffers must be 16-byte aligned", i);
+    if (q8 && (!al(x.absmax_m, 4) || (two_state && !al(x.absmax_v, 4))))
       return fail(OPT8_E_ALIGN, "tensor %d: absmax arrays must be 4-byte aligned", i);
     const uintptr_t ne = static_cast<uintptr_t>(x.numel);
     const uintptr_t sb = state_bytes(x.mode);
@@ -253,11 +260,11 @@ int validate_tensors(const opt8_tensor* t, int32_t n) {
     add(x.param, 2 * ne, "param");
     add(x.grad, 2 * ne, "grad");
     add(x.m, sb * ne, "m");
-    add(x.v, sb * ne, "v");
+    if (two_state) add(x.v, sb * ne, "v");
     if (q8) {
       const uintptr_t ab = 4 * static_cast<uintptr_t>(nblocks_of(x.numel));
       add(x.absmax_m, ab, "absmax_m");
-      add(x.absmax_v, ab, "absmax_v");
+      if (two_state) add(x.absmax_v, ab, "absmax_v");
     }
     ids.push_back(x.tensor_id);
   }
@@ -278,6 +285,7 @@ int validate_tensors(const opt8_tensor* t, int32_t n) {
 constexpr int kSlots = 4;
 constexpr int kMaxDevices = 64;
 constexpr int kKinds = 4;
+constexpr int kAlgos = 3;
 
 struct Slot {
   DevTensor* dev = nullptr;
@@ -293,7 +301,7 @@ struct Slot {
 struct DeviceState {
   bool init = false;
   int num_cu = 0;
-  int occ[kKinds] = {1, 1, 1, 1};
+  int occ[kAlgos][kKinds] = {};
   Slot slots[kSlots];
   uint64_t clock = 0;
   PowCache pow;
@@ -393,7 +401,8 @@ extern "C" int opt8_init_codebooks(float* signed_out, float* unsigned_out) {
   if (e != hipSuccess) return hip_fail(e, "upload of codebooks");
   e = hipDeviceGetAttribute(&ds.num_cu, hipDeviceAttributeMultiprocessorCount, dev);
   if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute(CU count)");
-  for (int k = 0; k < kKinds; ++k) ds.occ[k] = occupancy_per_cu(static_cast<Kind>(k));
+  for (int a = 0; a < kAlgos; ++a)
+    for (int k = 0; k < kKinds; ++k) ds.occ[a][k] = occupancy_per_cu(static_cast<Kind>(k), a);
   for (Slot& s : ds.slots) {
     if (!s.done) {
       e = hipEventCreateWithFlags(&s.done, hipEventDisableTiming);
@@ -412,15 +421,19 @@ extern "C" int32_t opt8_default_mode(int64_t numel) {
 
 extern "C" const char* opt8_last_error(void) { return t_error.c_str(); }
 
-extern "C" int opt8_adamw_step(const opt8_tensor* tensors, int32_t n, const opt8_hparams* hp,
-                               void* hip_stream) {
+namespace opt8 {
+namespace {
+
+// One step of update rule `algo` over a tensor list (every entry point).
+int run_step(int algo, const opt8_tensor* tensors, int32_t n, const opt8_hparams* hp, void* hip_stream) {
   t_error.clear();
   if (!hp) return fail(OPT8_E_NULL, "hparams is NULL");
   if (n < 0) return fail(OPT8_E_SIZE, "n must be >= 0 (got %d)", n);
   if (n > 0 && !tensors) return fail(OPT8_E_NULL, "tensor list is NULL");
-  int rc = validate_hparams(*hp);
+  const bool two_state = algo == kAdamW;
+  int rc = validate_hparams(*hp, algo);
   if (rc != OPT8_OK) return rc;
-  rc = validate_tensors(tensors, n);
+  rc = validate_tensors(tensors, n, two_state);
   if (rc != OPT8_OK) return rc;
   if (n == 0) return OPT8_OK;
 
@@ -453,9 +466,9 @@ extern "C" int opt8_adamw_step(const opt8_tensor* tensors, int32_t n, const opt8
       d.param = x.param;
       d.grad = x.grad;
       d.m = x.m;
-      d.v = x.v;
+      d.v = two_state ? x.v : nullptr;
       d.amax_m = mode == OPT8_STATE_8BIT ? x.absmax_m : nullptr;
-      d.amax_v = mode == OPT8_STATE_8BIT ? x.absmax_v : nullptr;
+      d.amax_v = (two_state && mode == OPT8_STATE_8BIT) ? x.absmax_v : nullptr;
       d.numel = x.numel;
       d.index_base = x.index_base;
       d.block_begin = blocks[kind];
@@ -470,11 +483,11 @@ extern "C" int opt8_adamw_step(const opt8_tensor* tensors, int32_t n, const opt8
   Slot* slot = nullptr;
   rc = acquire_slot(ds, list, stream, slot);
   if (rc != OPT8_OK) return rc;
-  const StepScalars sc = make_scalars(*hp, ds.pow);
+  const StepScalars sc = make_scalars(*hp, algo, ds.pow);
   for (int kind = 0; kind < kKinds; ++kind) {
     if (!count[kind]) continue;
-    const int cap = ds.num_cu * ds.occ[kind];
-    const hipError_t e = launch_step(static_cast<Kind>(kind), slot->dev + first[kind], count[kind],
+    const int cap = ds.num_cu * ds.occ[algo][kind];
+    const hipError_t e = launch_step(static_cast<Kind>(kind), algo, slot->dev + first[kind], count[kind],
                                      blocks[kind], sc, stream, cap);
     if (e != hipSuccess) return hip_fail(e, "kernel launch");
   }
@@ -482,4 +495,22 @@ extern "C" int opt8_adamw_step(const opt8_tensor* tensors, int32_t n, const opt8
   if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
   slot->last_stream = stream;
   return OPT8_OK;
+}
+
+}  // namespace
+}  // namespace opt8
+
+extern "C" int opt8_adamw_step(const opt8_tensor* tensors, int32_t n, const opt8_hparams* hp,
+                               void* hip_stream) {
+  return run_step(kAdamW, tensors, n, hp, hip_stream);
+}
+
+extern "C" int opt8_lion_step(const opt8_tensor* tensors, int32_t n, const opt8_hparams* hp,
+                              void* hip_stream) {
+  return run_step(kLion, tensors, n, hp, hip_stream);
+}
+
+extern "C" int opt8_momentum_step(const opt8_tensor* tensors, int32_t n, const opt8_hparams* hp,
+                                  void* hip_stream) {
+  return run_step(kMomentum, tensors, n, hp, hip_stream);
 }

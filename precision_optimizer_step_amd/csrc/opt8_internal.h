@@ -30,10 +30,13 @@ static_assert(sizeof(DevTensor) == 80, "descriptor layout");
 
 // Scalars of one step, computed on the host in double and rounded once to fp32.
 struct StepScalars {
-  float beta1, beta2, w1, w2, eps, step_size, rbc2, lrwd;
+  float beta1, beta2, w1, w2, eps, step_size, rbc2, lrwd, lr;
   uint32_t seed_lo, seed_hi, step_lo;
   int32_t param_round;   // 0 stochastic, 1 nearest-even
 };
+
+// Update rules sharing the state machinery.
+enum Algo : int { kAdamW = 0, kLion = 1, kMomentum = 2 };
 
 // Host-built lookup tables, uploaded once per device and staged by every
 // workgroup into LDS with the same byte layout:
@@ -67,9 +70,9 @@ enum class Kind : int { k8bit = 0, kBf16 = 1, kFp32 = 2, k8bitTail = 3 };
 
 // Kernel side (opt8_kernels.hip).
 hipError_t upload_tables(const uint8_t* host_tables);   // kTableBytes, to the current device
-hipError_t launch_step(Kind kind, const DevTensor* dev_list, int ntensors, int64_t total_blocks,
-                       const StepScalars& sc, hipStream_t stream, int grid_cap);
-// Workgroups per CU that the kernel of this kind can keep resident.
-int occupancy_per_cu(Kind kind);
+hipError_t launch_step(Kind kind, int algo, const DevTensor* dev_list, int ntensors,
+                       int64_t total_blocks, const StepScalars& sc, hipStream_t stream, int grid_cap);
+// Workgroups per CU that the kernel of this kind and algorithm can keep resident.
+int occupancy_per_cu(Kind kind, int algo);
 
 }  // namespace opt8

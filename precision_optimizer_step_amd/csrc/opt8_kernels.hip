@@ -706,6 +706,228 @@ __device__ __forceinline__ void block_fp32(const DevTensor& d, int64_t blk, int 
   }
 }
 
+// ----------------------------------------------------------------------------- Lion, momentum
+// One-state rules on the same machinery (readings: Lion as in "Symbolic
+// Discovery of Optimization Algorithms", SGD momentum with dampening 0, weight
+// decay decoupled as for AdamW; the pages name both, "8-bit Optimizers via
+// Block-wise Quantization", motivation, and "Stochastic rounding support for
+// 8-bit optimizers", motivation).  Returns the new fp32 parameter.
+template <int A>
+__device__ __forceinline__ float update1(float p, float g, float m1, const StepScalars& sc, float& m2) {
+  if constexpr (A == kLion) {
+    const float c = sc.beta1 * m1 + sc.w1 * g;          // direction from the old moment
+    m2 = sc.beta2 * m1 + sc.w2 * g;
+    // lr * sign(c): +-lr, +0 for a zero c, NaN for a NaN c
+    const float t = (c > 0.0f) ? sc.lr : (c < 0.0f) ? -sc.lr : (c == c) ? 0.0f : c;
+    return (p - sc.lrwd * p) - t;
+  } else {
+    m2 = sc.beta1 * m1 + g;
+    return (p - sc.lrwd * p) - sc.lr * m2;
+  }
+}
+
+// 8-bit state, plain path: partial blocks and any block with a NaN result or a
+// non-finite moment.
+template <int A, bool kFull>
+__device__ __forceinline__ void block_1s_8bit_plain(const DevTensor& d, int64_t blk, int lane, int valid,
+                                                    const StepScalars& sc, const uint8_t* lds) {
+  const float* cb_s = reinterpret_cast<const float*>(lds + kOffCbS);
+  const float* mid_s = reinterpret_cast<const float*>(lds + kOffMidS);
+  const int64_t e0 = blk * kBlock;
+  const uint16_t* gp = d.grad + e0;
+  uint16_t* pp = d.param + e0;
+  uint8_t* mp = static_cast<uint8_t*>(d.m) + e0;
+  const float am = d.amax_m[blk];
+  const bool nearest = sc.param_round != 0;
+  float M2[kGroups * 8];
+  float mxm = 0.0f;
+  const uint64_t grp0 = static_cast<uint64_t>(d.index_base + e0) >> 3;
+#pragma unroll
+  for (int r = 0; r < kGroups; ++r) {
+    const int off = r * 512 + lane * 8;
+    uint4 G, P;
+    uint2 QM;
+    if (kFull) {
+      G = *reinterpret_cast<const uint4*>(gp + off);
+      P = *reinterpret_cast<const uint4*>(pp + off);
+      QM = *reinterpret_cast<const uint2*>(mp + off);
+    } else {
+      uint32_t g32[4] = {0, 0, 0, 0}, p32[4] = {0, 0, 0, 0}, m32[2] = {0, 0};
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        if (off + j < valid) {
+          g32[j >> 1] |= static_cast<uint32_t>(gp[off + j]) << (16 * (j & 1));
+          p32[j >> 1] |= static_cast<uint32_t>(pp[off + j]) << (16 * (j & 1));
+          m32[j >> 2] |= static_cast<uint32_t>(mp[off + j]) << (8 * (j & 3));
+        }
+      }
+      G = make_uint4(g32[0], g32[1], g32[2], g32[3]);
+      P = make_uint4(p32[0], p32[1], p32[2], p32[3]);
+      QM = make_uint2(m32[0], m32[1]);
+    }
+    Rand4 rnd{{0, 0, 0, 0}};
+    if (!nearest) rnd = group_bits(grp0 + (off >> 3), 0u, d.tensor_id, sc);
+    uint32_t outw[4] = {0, 0, 0, 0};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      float m2;
+      const float pn = update1<A>(bf16_at(P, j), bf16_at(G, j), cb_s[byte_at(QM, j)] * am, sc, m2);
+      outw[j >> 1] |= to_bf16(pn, r16_of(rnd, j), nearest) << (16 * (j & 1));
+      const bool ok = kFull || (off + j < valid);
+      M2[r * 8 + j] = ok ? m2 : 0.0f;
+      mxm = nan_max(mxm, fabsf(M2[r * 8 + j]));
+    }
+    if (kFull) {
+      *reinterpret_cast<uint4*>(pp + off) = make_uint4(outw[0], outw[1], outw[2], outw[3]);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (off + j < valid) pp[off + j] = static_cast<uint16_t>(outw[j >> 1] >> (16 * (j & 1)));
+    }
+  }
+  mxm = wave_nan_max(mxm);
+  const bool live = mxm >= kMinNormal;
+  const float inv = live ? 1.0f / mxm : 0.0f;
+#pragma unroll
+  for (int r = 0; r < kGroups; ++r) {
+    const int off = r * 512 + lane * 8;
+    uint32_t cm[2] = {0, 0};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t q = live ? code_search(M2[r * 8 + j] * inv, mid_s) : 127u;
+      cm[j >> 2] |= q << (8 * (j & 3));
+    }
+    if (kFull) {
+      *reinterpret_cast<uint2*>(mp + off) = make_uint2(cm[0], cm[1]);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (off + j < valid) mp[off + j] = static_cast<uint8_t>(cm[j >> 2] >> (8 * (j & 3)));
+    }
+  }
+  if (lane == 0) d.amax_m[blk] = mxm;
+}
+
+// 8-bit state, full block: LUT requantisation and the plain add-and-truncate
+// rounding; returns false (nothing written) on a NaN parameter or moment, or
+// an infinite block maximum.
+template <int A, bool kNearest>
+__device__ __forceinline__ bool block_1s_8bit_fast(const DevTensor& d, int64_t blk, int lane,
+                                                   const StepScalars& sc, const uint8_t* lds) {
+  const float* cb_s = reinterpret_cast<const float*>(lds + kOffCbS);
+  const float* mid_s = reinterpret_cast<const float*>(lds + kOffMidS);
+  const int64_t e0 = blk * kBlock;
+  const uint16_t* gp = d.grad + e0;
+  uint16_t* pp = d.param + e0;
+  uint8_t* mp = static_cast<uint8_t*>(d.m) + e0;
+  const float am = d.amax_m[blk];
+  uint4 G[kGroups], P[kGroups];
+  uint2 QM[kGroups];
+#pragma unroll
+  for (int r = 0; r < kGroups; ++r) {
+    const int off = r * 512 + lane * 8;
+    G[r] = ld_stream16(gp + off);
+    P[r] = ld_stream16(pp + off);
+    QM[r] = ld_stream8(mp + off);
+  }
+  uint32_t c0[4] = {0, 0, 0, 0}, c1[4] = {0, 0, 0, 0}, c2[4] = {0, 0, 0, 0}, c3[4] = {0, 0, 0, 0};
+  if (!kNearest) {
+    const uint64_t grp0 = (static_cast<uint64_t>(d.index_base + e0) >> 3) + static_cast<uint64_t>(lane);
+#pragma unroll
+    for (int r = 0; r < kGroups; ++r) {
+      const uint64_t grp = grp0 + static_cast<uint64_t>(r * 64);
+      c0[r] = static_cast<uint32_t>(grp);
+      c1[r] = static_cast<uint32_t>(grp >> 32);
+      c2[r] = sc.step_lo;
+      c3[r] = d.tensor_id;
+    }
+    philox10_x4(c0, c1, c2, c3, sc.seed_lo, sc.seed_hi);
+  }
+  float M2[kGroups * 8];
+  float mxm = 0.0f;
+  uint64_t nan_lanes = 0;
+#pragma unroll
+  for (int r = 0; r < kGroups; ++r) {
+    const Rand4 rnd{{c0[r], c1[r], c2[r], c3[r]}};
+    uint32_t sums[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      float m2;
+      const float pn = update1<A>(bf16_at(P[r], j), bf16_at(G[r], j), cb_s[byte_at(QM[r], j)] * am, sc, m2);
+      M2[r * 8 + j] = m2;
+      mxm = fmaxf(mxm, fabsf(m2));
+      // a NaN moment need not make a NaN parameter (Lion with beta2 = 0 and an
+      // infinite old moment), and fmaxf would drop it from the maximum
+      nan_lanes |= __builtin_amdgcn_ballot_w64(__builtin_isunordered(pn, m2));
+      const uint32_t b = __float_as_uint(pn);
+      sums[j] = b + (kNearest ? (0x7FFFu + ((b >> 16) & 1u)) : r16_of(rnd, j));
+    }
+    P[r] = make_uint4(__builtin_amdgcn_perm(sums[1], sums[0], 0x07060302u),
+                      __builtin_amdgcn_perm(sums[3], sums[2], 0x07060302u),
+                      __builtin_amdgcn_perm(sums[5], sums[4], 0x07060302u),
+                      __builtin_amdgcn_perm(sums[7], sums[6], 0x07060302u));
+  }
+  mxm = wave_max(mxm);
+  if (nan_lanes != 0 || !(mxm <= 3.0e38f)) return false;
+#pragma unroll
+  for (int r = 0; r < kGroups; ++r) st_stream16(pp + r * 512 + lane * 8, P[r]);
+  const bool live = mxm >= kMinNormal;
+  const float inv = live ? 1.0f / mxm : 0.0f;
+#pragma unroll
+  for (int r = 0; r < kGroups; ++r) {
+    uint32_t cm[2] = {0, 0};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) cm[j >> 2] |= code_s(M2[r * 8 + j] * inv, lds, mid_s) << (8 * (j & 3));
+    if (!live) cm[0] = cm[1] = 0x7F7F7F7Fu;
+    st_stream8(mp + r * 512 + lane * 8, make_uint2(cm[0], cm[1]));
+  }
+  if (lane == 0) d.amax_m[blk] = mxm;
+  return true;
+}
+
+// bf16 or fp32 state (any block, partial included): plain operations.
+template <int A, bool kBf16State>
+__device__ __forceinline__ void block_1s_wide(const DevTensor& d, int64_t blk, int lane, int valid,
+                                              const StepScalars& sc) {
+  const int64_t e0 = blk * kBlock;
+  const uint16_t* gp = d.grad + e0;
+  uint16_t* pp = d.param + e0;
+  const bool nearest = sc.param_round != 0;
+  const uint64_t grp0 = static_cast<uint64_t>(d.index_base + e0) >> 3;
+#pragma unroll 1
+  for (int r = 0; r < kGroups; ++r) {
+    const int off = r * 512 + lane * 8;
+    float g[8], p[8], m1[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const bool ok = off + j < valid;
+      g[j] = ok ? __uint_as_float(static_cast<uint32_t>(gp[off + j]) << 16) : 0.0f;
+      p[j] = ok ? __uint_as_float(static_cast<uint32_t>(pp[off + j]) << 16) : 0.0f;
+      if constexpr (kBf16State)
+        m1[j] = ok ? __uint_as_float(static_cast<uint32_t>(static_cast<uint16_t*>(d.m)[e0 + off + j]) << 16)
+                   : 0.0f;
+      else
+        m1[j] = ok ? static_cast<float*>(d.m)[e0 + off + j] : 0.0f;
+    }
+    const uint64_t grp = grp0 + (off >> 3);
+    Rand4 rp{{0, 0, 0, 0}}, rm{{0, 0, 0, 0}};
+    if (!nearest) rp = group_bits(grp, 0u, d.tensor_id, sc);
+    if (kBf16State) rm = group_bits(grp, 1u, d.tensor_id, sc);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      float m2;
+      const float pn = update1<A>(p[j], g[j], m1[j], sc, m2);
+      if (off + j < valid) {
+        pp[off + j] = static_cast<uint16_t>(to_bf16(pn, r16_of(rp, j), nearest));
+        if constexpr (kBf16State)
+          static_cast<uint16_t*>(d.m)[e0 + off + j] = static_cast<uint16_t>(to_bf16(m2, r16_of(rm, j), false));
+        else
+          static_cast<float*>(d.m)[e0 + off + j] = m2;
+      }
+    }
+  }
+}
+
 // ----------------------------------------------------------------------------- driver
 __device__ __forceinline__ void stage_tables(uint8_t* lds) {
   uint4* dst = reinterpret_cast<uint4*>(lds);
@@ -715,7 +937,7 @@ __device__ __forceinline__ void stage_tables(uint8_t* lds) {
   __syncthreads();
 }
 
-template <Kind K>
+template <Kind K, int A>
 __global__ void __launch_bounds__(kThreads)
 step_kernel(const DevTensor* __restrict__ list, int ntensors, int64_t total_blocks, StepScalars sc,
             int range_ok) {
@@ -741,7 +963,20 @@ step_kernel(const DevTensor* __restrict__ list, int ntensors, int64_t total_bloc
   for (; b < bend; ++b) {
     while (b >= d.block_begin + static_cast<int64_t>(d.nblocks)) d = list[++t];
     const int64_t blk = b - d.block_begin;
-    if constexpr (K == Kind::k8bit) {
+    if constexpr (A != kAdamW) {
+      if constexpr (K == Kind::k8bit) {
+        const bool done = sc.param_round ? block_1s_8bit_fast<A, true>(d, blk, lane, sc, lds)
+                                         : block_1s_8bit_fast<A, false>(d, blk, lane, sc, lds);
+        if (!done) block_1s_8bit_plain<A, true>(d, blk, lane, kBlock, sc, lds);
+      } else if constexpr (K == Kind::k8bitTail) {
+        const int64_t tail = (d.numel - 1) / kBlock;
+        block_1s_8bit_plain<A, false>(d, tail, lane, static_cast<int>(d.numel - tail * kBlock), sc, lds);
+      } else {
+        const int64_t left = d.numel - blk * kBlock;
+        const int valid = left >= kBlock ? kBlock : static_cast<int>(left);
+        block_1s_wide<A, K == Kind::kBf16>(d, blk, lane, valid, sc);
+      }
+    } else if constexpr (K == Kind::k8bit) {
       // this list holds the full blocks of 8-bit tensors only
       const bool done = sc.param_round ? block_8bit_fast<true>(d, blk, lane, sc, lds, range_ok != 0)
                                        : block_8bit_fast<false>(d, blk, lane, sc, lds, range_ok != 0);
@@ -766,23 +1001,44 @@ step_kernel(const DevTensor* __restrict__ list, int ntensors, int64_t total_bloc
   }
 }
 
-template <Kind K>
+template <Kind K, int A>
 hipError_t launch_kind(const DevTensor* list, int n, int64_t total_blocks, const StepScalars& sc,
                        hipStream_t stream, int grid_cap, int range_ok) {
   int64_t grid = (total_blocks + kWaves - 1) / kWaves;
   if (grid_cap > 0 && grid > grid_cap) grid = grid_cap;
   if (grid < 1) grid = 1;
-  hipLaunchKernelGGL(step_kernel<K>, dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0, stream,
+  hipLaunchKernelGGL((step_kernel<K, A>), dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0, stream,
                      list, n, total_blocks, sc, range_ok);
   return hipGetLastError();
 }
 
-template <Kind K>
+template <Kind K, int A>
 int occupancy_kind() {
   int n = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, step_kernel<K>, kThreads, 0) != hipSuccess)
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, step_kernel<K, A>, kThreads, 0) != hipSuccess)
     return 1;
   return n > 0 ? n : 1;
+}
+
+template <Kind K>
+hipError_t launch_algo(int algo, const DevTensor* list, int n, int64_t total_blocks, const StepScalars& sc,
+                       hipStream_t stream, int grid_cap, int range_ok) {
+  switch (algo) {
+    case kAdamW: return launch_kind<K, kAdamW>(list, n, total_blocks, sc, stream, grid_cap, range_ok);
+    case kLion: return launch_kind<K, kLion>(list, n, total_blocks, sc, stream, grid_cap, range_ok);
+    case kMomentum: return launch_kind<K, kMomentum>(list, n, total_blocks, sc, stream, grid_cap, range_ok);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <Kind K>
+int occupancy_algo(int algo) {
+  switch (algo) {
+    case kAdamW: return occupancy_kind<K, kAdamW>();
+    case kLion: return occupancy_kind<K, kLion>();
+    case kMomentum: return occupancy_kind<K, kMomentum>();
+  }
+  return 1;
 }
 
 }  // namespace
@@ -791,28 +1047,28 @@ hipError_t upload_tables(const uint8_t* host_tables) {
   return hipMemcpyToSymbol(HIP_SYMBOL(g_tables), host_tables, kTableBytes, 0, hipMemcpyHostToDevice);
 }
 
-hipError_t launch_step(Kind kind, const DevTensor* list, int n, int64_t total_blocks,
+hipError_t launch_step(Kind kind, int algo, const DevTensor* list, int n, int64_t total_blocks,
                        const StepScalars& sc, hipStream_t stream, int grid_cap) {
   if (n <= 0 || total_blocks <= 0) return hipSuccess;
-  // the fast 8-bit path needs eps well inside the normal range and a bounded
-  // second-moment correction (it then checks each block's own values)
+  // the fast AdamW paths need eps well inside the normal range and a bounded
+  // second-moment correction (they then check each block's own values)
   const int range_ok = (sc.eps >= 0x1p-60f && sc.eps <= 0x1p+60f && sc.rbc2 <= 0x1p+20f) ? 1 : 0;
   switch (kind) {
-    case Kind::k8bit: return launch_kind<Kind::k8bit>(list, n, total_blocks, sc, stream, grid_cap, range_ok);
+    case Kind::k8bit: return launch_algo<Kind::k8bit>(algo, list, n, total_blocks, sc, stream, grid_cap, range_ok);
     case Kind::k8bitTail:
-      return launch_kind<Kind::k8bitTail>(list, n, total_blocks, sc, stream, grid_cap, range_ok);
-    case Kind::kBf16: return launch_kind<Kind::kBf16>(list, n, total_blocks, sc, stream, grid_cap, range_ok);
-    case Kind::kFp32: return launch_kind<Kind::kFp32>(list, n, total_blocks, sc, stream, grid_cap, range_ok);
+      return launch_algo<Kind::k8bitTail>(algo, list, n, total_blocks, sc, stream, grid_cap, range_ok);
+    case Kind::kBf16: return launch_algo<Kind::kBf16>(algo, list, n, total_blocks, sc, stream, grid_cap, range_ok);
+    case Kind::kFp32: return launch_algo<Kind::kFp32>(algo, list, n, total_blocks, sc, stream, grid_cap, range_ok);
   }
   return hipErrorInvalidValue;
 }
 
-int occupancy_per_cu(Kind kind) {
+int occupancy_per_cu(Kind kind, int algo) {
   switch (kind) {
-    case Kind::k8bit: return occupancy_kind<Kind::k8bit>();
-    case Kind::k8bitTail: return occupancy_kind<Kind::k8bitTail>();
-    case Kind::kBf16: return occupancy_kind<Kind::kBf16>();
-    case Kind::kFp32: return occupancy_kind<Kind::kFp32>();
+    case Kind::k8bit: return occupancy_algo<Kind::k8bit>(algo);
+    case Kind::k8bitTail: return occupancy_algo<Kind::k8bitTail>(algo);
+    case Kind::kBf16: return occupancy_algo<Kind::kBf16>(algo);
+    case Kind::kFp32: return occupancy_algo<Kind::kFp32>(algo);
   }
   return 1;
 }

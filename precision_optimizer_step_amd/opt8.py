@@ -88,9 +88,11 @@ def lib() -> ctypes.CDLL:
         L.opt8_init_codebooks.restype = ctypes.c_int
         L.opt8_default_mode.argtypes = [ctypes.c_int64]
         L.opt8_default_mode.restype = ctypes.c_int32
-        L.opt8_adamw_step.argtypes = [ctypes.POINTER(opt8_tensor), ctypes.c_int32,
-                                      ctypes.POINTER(opt8_hparams), ctypes.c_void_p]
-        L.opt8_adamw_step.restype = ctypes.c_int
+        for name in ("opt8_adamw_step", "opt8_lion_step", "opt8_momentum_step"):
+            fn = getattr(L, name)
+            fn.argtypes = [ctypes.POINTER(opt8_tensor), ctypes.c_int32,
+                           ctypes.POINTER(opt8_hparams), ctypes.c_void_p]
+            fn.restype = ctypes.c_int
         L.opt8_last_error.argtypes = []
         L.opt8_last_error.restype = ctypes.c_char_p
         _lib = L
@@ -158,24 +160,41 @@ def tensor_array(descs) -> ctypes.Array:
     return arr
 
 
+def _stream_handle(stream):
+    if stream is None:
+        try:
+            import torch
+            return torch.cuda.current_stream().cuda_stream if torch.cuda.is_available() else 0
+        except ImportError:
+            return 0
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _run(fn, tensors, hp, stream, n, check):
+    if not isinstance(tensors, ctypes.Array):
+        tensors = tensor_array(tensors)
+    count = getattr(tensors, "_n", len(tensors)) if n is None else int(n)
+    handle = _stream_handle(stream)
+    rc = fn(tensors, count, ctypes.byref(hp), ctypes.c_void_p(handle or None))
+    return _check(rc) if check else rc
+
+
 def opt8_adamw_step(tensors, hp: opt8_hparams, stream=None, n=None, check: bool = True) -> int:
-    """One fused step over a descriptor list (a list of opt8_tensor or tensor_array()).
+    """One fused AdamW step over a descriptor list (a list of opt8_tensor or tensor_array()).
 
     stream: a torch.cuda.Stream, a raw hipStream_t int, or None for the current
     torch stream (the null stream if torch is not in use).
     """
-    if not isinstance(tensors, ctypes.Array):
-        tensors = tensor_array(tensors)
-    count = getattr(tensors, "_n", len(tensors)) if n is None else int(n)
-    if stream is None:
-        try:
-            import torch
-            handle = torch.cuda.current_stream().cuda_stream if torch.cuda.is_available() else 0
-        except ImportError:
-            handle = 0
-    elif isinstance(stream, int):
-        handle = stream
-    else:
-        handle = stream.cuda_stream
-    rc = lib().opt8_adamw_step(tensors, count, ctypes.byref(hp), ctypes.c_void_p(handle or None))
-    return _check(rc) if check else rc
+    return _run(lib().opt8_adamw_step, tensors, hp, stream, n, check)
+
+
+def opt8_lion_step(tensors, hp: opt8_hparams, stream=None, n=None, check: bool = True) -> int:
+    """One fused Lion step (v, absmax_v and eps unused); arguments as for opt8_adamw_step."""
+    return _run(lib().opt8_lion_step, tensors, hp, stream, n, check)
+
+
+def opt8_momentum_step(tensors, hp: opt8_hparams, stream=None, n=None, check: bool = True) -> int:
+    """One fused SGD-with-momentum step (beta1 = momentum; v, absmax_v, beta2, eps unused)."""
+    return _run(lib().opt8_momentum_step, tensors, hp, stream, n, check)

@@ -35,7 +35,8 @@ def declared_functions():
 
 def test_library_exports_every_declared_symbol(L):
     names = declared_functions()
-    assert names == ["opt8_adamw_step", "opt8_default_mode", "opt8_init_codebooks", "opt8_last_error"]
+    assert names == ["opt8_adamw_step", "opt8_default_mode", "opt8_init_codebooks", "opt8_last_error",
+                     "opt8_lion_step", "opt8_momentum_step"]
     out = subprocess.run(["nm", "-D", "--defined-only", opt8.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = set(re.findall(r"\bT (opt8_\w+)", out))
@@ -184,3 +185,32 @@ def test_binding_raises_on_error(L):
     with pytest.raises(opt8.Opt8Error) as e:
         opt8.opt8_adamw_step([fake_tensor(0, numel=0)], opt8.make_hparams(1e-3), stream=0)
     assert e.value.status == opt8.OPT8_E_SIZE
+
+
+ONE_STATE = [("opt8_lion_step", opt8.opt8_lion_step), ("opt8_momentum_step", opt8.opt8_momentum_step)]
+
+
+@pytest.mark.parametrize("name,fn", ONE_STATE)
+def test_one_state_rules_ignore_v_and_eps(L, name, fn):
+    """Lion and momentum accept NULL v / absmax_v, overlapping garbage in v, and eps = 0;
+    everything else is validated as for AdamW."""
+    def run(descs, hp=None, n=None):
+        hp = hp or opt8.make_hparams(1e-4, weight_decay=0.1, step=1, seed=1)
+        return fn(opt8.tensor_array(descs), hp, stream=0, n=n, check=False)
+    ok = (opt8.OPT8_E_HIP, opt8.OPT8_E_NOT_INIT)
+    rc = run([fake_tensor(0, v=None, absmax_v=None), fake_tensor(1, mode=opt8.OPT8_STATE_FP32, numel=100,
+                                                               v=None, absmax_v=None)])
+    assert rc in ok, opt8.opt8_last_error()
+    # v is not read: an address overlapping m is not an alias
+    assert run([fake_tensor(0, v=BASE + (2 << 28))]) in ok, opt8.opt8_last_error()
+    assert run([fake_tensor(0)], hp=opt8.make_hparams(1e-4, eps=0.0)) in ok, opt8.opt8_last_error()
+    expect(run([fake_tensor(0, m=None)]), opt8.OPT8_E_NULL, "tensor 0")
+    expect(run([fake_tensor(0, absmax_m=None)]), opt8.OPT8_E_NULL, "absmax_m")
+    expect(run([fake_tensor(0, m=BASE + (2 << 28) + 1)]), opt8.OPT8_E_ALIGN)
+    expect(run([fake_tensor(0, m=BASE + 4096)]), opt8.OPT8_E_ALIAS)
+    expect(run([fake_tensor(0, tid=3), fake_tensor(1, tid=3)]), opt8.OPT8_E_DUPID)
+    expect(run([fake_tensor(0)], hp=opt8.make_hparams(-1.0)), opt8.OPT8_E_HPARAM)
+    expect(run([fake_tensor(0)], hp=opt8.make_hparams(1e-4, beta1=1.0)), opt8.OPT8_E_HPARAM)
+    expect(run([fake_tensor(0)], hp=opt8.make_hparams(1e-4, step=0)), opt8.OPT8_E_HPARAM)
+    expect(run([fake_tensor(0, mode=7)]), opt8.OPT8_E_MODE)
+    assert run([], n=0) == opt8.OPT8_OK

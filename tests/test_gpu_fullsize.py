@@ -13,13 +13,11 @@ import pytest
 import torch
 
 import oracle
-from gpu_helpers import compare_state, log
+from gpu_helpers import build_list, compare_state, descriptors, log, sample_blocks, snapshot
 from precision_optimizer_step_amd import opt8
-from workloads import gen, shapes
+from workloads import shapes
 
 pytestmark = pytest.mark.gpu
-
-BLOCK = 2048
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -28,81 +26,6 @@ def device():
         pytest.fail("GPU tests need a visible AMD GPU")
     torch.cuda.set_device(0)
     opt8.opt8_init_codebooks()
-
-
-def _mode_of(w, spec):
-    if w.state_mode == "bf16":
-        return oracle.MODE_BF16_SR
-    return opt8.opt8_default_mode(spec.numel)
-
-
-def build_list(w, step=1, state_seed=7):
-    """Device tensors of workload w: params, step-`step` grads and a random non-zero state."""
-    dev = torch.device("cuda:0")
-    g = torch.Generator(device=dev)
-    out = []
-    for tid, spec in enumerate(w.tensors):
-        n = spec.numel
-        mode = _mode_of(w, spec)
-        P = torch.empty(n, dtype=torch.bfloat16, device=dev)
-        G = torch.empty(n, dtype=torch.bfloat16, device=dev)
-        gen.param_init_device(spec, w, tid, P)
-        gen.grad_init_device(spec, w, step, tid, G)
-        g.manual_seed(gen.derived_seed(state_seed, 0, tid, gen.P_STATE_M))
-        AM = AV = None
-        if mode == oracle.MODE_8BIT:
-            M = torch.randint(0, 256, (n,), dtype=torch.uint8, device=dev, generator=g)
-            V = torch.randint(0, 256, (n,), dtype=torch.uint8, device=dev, generator=g)
-            nb = (n + BLOCK - 1) // BLOCK
-            AM = torch.empty(nb, dtype=torch.float32, device=dev).normal_(0, 1e-3, generator=g).abs_()
-            AV = torch.empty(nb, dtype=torch.float32, device=dev).normal_(0, 1e-3, generator=g).square_()
-        elif mode == oracle.MODE_BF16_SR:
-            M = torch.empty(n, dtype=torch.bfloat16, device=dev).normal_(0, 1e-3, generator=g)
-            V = torch.empty(n, dtype=torch.bfloat16, device=dev).normal_(0, 1e-3, generator=g).square_()
-        else:
-            M = torch.empty(n, dtype=torch.float32, device=dev).normal_(0, 1e-3, generator=g)
-            V = torch.empty(n, dtype=torch.float32, device=dev).normal_(0, 1e-3, generator=g).square_()
-        out.append(dict(tid=tid, mode=mode, n=n, P=P, G=G, M=M, V=V, AM=AM, AV=AV))
-    return out
-
-
-def descriptors(lst):
-    return opt8.tensor_array(opt8.make_tensor(t["P"], t["G"], t["M"], t["V"], t["AM"], t["AV"],
-                                              tensor_id=t["tid"], mode=t["mode"]) for t in lst)
-
-
-def sample_blocks(lst, per_tensor, rng):
-    pick = []
-    for i, t in enumerate(lst):
-        nb = (t["n"] + BLOCK - 1) // BLOCK
-        cand = {0, nb - 1}
-        if nb > 2:
-            cand |= set(int(x) for x in rng.integers(1, nb - 1, min(per_tensor, nb - 2)))
-        pick += [(i, b) for b in sorted(cand)]
-    return pick
-
-
-def _np(t, dtype):
-    h = t.detach().cpu()
-    if h.dtype == torch.bfloat16:
-        h = h.view(torch.int16)
-    return h.numpy().view(dtype).copy()
-
-
-def snapshot(lst, blocks):
-    snap = []
-    for i, b in blocks:
-        t = lst[i]
-        lo, hi = b * BLOCK, min(t["n"], (b + 1) * BLOCK)
-        sd = np.uint8 if t["mode"] == oracle.MODE_8BIT else np.uint16 if t["mode"] == oracle.MODE_BF16_SR \
-            else np.float32
-        item = dict(p=_np(t["P"][lo:hi], np.uint16), g=_np(t["G"][lo:hi], np.uint16),
-                    m=_np(t["M"][lo:hi], sd), v=_np(t["V"][lo:hi], sd), am=None, av=None)
-        if t["AM"] is not None:
-            item["am"] = _np(t["AM"][b:b + 1], np.float32)
-            item["av"] = _np(t["AV"][b:b + 1], np.float32)
-        snap.append(item)
-    return snap
 
 
 @pytest.mark.parametrize("name", ["gptneo-6.7b", "gptneo-2.7b", "gptneo-2.7b-bf16", "lm-1.5b", "gpt2-350m"])
