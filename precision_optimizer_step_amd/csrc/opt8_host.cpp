@@ -93,10 +93,6 @@ float bits_f32(uint32_t b) {
   return f;
 }
 
-// Inverse of the monotone map fp32 -> uint32 that flips the sign bit of
-// non-negative values and every bit of negative ones.
-float unsortable(uint32_t u) { return bits_f32((u >> 31) ? (u & 0x7FFFFFFFu) : ~u); }
-
 // #{k : mid[k] < x} is constant on a bucket except at most one step; the LUT
 // entry is its value at the bucket's smallest member.  Returns false if a
 // bucket holds two midpoints (the lookup would then be wrong).
@@ -107,20 +103,20 @@ bool lut_entry(const float* mid, float least, float most, uint8_t& out) {
   return top - base <= 1;
 }
 
-// Code LUTs for the signed table (keys of sortable(n) >> 17) and the unsigned
-// table (keys of bits(n) >> 16, clamped below at kKeyLo).
+// Code LUTs: the signed table keyed by bits(n) >> 17 (a bucket of n >= +0
+// grows with its bits, one of n <= -0 shrinks), the unsigned table keyed by
+// bits(n) >> 16, clamped below at kKeyLo.
 bool build_luts(uint8_t* bytes) {
   const float* mid_s = reinterpret_cast<const float*>(bytes + kOffMidS);
   const float* mid_u = reinterpret_cast<const float*>(bytes + kOffMidU);
-  for (uint32_t key = kKeySLo; key <= kKeySHi; ++key) {
-    const float least = unsortable(key << 17);
-    const float most = unsortable((key << 17) | 0x1FFFFu);
-    if (!lut_entry(mid_s, least, most, bytes[key])) return false;
-  }
+  for (uint32_t key = 0; key < kKeySPosEnd; ++key)
+    if (!lut_entry(mid_s, bits_f32(key << 17), bits_f32((key << 17) | 0x1FFFFu), bytes[key])) return false;
+  for (uint32_t key = kKeySNeg; key < kKeySNegEnd; ++key)
+    if (!lut_entry(mid_s, bits_f32((key << 17) | 0x1FFFFu), bits_f32(key << 17), bytes[key])) return false;
   for (uint32_t key = kKeyLo; key <= kKeyHi; ++key) {
     const float least = key == kKeyLo ? 0.0f : bits_f32(key << 16);
     const float most = bits_f32((key << 16) | 0xFFFFu);
-    if (!lut_entry(mid_u, least, most, bytes[key + kOffLutU])) return false;
+    if (!lut_entry(mid_u, least, most, bytes[key])) return false;
   }
   return true;
 }

@@ -39,32 +39,31 @@ struct StepScalars {
 enum Algo : int { kAdamW = 0, kLion = 1, kMomentum = 2 };
 
 // Host-built lookup tables, uploaded once per device and staged by every
-// workgroup into LDS with the same byte layout:
-//   [0, 1024)      signed codebook (fp32[256], ascending)
-//   [1024, 2048)   signed midpoints (fp32[255], then +inf)
-//   [2048, 3072)   unsigned codebook
-//   [3072, 4096)   unsigned midpoints (fp32[255], then +inf)
-//   signed code LUT (u8) at byte k for the key k = sortable(n) >> 17, where
-//                  sortable(n) flips the sign bit of n >= 0 and every bit of
-//                  n < 0, so keys grow with n; keys of |n| < 2 span
-//                  [kKeySLo, kKeySHi].
-//   unsigned code LUT (u8) at byte k + kOffLutU for the key
-//                  k = max(bits(n) >> 16, kKeyLo) of n >= 0 (magnitudes below
-//                  2^-27 share the lowest bucket); keys of n < 2 end at kKeyHi.
-// Each entry is the code of the smallest value of its bucket (the values
-// sharing a key).  No bucket holds more than one midpoint (checked when the
-// tables are built), so code = lut + (mid[lut] < n) exactly.
-constexpr uint32_t kKeySLo = 0x1FFFu;       // sortable(-2) >> 17
-constexpr uint32_t kKeySHi = 0x6000u;       // sortable(+2) >> 17
-constexpr uint32_t kKeyLo = 100u << 7;      // |n| < 2^-27 share the lowest bucket
-constexpr uint32_t kKeyHi = 0x3FFFu;        // last key below 2.0
-constexpr int kLutSN = static_cast<int>(kKeySHi - kKeySLo + 1);
-constexpr int kLutN = static_cast<int>(kKeyHi - kKeyLo + 1);
-constexpr int kOffCbS = 0, kOffMidS = 1024, kOffCbU = 2048, kOffMidU = 3072;
-constexpr int kOffLutSBytes = static_cast<int>(kKeySLo);   // first byte of the signed LUT
-constexpr int kOffLutUBytes = (kOffLutSBytes + kLutSN + 15) / 16 * 16;
-constexpr int kOffLutU = kOffLutUBytes - static_cast<int>(kKeyLo);   // address = key + kOffLutU
-constexpr int kTableBytes = (kOffLutUBytes + kLutN + 15) / 16 * 16;
+// workgroup into LDS with the same byte layout (every address below is a
+// constant, so each lookup is one LDS read with an immediate offset):
+//   [0x0000, 0x2000)  signed code LUT (u8) for 0 <= n < 2, at byte bits(n) >> 17
+//   [0x2000, 0x2400)  signed codebook (fp32[256], ascending)
+//   [0x2400, 0x2800)  signed midpoints (fp32[255], then +inf)
+//   [0x2800, 0x2C00)  unsigned codebook
+//   [0x2C00, 0x3000)  unsigned midpoints (fp32[255], then +inf)
+//   [0x3200, 0x4000)  unsigned code LUT (u8) for 0 <= n < 2, at byte
+//                     max(bits(n) >> 16, kKeyLo) (magnitudes below 2^-27
+//                     share the lowest bucket)
+//   [0x4000, 0x6000)  signed code LUT (u8) for -2 < n <= -0, at byte bits(n) >> 17
+// A bucket is the set of values sharing a key (a contiguous interval of
+// fp32 values); its entry is the code of its smallest value.  No bucket
+// holds more than one midpoint (checked when the tables are built), so
+// code = lut + (mid[lut] < n) exactly.
+constexpr uint32_t kKeyLo = 100u << 7;      // unsigned key floor: |n| < 2^-27
+constexpr uint32_t kKeyHi = 0x3FFFu;        // last unsigned key below 2.0
+constexpr uint32_t kKeySPosEnd = 0x2000u;   // signed keys of +0 <= n < 2: [0, kKeySPosEnd)
+constexpr uint32_t kKeySNeg = 0x4000u;      // signed keys of -2 < n <= -0: [kKeySNeg, kKeySNegEnd)
+constexpr uint32_t kKeySNegEnd = 0x6000u;
+constexpr int kOffCbS = 0x2000, kOffMidS = 0x2400, kOffCbU = 0x2800, kOffMidU = 0x2C00;
+constexpr int kTableBytes = 0x6000;
+static_assert(kKeyLo == 0x3200u && kOffMidU + 1024 <= static_cast<int>(kKeyLo),
+              "the unsigned LUT sits at its own keys, after the codebooks");
+static_assert(kOffCbS >= static_cast<int>(kKeySPosEnd) && kKeyHi < kKeySNeg, "LUT regions overlap");
 
 enum class Kind : int { k8bit = 0, kBf16 = 1, kFp32 = 2, k8bitTail = 3 };
 

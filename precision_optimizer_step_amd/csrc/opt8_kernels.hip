@@ -89,25 +89,30 @@ __device__ __forceinline__ uint32_t to_bf16(float x, uint32_t r16, bool nearest)
 
 // Streaming global accesses: every byte of the step is read once and written
 // once, so loads and stores are non-temporal (no reuse to keep in the caches).
+// The pointers are cast to the global address space so the accesses are
+// global_* instructions (scalar base + 32-bit lane offset) rather than flat
+// ones, which would also count against the LDS wait counter.
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(1))) u32x4_t g_u32x4_t;
+typedef __attribute__((address_space(1))) u32x2_t g_u32x2_t;
 __device__ __forceinline__ uint4 ld_stream16(const void* p) {
-  const u32x4_t v = __builtin_nontemporal_load(static_cast<const u32x4_t*>(p));
+  const u32x4_t v = __builtin_nontemporal_load((const g_u32x4_t*)(p));
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 __device__ __forceinline__ uint2 ld_stream8(const void* p) {
-  const u32x2_t v = __builtin_nontemporal_load(static_cast<const u32x2_t*>(p));
+  const u32x2_t v = __builtin_nontemporal_load((const g_u32x2_t*)(p));
   return make_uint2(v.x, v.y);
 }
 __device__ __forceinline__ void st_stream16(void* p, const uint4& q) {
   u32x4_t v;
   v.x = q.x; v.y = q.y; v.z = q.z; v.w = q.w;
-  __builtin_nontemporal_store(v, static_cast<u32x4_t*>(p));
+  __builtin_nontemporal_store(v, (g_u32x4_t*)(p));
 }
 __device__ __forceinline__ void st_stream8(void* p, const uint2& q) {
   u32x2_t v;
   v.x = q.x; v.y = q.y;
-  __builtin_nontemporal_store(v, static_cast<u32x2_t*>(p));
+  __builtin_nontemporal_store(v, (g_u32x2_t*)(p));
 }
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
@@ -301,15 +306,12 @@ __device__ __forceinline__ void block_8bit_plain(const DevTensor& d, int64_t blk
 // Codes through the bucket LUTs: code = lut[key] + (mid[lut[key]] < n).
 __device__ __forceinline__ uint32_t code_u(float n, const uint8_t* lds, const float* mid) {
   const uint32_t key = max(__float_as_uint(n) >> 16, kKeyLo);    // 0 <= n < 2
-  const uint32_t c = lds[key + kOffLutU];
+  const uint32_t c = lds[key];
   return c + ((mid[c] < n) ? 1u : 0u);
 }
 
 __device__ __forceinline__ uint32_t code_s(float n, const uint8_t* lds, const float* mid) {
-  const uint32_t b = __float_as_uint(n);                          // -2 < n < 2
-  const uint32_t neg = static_cast<uint32_t>(static_cast<int32_t>(b) >> 31);
-  const uint32_t key = (b ^ (neg | 0x80000000u)) >> 17;          // sortable(n) >> 17
-  const uint32_t c = lds[key];
+  const uint32_t c = lds[__float_as_uint(n) >> 17];              // -2 < n < 2
   return c + ((mid[c] < n) ? 1u : 0u);
 }
 
@@ -339,10 +341,7 @@ __device__ __forceinline__ void philox10_x4(uint32_t (&c0)[4], uint32_t (&c1)[4]
 // take the plain path instead.
 template <bool kNearest>
 __device__ __forceinline__ bool block_8bit_fast(const DevTensor& d, int64_t blk, int lane,
-                                                const StepScalars& sc, const uint8_t* lds,
-                                                bool range_ok) {
-  const float* cb_s = reinterpret_cast<const float*>(lds + kOffCbS);
-  const float* cb_u = reinterpret_cast<const float*>(lds + kOffCbU);
+                                                const StepScalars& sc, const uint8_t* lds, bool range_ok) {
   const int64_t e0 = blk * kBlock;
   const uint16_t* gp = d.grad + e0;
   uint16_t* pp = d.param + e0;
@@ -367,6 +366,8 @@ __device__ __forceinline__ bool block_8bit_fast(const DevTensor& d, int64_t blk,
     P[r] = ld_stream16(pp + r * 512 + lane * 8);
 
   // pass 1: moments, block maxima, smallest exponents
+  const float* cb_s = reinterpret_cast<const float*>(lds + kOffCbS);
+  const float* cb_u = reinterpret_cast<const float*>(lds + kOffCbU);
   float M2[kGroups * 8], V2[kGroups * 8];
   float mxm = 0.0f, mxv = 0.0f;
   int emin = 0;
@@ -931,9 +932,7 @@ __device__ __forceinline__ void block_1s_wide(const DevTensor& d, int64_t blk, i
 // ----------------------------------------------------------------------------- driver
 __device__ __forceinline__ void stage_tables(uint8_t* lds) {
   uint4* dst = reinterpret_cast<uint4*>(lds);
-  // codebooks and midpoints, then the LUTs (the per-wave scratch is not copied)
-  for (int i = threadIdx.x; i < kOffMidU / 16 + 64; i += kThreads) dst[i] = g_tables[i];
-  for (int i = kOffLutSBytes / 16 + threadIdx.x; i < kTableBytes / 16; i += kThreads) dst[i] = g_tables[i];
+  for (int i = threadIdx.x; i < kTableBytes / 16; i += kThreads) dst[i] = g_tables[i];
   __syncthreads();
 }
 
