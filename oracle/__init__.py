@@ -21,11 +21,12 @@ Modules
   rounding  bf16 decode, stochastic rounding and round-to-nearest-even
   adamw     host scalars, block quantiser and the per-tensor AdamW step
   onestate  Lion and SGD with momentum on the same state machinery
+  state_sr  stochastic rounding of the 8-bit state between neighbouring entries
 
 Parity status of each function is stated in its module header.
 """
 
-from . import codebook, philox, rounding, adamw, onestate  # noqa: F401
+from . import codebook, philox, rounding, adamw, onestate, state_sr  # noqa: F401
 from .adamw import (  # noqa: F401
     Hparams,
     Scalars,
@@ -44,3 +45,4 @@ from .adamw import (  # noqa: F401
     default_mode,
 )
 from .onestate import ALGO_LION, ALGO_MOMENTUM, step_tensor_1state  # noqa: F401
+from .state_sr import STATE_ROUND_NEAREST, STATE_ROUND_STOCHASTIC  # noqa: F401

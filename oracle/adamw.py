@@ -45,6 +45,9 @@ Readings where the pages are silent (each repeated where it is used):
     to tensors with fewer than 4096 elements.  The bf16-state mode keeps every
     tensor in bf16 and always rounds the moments stochastically (streams 1 and
     2); the round flag chooses only how the parameter is written.
+  * The 8-bit state is rounded to the nearest codebook entry unless
+    state_round asks for stochastic rounding between the two neighbouring
+    entries (state_sr.py; streams 1 and 2, as for bf16 momenta).
 
 Parity: pinned by tests against closed forms at step 1, torch.optim.AdamW
 on fp32 (test side only), a float64 trajectory, invariants (zero lr and wd
@@ -87,6 +90,7 @@ class Hparams:
     step: int = 1          # 1-based
     seed: int = 0          # 64-bit
     param_round: int = ROUND_STOCHASTIC
+    state_round: int = 0   # 8-bit state: 0 nearest entry, 1 stochastic between neighbours
 
 
 @dataclass
@@ -217,6 +221,13 @@ def step_tensor(mode: int, param, grad, m, v, absmax_m, absmax_v, hp: Hparams,
     p_out = _round_param(pn, hp, tensor_id, index)
 
     if mode == MODE_8BIT:
+        if hp.state_round:
+            from .state_sr import quantize_blockwise_sr
+            qm, am = quantize_blockwise_sr(m2, cs, codebook.SIGNED_ZERO_CODE,
+                                           sr_bits(hp.seed, hp.step, tensor_id, index, STREAM_M))
+            qv, av = quantize_blockwise_sr(v2, cu, codebook.UNSIGNED_ZERO_CODE,
+                                           sr_bits(hp.seed, hp.step, tensor_id, index, STREAM_V))
+            return p_out, qm, qv, am, av
         qm, am = quantize_blockwise(m2, mid_s, codebook.SIGNED_ZERO_CODE)
         qv, av = quantize_blockwise(v2, mid_u, codebook.UNSIGNED_ZERO_CODE)
         return p_out, qm, qv, am, av

@@ -18,8 +18,10 @@ SGD with momentum (the torch.optim.SGD form with dampening 0):
 Everything else is as for the AdamW oracle: fp32 with one rounding per
 operation, host scalars in double rounded once (lr, lrwd, beta, 1-beta), the
 state in one of three modes (8-bit block-wise with the SIGNED dynamic-tree
-codebook, bf16 written with stochastic rounding on stream 1, or fp32), the
-parameter written with stochastic rounding on stream 0 (or nearest-even).
+codebook, rounded to the nearest entry or, as state_round asks, stochastically
+between neighbouring entries; bf16 written with stochastic rounding on stream
+1; or fp32), the parameter written with stochastic rounding on stream 0 (or
+nearest-even).
 
 Parity: Lion is pinned by its step-1 closed form (p(1 - lr wd) - lr sign(g)),
 by the sign invariant |p' - (p - lrwd p)| == lr exactly and by a float64
@@ -109,6 +111,11 @@ def step_tensor_1state(algo: int, mode: int, param, grad, m, absmax_m, hp: Hpara
     else:
         p_out = f32_to_bf16_sr(pn, sr_bits(hp.seed, hp.step, tensor_id, index, STREAM_PARAM))
     if mode == MODE_8BIT:
+        if hp.state_round:
+            from .state_sr import quantize_blockwise_sr
+            qm, am = quantize_blockwise_sr(m2, cs, codebook.SIGNED_ZERO_CODE,
+                                           sr_bits(hp.seed, hp.step, tensor_id, index, STREAM_M))
+            return p_out, qm, am
         qm, am = quantize_blockwise(m2, mid_s, codebook.SIGNED_ZERO_CODE)
         return p_out, qm, am
     if mode == MODE_BF16_SR:
