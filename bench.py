@@ -106,6 +106,8 @@ def parse():
     ap.add_argument("--cpu-sample-elems", type=int, default=96 * 1024 * 1024)
     ap.add_argument("--algo", choices=("adamw", "lion", "momentum"), default="adamw",
                     help="update rule (lion / momentum: one 8-bit state, the same machinery)")
+    ap.add_argument("--state-round", choices=("nearest", "stochastic"), default="nearest",
+                    help="8-bit state rounding: nearest codebook entry, or stochastic between neighbours")
     return ap.parse_args()
 
 
@@ -185,10 +187,11 @@ def main():
              for k in range(pool)]
 
     rnd = opt8.OPT8_ROUND_NEAREST if args.round == "nearest" else opt8.OPT8_ROUND_STOCHASTIC
+    srnd = opt8.OPT8_STATE_ROUND_STOCHASTIC if args.state_round == "stochastic" else opt8.OPT8_STATE_ROUND_NEAREST
 
     def step(t):
         hp = opt8.make_hparams(lr, w.beta1, beta2, w.eps, w.weight_decay, step=t, seed=w.seed,
-                               param_round=rnd)
+                               param_round=rnd, state_round=srnd)
         step_fn(lists[(t - 1) % pool], hp)
 
     # ---------------------------------------------------------------- timing
@@ -225,6 +228,8 @@ def main():
         kname = {0: "step_kernel<8bit>", 1: "step_kernel<bf16>", 2: "step_kernel<fp32>"}[dom]
         if one_state:
             kname = kname[:-1] + f",{args.algo}>"
+        if srnd and dom == 0:
+            kname = kname[:-1] + ",sr-state>"
         traffic = profiled_traffic(kname, w.name)
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": int(traffic) if traffic else None,
@@ -258,7 +263,7 @@ def main():
         am = big["AM"][: (n + BLOCK - 1) // BLOCK].cpu().numpy() if big["AM"] is not None else None
         av = big["AV"][: (n + BLOCK - 1) // BLOCK].cpu().numpy() if big["AV"] is not None else None
         hp = oracle.Hparams(lr=lr, beta1=w.beta1, beta2=beta2, eps=w.eps,
-                            weight_decay=w.weight_decay, step=t_step, seed=w.seed)
+                            weight_decay=w.weight_decay, step=t_step, seed=w.seed, state_round=srnd)
         c0t = time.perf_counter()
         if one_state:
             oracle.step_tensor_1state(algo_id, big["mode"], p, g, m, am, hp, big["tid"])
@@ -285,7 +290,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "tensors": len(tensors), "params": total,
                    "state": "bf16-sr" if w.state_mode == "bf16" else "8bit+fp32<4096",
-                   "param_round": args.round, "algo": args.algo,
+                   "param_round": args.round, "algo": args.algo, "state_round": args.state_round,
                    "grad_pool": pool, "hbm_pct_of_peak": round(100 * sum(alg.values()) / (ms_per_step / 1000.0)
                                                               / 1e9 / HBM_PEAK_GBPS, 2),
                    "attainable_copy_GBps": attain.get("copy"),

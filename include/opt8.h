@@ -51,6 +51,15 @@
  * A value is rounded to the entry whose midpoint interval holds it, ties to
  * the lower code.  A block whose new absmax is below 2^-126 stores the zero
  * code everywhere (the absmax itself is stored as computed).
+ *
+ * Stochastic state rounding (state_round = 1, 8-bit state; the pages suggest
+ * stochastic rounding of the momenta, "[Feat]: Stochastic rounding of AdamW
+ * momentums", comment thread, and this carries it to the 8-bit codes): with
+ * n the normalised value, k = (number of entries <= n) - 1 clamped to
+ * [0, 254], W[k] = fp32(65536 / (C[k+1] - C[k])) (double arithmetic) and
+ * f = fp32(fp32(n - C[k]) * W[k]), the code is k + 1 if f > r and k
+ * otherwise, r being the element's 16 random bits on stream 1 (first moment)
+ * or 2 (second moment); a NaN n stores 255.
  */
 #ifndef OPT8_H_
 #define OPT8_H_
@@ -70,7 +79,7 @@ typedef enum {
   OPT8_E_NULL = -1,      /* a required pointer is NULL                               */
   OPT8_E_ALIGN = -2,     /* param/grad/m/v not 16-byte aligned, absmax not 4-byte    */
   OPT8_E_SIZE = -3,      /* n < 0, numel <= 0, bad index_base, size overflow         */
-  OPT8_E_MODE = -4,      /* unknown state mode or rounding mode                      */
+  OPT8_E_MODE = -4,      /* unknown state mode, rounding mode or state rounding      */
   OPT8_E_HPARAM = -5,    /* lr/betas/eps/weight_decay/step outside their ranges      */
   OPT8_E_ALIAS = -6,     /* two buffers of the list overlap                          */
   OPT8_E_DUPID = -7,     /* tensor_id repeated in one list                           */
@@ -88,6 +97,13 @@ typedef enum {
   OPT8_ROUND_STOCHASTIC = 0, /* parameter written with stochastic rounding          */
   OPT8_ROUND_NEAREST = 1     /* parameter written round-to-nearest-even             */
 } opt8_round_mode;
+
+typedef enum {
+  OPT8_STATE_ROUND_NEAREST = 0,    /* 8-bit state: nearest codebook entry (default) */
+  OPT8_STATE_ROUND_STOCHASTIC = 1  /* 8-bit state: one of the two entries around    */
+                                   /*   the value, the upper one with probability   */
+                                   /*   (n - C[k]) / (C[k+1] - C[k])                */
+} opt8_state_round;
 
 /* One tensor of the list.  All pointers are DEVICE pointers on the current
  * HIP device, owned by the caller, and must stay valid until the work queued
@@ -115,7 +131,8 @@ typedef struct opt8_hparams {
   int64_t step;           /* 1-based step count t of this update, >= 1                 */
   uint64_t seed;          /* Philox key                                                */
   int32_t param_round;    /* opt8_round_mode                                           */
-  int32_t reserved;       /* must be 0                                                 */
+  int32_t state_round;    /* opt8_state_round (8-bit state only; 0 keeps the nearest   */
+                          /*   entry)                                                  */
 } opt8_hparams;
 
 /* Build the two 256-entry codebooks (and their 255 midpoints) on the host and

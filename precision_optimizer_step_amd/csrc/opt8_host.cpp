@@ -74,7 +74,7 @@ void tree_levels(int magnitude_bits, bool negative_too, std::vector<float>& out)
 }
 
 struct Tables {
-  alignas(16) uint8_t bytes[kTableBytes];
+  alignas(16) uint8_t bytes[kTableBytesSR];
   const float* cb_s() const { return reinterpret_cast<const float*>(bytes + kOffCbS); }
   const float* cb_u() const { return reinterpret_cast<const float*>(bytes + kOffCbU); }
   bool ok = false;
@@ -121,6 +121,51 @@ bool build_luts(uint8_t* bytes) {
   return true;
 }
 
+// #{k : table[k] <= x} over the 256 entries.
+int count_at_or_below(const float* table, float x) {
+  int c = 0;
+  while (c < kCodes && table[c] <= x) ++c;
+  return c;
+}
+
+// Floor LUT entry: the largest entry at or below the bucket's smallest value
+// (0 when the bucket starts below the table); false if a bucket holds two entries.
+bool floor_entry(const float* table, float least, float most, uint8_t& out) {
+  const int base = std::max(count_at_or_below(table, least) - 1, 0);
+  const int top = std::max(count_at_or_below(table, most) - 1, 0);
+  out = static_cast<uint8_t>(base);
+  return top - base <= 1;
+}
+
+// The stochastic-state half of the image: floor LUTs and (entry, gap weight) pairs.
+bool build_sr_tables(uint8_t* bytes) {
+  const float* cb_s = reinterpret_cast<const float*>(bytes + kOffCbS);
+  const float* cb_u = reinterpret_cast<const float*>(bytes + kOffCbU);
+  for (uint32_t key = 0; key < kKeySPosEnd; ++key)
+    if (!floor_entry(cb_s, bits_f32(key << 17), bits_f32((key << 17) | 0x1FFFFu), bytes[kOffFloor + key]))
+      return false;
+  for (uint32_t key = kKeySNeg; key < kKeySNegEnd; ++key)
+    if (!floor_entry(cb_s, bits_f32((key << 17) | 0x1FFFFu), bits_f32(key << 17), bytes[kOffFloor + key]))
+      return false;
+  for (uint32_t key = kKeyLo; key <= kKeyHi; ++key) {
+    const float least = key == kKeyLo ? 0.0f : bits_f32(key << 16);
+    if (!floor_entry(cb_u, least, bits_f32((key << 16) | 0xFFFFu), bytes[kOffFloor + key])) return false;
+  }
+  auto pairs = [&](const float* table, int off) {
+    float pr[2 * kCodes];
+    for (int k = 0; k < kCodes; ++k) {
+      pr[2 * k] = table[k];
+      pr[2 * k + 1] = k + 1 < kCodes
+          ? static_cast<float>(65536.0 / (static_cast<double>(table[k + 1]) - static_cast<double>(table[k])))
+          : 0.0f;
+    }
+    std::memcpy(bytes + off, pr, sizeof pr);
+  };
+  pairs(cb_s, kOffPairS);
+  pairs(cb_u, kOffPairU);
+  return true;
+}
+
 Tables build_tables() {
   std::vector<float> s, u;
   tree_levels(7, true, s);
@@ -143,7 +188,7 @@ Tables build_tables() {
   };
   fill(s, kOffCbS, kOffMidS);
   fill(u, kOffCbU, kOffMidU);
-  t.ok = s.size() == kCodes && u.size() == kCodes && build_luts(t.bytes);
+  t.ok = s.size() == kCodes && u.size() == kCodes && build_luts(t.bytes) && build_sr_tables(t.bytes);
   return t;
 }
 
@@ -194,6 +239,7 @@ StepScalars make_scalars(const opt8_hparams& hp, int algo, PowCache& cache) {
   s.seed_hi = static_cast<uint32_t>(hp.seed >> 32);
   s.step_lo = static_cast<uint32_t>(hp.step);
   s.param_round = hp.param_round;
+  s.state_round = hp.state_round;
   return s;
 }
 
@@ -210,7 +256,8 @@ int validate_hparams(const opt8_hparams& hp, int algo) {
   if (!(std::isfinite(hp.weight_decay) && hp.weight_decay >= 0))
     return fail(OPT8_E_HPARAM, "weight_decay must be finite and >= 0 (got %g)", hp.weight_decay);
   if (hp.step < 1) return fail(OPT8_E_HPARAM, "step is 1-based (got %lld)", static_cast<long long>(hp.step));
-  if (hp.reserved != 0) return fail(OPT8_E_HPARAM, "reserved field must be 0");
+  if (hp.state_round != OPT8_STATE_ROUND_NEAREST && hp.state_round != OPT8_STATE_ROUND_STOCHASTIC)
+    return fail(OPT8_E_MODE, "unknown state_round %d", hp.state_round);
   if (hp.param_round != OPT8_ROUND_STOCHASTIC && hp.param_round != OPT8_ROUND_NEAREST)
     return fail(OPT8_E_MODE, "unknown param_round %d", hp.param_round);
   return OPT8_OK;
@@ -297,7 +344,7 @@ struct Slot {
 struct DeviceState {
   bool init = false;
   int num_cu = 0;
-  int occ[kAlgos][kKinds] = {};
+  int occ[2][kAlgos][kKinds] = {};   // [state_round][algo][kind]
   Slot slots[kSlots];
   uint64_t clock = 0;
   PowCache pow;
@@ -397,8 +444,9 @@ extern "C" int opt8_init_codebooks(float* signed_out, float* unsigned_out) {
   if (e != hipSuccess) return hip_fail(e, "upload of codebooks");
   e = hipDeviceGetAttribute(&ds.num_cu, hipDeviceAttributeMultiprocessorCount, dev);
   if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute(CU count)");
-  for (int a = 0; a < kAlgos; ++a)
-    for (int k = 0; k < kKinds; ++k) ds.occ[a][k] = occupancy_per_cu(static_cast<Kind>(k), a);
+  for (int sr = 0; sr < 2; ++sr)
+    for (int a = 0; a < kAlgos; ++a)
+      for (int k = 0; k < kKinds; ++k) ds.occ[sr][a][k] = occupancy_per_cu(static_cast<Kind>(k), a, sr != 0);
   for (Slot& s : ds.slots) {
     if (!s.done) {
       e = hipEventCreateWithFlags(&s.done, hipEventDisableTiming);
@@ -482,7 +530,7 @@ int run_step(int algo, const opt8_tensor* tensors, int32_t n, const opt8_hparams
   const StepScalars sc = make_scalars(*hp, algo, ds.pow);
   for (int kind = 0; kind < kKinds; ++kind) {
     if (!count[kind]) continue;
-    const int cap = ds.num_cu * ds.occ[algo][kind];
+    const int cap = ds.num_cu * ds.occ[sc.state_round != 0][algo][kind];
     const hipError_t e = launch_step(static_cast<Kind>(kind), algo, slot->dev + first[kind], count[kind],
                                      blocks[kind], sc, stream, cap);
     if (e != hipSuccess) return hip_fail(e, "kernel launch");

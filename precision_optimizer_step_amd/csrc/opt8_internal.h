@@ -33,6 +33,7 @@ struct StepScalars {
   float beta1, beta2, w1, w2, eps, step_size, rbc2, lrwd, lr;
   uint32_t seed_lo, seed_hi, step_lo;
   int32_t param_round;   // 0 stochastic, 1 nearest-even
+  int32_t state_round;   // 8-bit state: 0 nearest entry, 1 stochastic between neighbours
 };
 
 // Update rules sharing the state machinery.
@@ -65,13 +66,32 @@ static_assert(kKeyLo == 0x3200u && kOffMidU + 1024 <= static_cast<int>(kKeyLo),
               "the unsigned LUT sits at its own keys, after the codebooks");
 static_assert(kOffCbS >= static_cast<int>(kKeySPosEnd) && kKeyHi < kKeySNeg, "LUT regions overlap");
 
+// Second half, staged only by the kernels that round the 8-bit state
+// stochastically (the same keys, shifted by kOffFloor):
+//   [0x6000, 0x8000)  signed floor LUT for 0 <= n < 2 at kOffFloor + (bits(n) >> 17)
+//   [0x8000, 0x8800)  signed pairs (C[k], W[k]), k = 0..255, fp32 each
+//   [0x8800, 0x9000)  unsigned pairs
+//   [0x9200, 0xA000)  unsigned floor LUT at kOffFloor + max(bits(n) >> 16, kKeyLo)
+//   [0xA000, 0xC000)  signed floor LUT for -2 < n <= -0 at kOffFloor + (bits(n) >> 17)
+// A floor entry is the index of the largest codebook entry at or below the
+// bucket's smallest value (0 below the table); no bucket holds more than one
+// entry (checked), so the entry at or below n is floor + (C[floor + 1] <= n).
+// W[k] = 65536 / (C[k+1] - C[k]) in double rounded once to fp32 (W[255] = 0).
+constexpr int kOffFloor = 0x6000;
+constexpr int kOffPairS = 0x8000, kOffPairU = 0x8800;
+constexpr int kTableBytesSR = 0xC000;
+static_assert(kOffPairU + 2048 <= kOffFloor + static_cast<int>(kKeyLo) &&
+              kOffFloor + static_cast<int>(kKeyHi) < kOffFloor + static_cast<int>(kKeySNeg),
+              "floor LUT regions overlap the pairs");
+
 enum class Kind : int { k8bit = 0, kBf16 = 1, kFp32 = 2, k8bitTail = 3 };
 
 // Kernel side (opt8_kernels.hip).
-hipError_t upload_tables(const uint8_t* host_tables);   // kTableBytes, to the current device
+hipError_t upload_tables(const uint8_t* host_tables);   // kTableBytesSR, to the current device
+// The 8-bit kinds take the stochastic-state kernels when sc.state_round is set.
 hipError_t launch_step(Kind kind, int algo, const DevTensor* dev_list, int ntensors,
                        int64_t total_blocks, const StepScalars& sc, hipStream_t stream, int grid_cap);
-// Workgroups per CU that the kernel of this kind and algorithm can keep resident.
-int occupancy_per_cu(Kind kind, int algo);
+// Workgroups per CU that the kernel of this kind, algorithm and state rounding can keep resident.
+int occupancy_per_cu(Kind kind, int algo, bool state_sr);
 
 }  // namespace opt8

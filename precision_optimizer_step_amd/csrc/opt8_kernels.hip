@@ -29,7 +29,7 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kGroups = kBlock / (64 * 8);  // 8-element groups per lane per block (4)
 constexpr float kMinNormal = 1.17549435e-38f;  // 2^-126
 
-__device__ uint4 g_tables[kTableBytes / 16];
+__device__ uint4 g_tables[kTableBytesSR / 16];
 
 // Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11): two 32x32->64 products per
 // round, the words permuted and xored with the round key, key bumped by the
@@ -75,6 +75,46 @@ __device__ __forceinline__ Rand4 group_bits(uint64_t grp, uint32_t stream, uint3
 
 __device__ __forceinline__ uint32_t r16_of(const Rand4& r, int j) {
   return (r.w[j >> 1] >> (16 * (j & 1))) & 0xFFFFu;
+}
+
+// Philox for N counters at once (four 8-element groups, or the streams of
+// one group), round by round, so each round key is computed once on the
+// scalar unit and used by all N.
+template <int N>
+__device__ __forceinline__ void philox10_n(uint32_t (&c0)[N], uint32_t (&c1)[N], uint32_t (&c2)[N],
+                                           uint32_t (&c3)[N], uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+#pragma unroll
+    for (int g = 0; g < N; ++g) {
+      const uint64_t p0 = static_cast<uint64_t>(kPhiloxM0) * c0[g];
+      const uint64_t p1 = static_cast<uint64_t>(kPhiloxM1) * c2[g];
+      const uint32_t n0 = __builtin_amdgcn_bitop3_b32(static_cast<uint32_t>(p1 >> 32), c1[g], k0, 0x96);
+      const uint32_t n2 = __builtin_amdgcn_bitop3_b32(static_cast<uint32_t>(p0 >> 32), c3[g], k1, 0x96);
+      c1[g] = static_cast<uint32_t>(p1);
+      c3[g] = static_cast<uint32_t>(p0);
+      c0[g] = n0;
+      c2[g] = n2;
+    }
+    k0 += kPhiloxW0;
+    k1 += kPhiloxW1;
+  }
+}
+
+// Random words of the first and second moment (streams 1 and 2) of group grp.
+__device__ __forceinline__ void state_bits(uint64_t grp, uint32_t tensor_id, const StepScalars& sc, Rand4& rm,
+                                           Rand4& rv) {
+  uint32_t c0[2], c1[2], c2[2], c3[2];
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    c0[s] = static_cast<uint32_t>(grp);
+    c1[s] = static_cast<uint32_t>(grp >> 32) | (static_cast<uint32_t>(s + 1) << 30);
+    c2[s] = sc.step_lo;
+    c3[s] = tensor_id;
+  }
+  philox10_n<2>(c0, c1, c2, c3, sc.seed_lo, sc.seed_hi);
+  rm = Rand4{{c0[0], c1[0], c2[0], c3[0]}};
+  rv = Rand4{{c0[1], c1[1], c2[1], c3[1]}};
 }
 
 // fp32 -> bf16 bits: stochastic (add 16 random bits below the kept half, then
@@ -180,6 +220,19 @@ __device__ __forceinline__ uint32_t code_search(float n, const float* mid) {
   return (n != n) ? 255u : idx;
 }
 
+// Stochastic state rounding, plain path: k = the entry at or below n (binary
+// search over the (entry, gap weight) pairs, clamped to [0, 254]), then the
+// upper entry iff fp32(fp32(n - C[k]) * W[k]) > r16; NaN stores 255.
+__device__ __forceinline__ uint32_t code_sr_search(float n, const float* pair, uint32_t r16) {
+  uint32_t pos = 0;   // #{k <= 254 : C[k] <= n}
+#pragma unroll
+  for (uint32_t s = 128; s >= 1; s >>= 1) pos += (pair[2 * (pos + s - 1)] <= n) ? s : 0u;
+  const uint32_t k = pos > 0 ? pos - 1 : 0u;
+  const float f = (n - pair[2 * k]) * pair[2 * k + 1];
+  const uint32_t code = k + ((f > static_cast<float>(r16)) ? 1u : 0u);
+  return (n != n) ? 255u : code;
+}
+
 __device__ __forceinline__ float wave_max(float x) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
@@ -196,7 +249,7 @@ __device__ __forceinline__ float wave_nan_max(float x) {
 // Every block whose values leave the fast path's range, every partial block,
 // and every non-finite case: IEEE operations, binary search over the
 // midpoints, NaN-propagating block max.
-template <bool kFull>
+template <bool kFull, bool kSS>
 __device__ __forceinline__ void block_8bit_plain(const DevTensor& d, int64_t blk, int lane, int valid,
                                               const StepScalars& sc, const uint8_t* lds) {
   const float* cb_s = reinterpret_cast<const float*>(lds + kOffCbS);
@@ -276,10 +329,20 @@ __device__ __forceinline__ void block_8bit_plain(const DevTensor& d, int64_t blk
   for (int r = 0; r < kGroups; ++r) {
     const int off = r * 512 + lane * 8;
     uint32_t cm[2] = {0, 0}, cv[2] = {0, 0};
+    Rand4 rm{{0, 0, 0, 0}}, rv{{0, 0, 0, 0}};
+    if constexpr (kSS) state_bits(grp0 + (off >> 3), d.tensor_id, sc, rm, rv);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const uint32_t qm = live_m ? code_search(M2[r * 8 + j] * inv_m, mid_s) : 127u;
-      const uint32_t qv = live_v ? code_search(V2[r * 8 + j] * inv_v, mid_u) : 0u;
+      const float nm = M2[r * 8 + j] * inv_m;
+      const float nv = V2[r * 8 + j] * inv_v;
+      uint32_t qm, qv;
+      if constexpr (kSS) {
+        qm = live_m ? code_sr_search(nm, reinterpret_cast<const float*>(lds + kOffPairS), r16_of(rm, j)) : 127u;
+        qv = live_v ? code_sr_search(nv, reinterpret_cast<const float*>(lds + kOffPairU), r16_of(rv, j)) : 0u;
+      } else {
+        qm = live_m ? code_search(nm, mid_s) : 127u;
+        qv = live_v ? code_search(nv, mid_u) : 0u;
+      }
       cm[j >> 2] |= qm << (8 * (j & 3));
       cv[j >> 2] |= qv << (8 * (j & 3));
     }
@@ -315,31 +378,22 @@ __device__ __forceinline__ uint32_t code_s(float n, const uint8_t* lds, const fl
   return c + ((mid[c] < n) ? 1u : 0u);
 }
 
-// Philox for four 8-element groups at once, round by round, so each round key
-// is computed once on the scalar unit and used by all four.
-__device__ __forceinline__ void philox10_x4(uint32_t (&c0)[4], uint32_t (&c1)[4], uint32_t (&c2)[4],
-                                            uint32_t (&c3)[4], uint32_t k0, uint32_t k1) {
-#pragma unroll
-  for (int r = 0; r < 10; ++r) {
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const uint64_t p0 = static_cast<uint64_t>(kPhiloxM0) * c0[g];
-      const uint64_t p1 = static_cast<uint64_t>(kPhiloxM1) * c2[g];
-      const uint32_t n0 = __builtin_amdgcn_bitop3_b32(static_cast<uint32_t>(p1 >> 32), c1[g], k0, 0x96);
-      const uint32_t n2 = __builtin_amdgcn_bitop3_b32(static_cast<uint32_t>(p0 >> 32), c3[g], k1, 0x96);
-      c1[g] = static_cast<uint32_t>(p1);
-      c3[g] = static_cast<uint32_t>(p0);
-      c0[g] = n0;
-      c2[g] = n2;
-    }
-    k0 += kPhiloxW0;
-    k1 += kPhiloxW1;
-  }
+// Stochastic state rounding through the floor LUTs (finite -2 < n < 2): the
+// entry at or below n is floor + (C[floor + 1] <= n), clamped to 254.
+template <bool kSigned>
+__device__ __forceinline__ uint32_t code_sr(float n, const uint8_t* lds, uint32_t r16) {
+  const uint32_t b = __float_as_uint(n);
+  const uint32_t key = kSigned ? (b >> 17) : max(b >> 16, kKeyLo);
+  const float* pair = reinterpret_cast<const float*>(lds + (kSigned ? kOffPairS : kOffPairU));
+  const uint32_t c = lds[kOffFloor + key];
+  const uint32_t k = min(c + ((pair[2 * c + 2] <= n) ? 1u : 0u), 254u);
+  const float f = (n - pair[2 * k]) * pair[2 * k + 1];
+  return k + ((f > static_cast<float>(r16)) ? 1u : 0u);
 }
 
 // A full block; returns false (having written nothing) when the block must
 // take the plain path instead.
-template <bool kNearest>
+template <bool kNearest, bool kSS>
 __device__ __forceinline__ bool block_8bit_fast(const DevTensor& d, int64_t blk, int lane,
                                                 const StepScalars& sc, const uint8_t* lds, bool range_ok) {
   const int64_t e0 = blk * kBlock;
@@ -415,7 +469,7 @@ __device__ __forceinline__ bool block_8bit_fast(const DevTensor& d, int64_t blk,
       c2[r] = sc.step_lo;
       c3[r] = d.tensor_id;
     }
-    philox10_x4(c0, c1, c2, c3, sc.seed_lo, sc.seed_hi);
+    philox10_n<4>(c0, c1, c2, c3, sc.seed_lo, sc.seed_hi);
   }
   uint64_t nan_lanes = 0;
 #pragma unroll
@@ -454,10 +508,20 @@ __device__ __forceinline__ bool block_8bit_fast(const DevTensor& d, int64_t blk,
   for (int r = 0; r < kGroups; ++r) {
     const int off = r * 512 + lane * 8;
     uint32_t cm[2] = {0, 0}, cv[2] = {0, 0};
+    Rand4 rm{{0, 0, 0, 0}}, rv{{0, 0, 0, 0}};
+    if constexpr (kSS)
+      state_bits((static_cast<uint64_t>(d.index_base + e0) >> 3) + static_cast<uint64_t>(lane + r * 64),
+                 d.tensor_id, sc, rm, rv);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const uint32_t qm = code_s(M2[r * 8 + j] * inv_m, lds, mid_s);
-      const uint32_t qv = code_u(V2[r * 8 + j] * inv_v, lds, mid_u);
+      uint32_t qm, qv;
+      if constexpr (kSS) {
+        qm = code_sr<true>(M2[r * 8 + j] * inv_m, lds, r16_of(rm, j));
+        qv = code_sr<false>(V2[r * 8 + j] * inv_v, lds, r16_of(rv, j));
+      } else {
+        qm = code_s(M2[r * 8 + j] * inv_m, lds, mid_s);
+        qv = code_u(V2[r * 8 + j] * inv_v, lds, mid_u);
+      }
       cm[j >> 2] |= qm << (8 * (j & 3));
       cv[j >> 2] |= qv << (8 * (j & 3));
     }
@@ -491,28 +555,6 @@ __device__ __forceinline__ void group_bf16_plain(const uint4& G, const uint4& P,
     po[j >> 1] |= to_bf16(pn, r16_of(rp, j), nearest) << s;
     mo[j >> 1] |= to_bf16(m2, r16_of(rm, j), false) << s;
     vo[j >> 1] |= to_bf16(v2, r16_of(rv, j), false) << s;
-  }
-}
-
-// Philox for the three streams (param, m, v) of one 8-element group, round by
-// round so each round key is computed once.
-__device__ __forceinline__ void philox10_x3(uint32_t (&c0)[3], uint32_t (&c1)[3], uint32_t (&c2)[3],
-                                            uint32_t (&c3)[3], uint32_t k0, uint32_t k1) {
-#pragma unroll
-  for (int r = 0; r < 10; ++r) {
-#pragma unroll
-    for (int g = 0; g < 3; ++g) {
-      const uint64_t p0 = static_cast<uint64_t>(kPhiloxM0) * c0[g];
-      const uint64_t p1 = static_cast<uint64_t>(kPhiloxM1) * c2[g];
-      const uint32_t n0 = __builtin_amdgcn_bitop3_b32(static_cast<uint32_t>(p1 >> 32), c1[g], k0, 0x96);
-      const uint32_t n2 = __builtin_amdgcn_bitop3_b32(static_cast<uint32_t>(p0 >> 32), c3[g], k1, 0x96);
-      c1[g] = static_cast<uint32_t>(p1);
-      c3[g] = static_cast<uint32_t>(p0);
-      c0[g] = n0;
-      c2[g] = n2;
-    }
-    k0 += kPhiloxW0;
-    k1 += kPhiloxW1;
   }
 }
 
@@ -550,7 +592,7 @@ __device__ __forceinline__ void block_bf16_full(const DevTensor& d, int64_t blk,
       c2[s] = sc.step_lo;
       c3[s] = d.tensor_id;
     }
-    philox10_x3(c0, c1, c2, c3, sc.seed_lo, sc.seed_hi);
+    philox10_n<3>(c0, c1, c2, c3, sc.seed_lo, sc.seed_hi);
     const Rand4 rp{{c0[0], c1[0], c2[0], c3[0]}};
     const Rand4 rm{{c0[1], c1[1], c2[1], c3[1]}};
     const Rand4 rv{{c0[2], c1[2], c2[2], c3[2]}};
@@ -729,7 +771,7 @@ __device__ __forceinline__ float update1(float p, float g, float m1, const StepS
 
 // 8-bit state, plain path: partial blocks and any block with a NaN result or a
 // non-finite moment.
-template <int A, bool kFull>
+template <int A, bool kFull, bool kSS>
 __device__ __forceinline__ void block_1s_8bit_plain(const DevTensor& d, int64_t blk, int lane, int valid,
                                                     const StepScalars& sc, const uint8_t* lds) {
   const float* cb_s = reinterpret_cast<const float*>(lds + kOffCbS);
@@ -793,9 +835,16 @@ __device__ __forceinline__ void block_1s_8bit_plain(const DevTensor& d, int64_t 
   for (int r = 0; r < kGroups; ++r) {
     const int off = r * 512 + lane * 8;
     uint32_t cm[2] = {0, 0};
+    Rand4 rm{{0, 0, 0, 0}};
+    if constexpr (kSS) rm = group_bits(grp0 + (off >> 3), 1u, d.tensor_id, sc);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const uint32_t q = live ? code_search(M2[r * 8 + j] * inv, mid_s) : 127u;
+      const float nm = M2[r * 8 + j] * inv;
+      uint32_t q;
+      if constexpr (kSS)
+        q = live ? code_sr_search(nm, reinterpret_cast<const float*>(lds + kOffPairS), r16_of(rm, j)) : 127u;
+      else
+        q = live ? code_search(nm, mid_s) : 127u;
       cm[j >> 2] |= q << (8 * (j & 3));
     }
     if (kFull) {
@@ -812,7 +861,7 @@ __device__ __forceinline__ void block_1s_8bit_plain(const DevTensor& d, int64_t 
 // 8-bit state, full block: LUT requantisation and the plain add-and-truncate
 // rounding; returns false (nothing written) on a NaN parameter or moment, or
 // an infinite block maximum.
-template <int A, bool kNearest>
+template <int A, bool kNearest, bool kSS>
 __device__ __forceinline__ bool block_1s_8bit_fast(const DevTensor& d, int64_t blk, int lane,
                                                    const StepScalars& sc, const uint8_t* lds) {
   const float* cb_s = reinterpret_cast<const float*>(lds + kOffCbS);
@@ -842,7 +891,7 @@ __device__ __forceinline__ bool block_1s_8bit_fast(const DevTensor& d, int64_t b
       c2[r] = sc.step_lo;
       c3[r] = d.tensor_id;
     }
-    philox10_x4(c0, c1, c2, c3, sc.seed_lo, sc.seed_hi);
+    philox10_n<4>(c0, c1, c2, c3, sc.seed_lo, sc.seed_hi);
   }
   float M2[kGroups * 8];
   float mxm = 0.0f;
@@ -877,8 +926,15 @@ __device__ __forceinline__ bool block_1s_8bit_fast(const DevTensor& d, int64_t b
 #pragma unroll
   for (int r = 0; r < kGroups; ++r) {
     uint32_t cm[2] = {0, 0};
+    if constexpr (kSS) {
+      const Rand4 rm = group_bits((static_cast<uint64_t>(d.index_base + e0) >> 3) +
+                                      static_cast<uint64_t>(lane + r * 64), 1u, d.tensor_id, sc);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) cm[j >> 2] |= code_s(M2[r * 8 + j] * inv, lds, mid_s) << (8 * (j & 3));
+      for (int j = 0; j < 8; ++j) cm[j >> 2] |= code_sr<true>(M2[r * 8 + j] * inv, lds, r16_of(rm, j)) << (8 * (j & 3));
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) cm[j >> 2] |= code_s(M2[r * 8 + j] * inv, lds, mid_s) << (8 * (j & 3));
+    }
     if (!live) cm[0] = cm[1] = 0x7F7F7F7Fu;
     st_stream8(mp + r * 512 + lane * 8, make_uint2(cm[0], cm[1]));
   }
@@ -930,19 +986,23 @@ __device__ __forceinline__ void block_1s_wide(const DevTensor& d, int64_t blk, i
 }
 
 // ----------------------------------------------------------------------------- driver
+template <int kBytes>
 __device__ __forceinline__ void stage_tables(uint8_t* lds) {
   uint4* dst = reinterpret_cast<uint4*>(lds);
-  for (int i = threadIdx.x; i < kTableBytes / 16; i += kThreads) dst[i] = g_tables[i];
+  for (int i = threadIdx.x; i < kBytes / 16; i += kThreads) dst[i] = g_tables[i];
   __syncthreads();
 }
 
-template <Kind K, int A>
+// SS: the 8-bit state is rounded stochastically between neighbouring entries
+// (only the 8-bit kinds are instantiated with it).
+template <Kind K, int A, bool SS>
 __global__ void __launch_bounds__(kThreads)
 step_kernel(const DevTensor* __restrict__ list, int ntensors, int64_t total_blocks, StepScalars sc,
             int range_ok) {
   constexpr bool kQ8 = (K == Kind::k8bit || K == Kind::k8bitTail);
-  __shared__ __attribute__((aligned(16))) uint8_t lds[kQ8 ? kTableBytes : 16];
-  if constexpr (kQ8) stage_tables(lds);
+  constexpr int kLds = kQ8 ? (SS ? kTableBytesSR : kTableBytes) : 16;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kLds];
+  if constexpr (kQ8) stage_tables<kLds>(lds);
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
   const int64_t gw = static_cast<int64_t>(blockIdx.x) * kWaves + wave;
@@ -964,12 +1024,12 @@ step_kernel(const DevTensor* __restrict__ list, int ntensors, int64_t total_bloc
     const int64_t blk = b - d.block_begin;
     if constexpr (A != kAdamW) {
       if constexpr (K == Kind::k8bit) {
-        const bool done = sc.param_round ? block_1s_8bit_fast<A, true>(d, blk, lane, sc, lds)
-                                         : block_1s_8bit_fast<A, false>(d, blk, lane, sc, lds);
-        if (!done) block_1s_8bit_plain<A, true>(d, blk, lane, kBlock, sc, lds);
+        const bool done = sc.param_round ? block_1s_8bit_fast<A, true, SS>(d, blk, lane, sc, lds)
+                                         : block_1s_8bit_fast<A, false, SS>(d, blk, lane, sc, lds);
+        if (!done) block_1s_8bit_plain<A, true, SS>(d, blk, lane, kBlock, sc, lds);
       } else if constexpr (K == Kind::k8bitTail) {
         const int64_t tail = (d.numel - 1) / kBlock;
-        block_1s_8bit_plain<A, false>(d, tail, lane, static_cast<int>(d.numel - tail * kBlock), sc, lds);
+        block_1s_8bit_plain<A, false, SS>(d, tail, lane, static_cast<int>(d.numel - tail * kBlock), sc, lds);
       } else {
         const int64_t left = d.numel - blk * kBlock;
         const int valid = left >= kBlock ? kBlock : static_cast<int>(left);
@@ -977,13 +1037,13 @@ step_kernel(const DevTensor* __restrict__ list, int ntensors, int64_t total_bloc
       }
     } else if constexpr (K == Kind::k8bit) {
       // this list holds the full blocks of 8-bit tensors only
-      const bool done = sc.param_round ? block_8bit_fast<true>(d, blk, lane, sc, lds, range_ok != 0)
-                                       : block_8bit_fast<false>(d, blk, lane, sc, lds, range_ok != 0);
-      if (!done) block_8bit_plain<true>(d, blk, lane, kBlock, sc, lds);
+      const bool done = sc.param_round ? block_8bit_fast<true, SS>(d, blk, lane, sc, lds, range_ok != 0)
+                                       : block_8bit_fast<false, SS>(d, blk, lane, sc, lds, range_ok != 0);
+      if (!done) block_8bit_plain<true, SS>(d, blk, lane, kBlock, sc, lds);
     } else if constexpr (K == Kind::k8bitTail) {
       // this list holds the last, partial block of 8-bit tensors (one per entry)
       const int64_t tail = (d.numel - 1) / kBlock;
-      block_8bit_plain<false>(d, tail, lane, static_cast<int>(d.numel - tail * kBlock), sc, lds);
+      block_8bit_plain<false, SS>(d, tail, lane, static_cast<int>(d.numel - tail * kBlock), sc, lds);
     } else {
       const int64_t left = d.numel - blk * kBlock;
       const bool full = left >= kBlock;
@@ -1000,42 +1060,44 @@ step_kernel(const DevTensor* __restrict__ list, int ntensors, int64_t total_bloc
   }
 }
 
-template <Kind K, int A>
+template <Kind K, int A, bool SS>
 hipError_t launch_kind(const DevTensor* list, int n, int64_t total_blocks, const StepScalars& sc,
                        hipStream_t stream, int grid_cap, int range_ok) {
   int64_t grid = (total_blocks + kWaves - 1) / kWaves;
   if (grid_cap > 0 && grid > grid_cap) grid = grid_cap;
   if (grid < 1) grid = 1;
-  hipLaunchKernelGGL((step_kernel<K, A>), dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0, stream,
+  hipLaunchKernelGGL((step_kernel<K, A, SS>), dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0, stream,
                      list, n, total_blocks, sc, range_ok);
   return hipGetLastError();
 }
 
-template <Kind K, int A>
+template <Kind K, int A, bool SS>
 int occupancy_kind() {
   int n = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, step_kernel<K, A>, kThreads, 0) != hipSuccess)
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, step_kernel<K, A, SS>, kThreads, 0) != hipSuccess)
     return 1;
   return n > 0 ? n : 1;
 }
 
-template <Kind K>
+// Kernel of (kind, algorithm, state rounding): the bf16 and fp32 kinds have
+// no 8-bit state and always take SS = false.
+template <Kind K, bool SS>
 hipError_t launch_algo(int algo, const DevTensor* list, int n, int64_t total_blocks, const StepScalars& sc,
                        hipStream_t stream, int grid_cap, int range_ok) {
   switch (algo) {
-    case kAdamW: return launch_kind<K, kAdamW>(list, n, total_blocks, sc, stream, grid_cap, range_ok);
-    case kLion: return launch_kind<K, kLion>(list, n, total_blocks, sc, stream, grid_cap, range_ok);
-    case kMomentum: return launch_kind<K, kMomentum>(list, n, total_blocks, sc, stream, grid_cap, range_ok);
+    case kAdamW: return launch_kind<K, kAdamW, SS>(list, n, total_blocks, sc, stream, grid_cap, range_ok);
+    case kLion: return launch_kind<K, kLion, SS>(list, n, total_blocks, sc, stream, grid_cap, range_ok);
+    case kMomentum: return launch_kind<K, kMomentum, SS>(list, n, total_blocks, sc, stream, grid_cap, range_ok);
   }
   return hipErrorInvalidValue;
 }
 
-template <Kind K>
+template <Kind K, bool SS>
 int occupancy_algo(int algo) {
   switch (algo) {
-    case kAdamW: return occupancy_kind<K, kAdamW>();
-    case kLion: return occupancy_kind<K, kLion>();
-    case kMomentum: return occupancy_kind<K, kMomentum>();
+    case kAdamW: return occupancy_kind<K, kAdamW, SS>();
+    case kLion: return occupancy_kind<K, kLion, SS>();
+    case kMomentum: return occupancy_kind<K, kMomentum, SS>();
   }
   return 1;
 }
@@ -1043,7 +1105,7 @@ int occupancy_algo(int algo) {
 }  // namespace
 
 hipError_t upload_tables(const uint8_t* host_tables) {
-  return hipMemcpyToSymbol(HIP_SYMBOL(g_tables), host_tables, kTableBytes, 0, hipMemcpyHostToDevice);
+  return hipMemcpyToSymbol(HIP_SYMBOL(g_tables), host_tables, kTableBytesSR, 0, hipMemcpyHostToDevice);
 }
 
 hipError_t launch_step(Kind kind, int algo, const DevTensor* list, int n, int64_t total_blocks,
@@ -1052,22 +1114,30 @@ hipError_t launch_step(Kind kind, int algo, const DevTensor* list, int n, int64_
   // the fast AdamW paths need eps well inside the normal range and a bounded
   // second-moment correction (they then check each block's own values)
   const int range_ok = (sc.eps >= 0x1p-60f && sc.eps <= 0x1p+60f && sc.rbc2 <= 0x1p+20f) ? 1 : 0;
+  const bool ss = sc.state_round != 0;
   switch (kind) {
-    case Kind::k8bit: return launch_algo<Kind::k8bit>(algo, list, n, total_blocks, sc, stream, grid_cap, range_ok);
+    case Kind::k8bit:
+      return ss ? launch_algo<Kind::k8bit, true>(algo, list, n, total_blocks, sc, stream, grid_cap, range_ok)
+                : launch_algo<Kind::k8bit, false>(algo, list, n, total_blocks, sc, stream, grid_cap, range_ok);
     case Kind::k8bitTail:
-      return launch_algo<Kind::k8bitTail>(algo, list, n, total_blocks, sc, stream, grid_cap, range_ok);
-    case Kind::kBf16: return launch_algo<Kind::kBf16>(algo, list, n, total_blocks, sc, stream, grid_cap, range_ok);
-    case Kind::kFp32: return launch_algo<Kind::kFp32>(algo, list, n, total_blocks, sc, stream, grid_cap, range_ok);
+      return ss ? launch_algo<Kind::k8bitTail, true>(algo, list, n, total_blocks, sc, stream, grid_cap, range_ok)
+                : launch_algo<Kind::k8bitTail, false>(algo, list, n, total_blocks, sc, stream, grid_cap, range_ok);
+    case Kind::kBf16:
+      return launch_algo<Kind::kBf16, false>(algo, list, n, total_blocks, sc, stream, grid_cap, range_ok);
+    case Kind::kFp32:
+      return launch_algo<Kind::kFp32, false>(algo, list, n, total_blocks, sc, stream, grid_cap, range_ok);
   }
   return hipErrorInvalidValue;
 }
 
-int occupancy_per_cu(Kind kind, int algo) {
+int occupancy_per_cu(Kind kind, int algo, bool state_sr) {
   switch (kind) {
-    case Kind::k8bit: return occupancy_algo<Kind::k8bit>(algo);
-    case Kind::k8bitTail: return occupancy_algo<Kind::k8bitTail>(algo);
-    case Kind::kBf16: return occupancy_algo<Kind::kBf16>(algo);
-    case Kind::kFp32: return occupancy_algo<Kind::kFp32>(algo);
+    case Kind::k8bit:
+      return state_sr ? occupancy_algo<Kind::k8bit, true>(algo) : occupancy_algo<Kind::k8bit, false>(algo);
+    case Kind::k8bitTail:
+      return state_sr ? occupancy_algo<Kind::k8bitTail, true>(algo) : occupancy_algo<Kind::k8bitTail, false>(algo);
+    case Kind::kBf16: return occupancy_algo<Kind::kBf16, false>(algo);
+    case Kind::kFp32: return occupancy_algo<Kind::kFp32, false>(algo);
   }
   return 1;
 }

@@ -32,6 +32,8 @@ OPT8_STATE_FP32 = 2
 
 OPT8_ROUND_STOCHASTIC = 0
 OPT8_ROUND_NEAREST = 1
+OPT8_STATE_ROUND_NEAREST = 0
+OPT8_STATE_ROUND_STOCHASTIC = 1
 
 STATUS_NAMES = {0: "OPT8_OK", -1: "OPT8_E_NULL", -2: "OPT8_E_ALIGN", -3: "OPT8_E_SIZE",
                 -4: "OPT8_E_MODE", -5: "OPT8_E_HPARAM", -6: "OPT8_E_ALIAS", -7: "OPT8_E_DUPID",
@@ -63,7 +65,7 @@ class opt8_hparams(ctypes.Structure):
         ("step", ctypes.c_int64),
         ("seed", ctypes.c_uint64),
         ("param_round", ctypes.c_int32),
-        ("reserved", ctypes.c_int32),
+        ("state_round", ctypes.c_int32),
     ]
 
 
@@ -128,9 +130,9 @@ def opt8_default_mode(numel: int) -> int:
 
 
 def make_hparams(lr, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.0, step=1, seed=0,
-                 param_round=OPT8_ROUND_STOCHASTIC) -> opt8_hparams:
+                 param_round=OPT8_ROUND_STOCHASTIC, state_round=OPT8_STATE_ROUND_NEAREST) -> opt8_hparams:
     return opt8_hparams(float(lr), float(beta1), float(beta2), float(eps), float(weight_decay),
-                        int(step), int(seed) & 0xFFFFFFFFFFFFFFFF, int(param_round), 0)
+                        int(step), int(seed) & 0xFFFFFFFFFFFFFFFF, int(param_round), int(state_round))
 
 
 def _addr(x):

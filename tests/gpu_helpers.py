@@ -77,7 +77,7 @@ def gpu_step(sets, hp: "oracle.Hparams", algo=ALGO_ADAMW):
     descs = [s.desc() for s in sets]
     getattr(opt8, STEP_FN[algo])(descs, opt8.make_hparams(hp.lr, hp.beta1, hp.beta2, hp.eps,
                                                           hp.weight_decay, hp.step, hp.seed,
-                                                          hp.param_round))
+                                                          hp.param_round, hp.state_round))
     torch.cuda.synchronize()
 
 

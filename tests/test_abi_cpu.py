@@ -157,9 +157,8 @@ def test_hparam_errors(L, bad):
     kw = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.0, step=1)
     kw.update(bad)
     expect(step([fake_tensor(0)], hp=opt8.make_hparams(**kw)), opt8.OPT8_E_HPARAM)
-    hp = opt8.make_hparams(1e-3)
-    hp.reserved = 1
-    expect(step([fake_tensor(0)], hp=hp), opt8.OPT8_E_HPARAM, "reserved")
+    hp = opt8.make_hparams(1e-3, state_round=2)
+    expect(step([fake_tensor(0)], hp=hp), opt8.OPT8_E_MODE, "state_round")
 
 
 def test_alias_and_duplicate_id_errors(L):

@@ -13,7 +13,7 @@ import pytest
 import torch
 
 import oracle
-from gpu_helpers import build_list, compare_state, descriptors, log, sample_blocks, snapshot
+from gpu_helpers import BLOCK, build_list, compare_state, descriptors, log, sample_blocks, snapshot
 from precision_optimizer_step_amd import opt8
 from workloads import shapes
 
