@@ -111,3 +111,95 @@ def test_rne_without_ties_to_even_is_caught(monkeypatch):
         return (((b + np.uint32(0x8000)) & np.uint32(0xFFFF0000)) >> np.uint32(16)).astype(np.uint16)
     monkeypatch.setattr(TR, "f32_to_bf16_rne", no_even)
     _fails(TR.test_rne_matches_torch_conversion)
+
+
+# ----------------------------------------------------------------------------- one-state rules
+import oracle.state_sr as SS  # noqa: E402
+import test_oracle_onestate as TO  # noqa: E402
+import test_oracle_state_sr as TS  # noqa: E402
+
+
+def _lion_new_moment_direction(p, g, m1, s):
+    m2 = (s.beta2 * m1 + s.w2 * g).astype(np.float32)
+    c = (s.beta1 * m2 + s.w1 * g).astype(np.float32)
+    return m2, ((p - s.lrwd * p) - s.lr * np.sign(c).astype(np.float32)).astype(np.float32)
+
+
+def _lion_betas_swapped(p, g, m1, s):
+    c = (s.beta2 * m1 + s.w2 * g).astype(np.float32)
+    m2 = (s.beta1 * m1 + s.w1 * g).astype(np.float32)
+    return m2, ((p - s.lrwd * p) - s.lr * np.sign(c).astype(np.float32)).astype(np.float32)
+
+
+def _lion_sign_of_zero_is_one(p, g, m1, s):
+    c = (s.beta1 * m1 + s.w1 * g).astype(np.float32)
+    m2 = (s.beta2 * m1 + s.w2 * g).astype(np.float32)
+    sgn = np.where(c >= 0, 1, -1).astype(np.float32)
+    return m2, ((p - s.lrwd * p) - s.lr * sgn).astype(np.float32)
+
+
+@pytest.mark.parametrize("mutant,pin", [
+    (_lion_new_moment_direction, "test_lion_uses_the_old_moment_for_the_direction"),
+    (_lion_betas_swapped, "test_lion_uses_the_old_moment_for_the_direction"),
+    (_lion_sign_of_zero_is_one, "test_lion_step1_closed_form"),
+])
+def test_lion_mutants_are_caught(monkeypatch, mutant, pin):
+    monkeypatch.setattr(TO, "lion_update", mutant)
+    _fails(getattr(TO, pin))
+
+
+def _momentum_with_dampening(p, g, m1, s):
+    m2 = (s.beta1 * m1 + s.w1 * g).astype(np.float32)
+    return m2, ((p - s.lrwd * p) - s.lr * m2).astype(np.float32)
+
+
+def _momentum_coupled_decay(p, g, m1, s):
+    wd = np.float32(s.lrwd / s.lr) if s.lr else np.float32(0)
+    m2 = (s.beta1 * m1 + (g + wd * p)).astype(np.float32)
+    return m2, (p - s.lr * m2).astype(np.float32)
+
+
+def test_momentum_mutants_are_caught(monkeypatch):
+    monkeypatch.setattr(TO, "momentum_update", _momentum_with_dampening)
+    _fails(TO.test_momentum_matches_torch_sgd, 0.0)
+    monkeypatch.setattr(TO, "momentum_update", _momentum_coupled_decay)
+    _fails(TO.test_momentum_decoupled_decay_and_zero_gradient)
+
+
+# ----------------------------------------------------------------------------- state rounding
+def _sr_codes_variant(flip=False, ge=False, gap_below=False):
+    def codes(n, table, weights, r16):
+        n = np.asarray(n, dtype=np.float32)
+        count = np.searchsorted(table, n, side="right")
+        k = np.clip(count.astype(np.int64) - 1, 0, table.size - 2)
+        w = weights
+        if gap_below:   # gap weight of the gap below C[k] instead of above
+            w = np.concatenate([[weights[0]], weights[:-1]]).astype(np.float32)
+        f = ((n - table[k]).astype(np.float32) * w[k]).astype(np.float32)
+        r = np.asarray(r16, dtype=np.uint32).astype(np.float32)
+        up = (f >= r) if ge else (f > r)
+        if flip:
+            up = ~up
+        code = k + up.astype(np.int64)
+        return np.where(np.isnan(n), table.size - 1, code).astype(np.uint8)
+    return codes
+
+
+@pytest.mark.parametrize("kw,pin", [
+    (dict(flip=True), "test_mean_over_all_random_words_is_the_value"),
+    (dict(ge=True), "test_codes_are_the_two_neighbours_and_entries_stay"),
+    (dict(gap_below=True), "test_mean_over_all_random_words_is_the_value"),
+])
+def test_state_rounding_mutants_are_caught(monkeypatch, kw, pin):
+    monkeypatch.setattr(TS, "sr_codes", _sr_codes_variant(**kw))
+    _fails(getattr(TS, pin), "signed")
+
+
+def test_state_rounding_that_ignores_the_draw_is_caught(monkeypatch):
+    """Nearest rounding in place of the stochastic choice: the decay pin fails."""
+    real = SS.quantize_blockwise_sr
+
+    def nearest(x, table, zero_code, r16):
+        return real(x, table, zero_code, np.full(np.asarray(r16).shape, 32768, np.uint32))
+    monkeypatch.setattr(SS, "quantize_blockwise_sr", nearest)
+    _fails(TS.test_decaying_second_moment_is_frozen_by_nearest_and_followed_by_stochastic)

@@ -66,15 +66,18 @@ def test_lion_step1_closed_form():
 
 
 def test_lion_uses_the_old_moment_for_the_direction():
-    """Step 2 with m1 and g of opposite sign: c and m2 can have different signs."""
+    """Step 2 with m1 and g of opposite sign: c and m2 can have different signs, and a
+    direction formed from the NEW moment would flip the last pair."""
     s = host_scalars_1state(Hparams(lr=1e-3, beta1=0.9, beta2=0.99, step=2))
-    p = np.zeros(2, np.float32)
-    m1 = np.array([1.0, -1.0], np.float32)
-    g = np.array([-20.0, 20.0], np.float32)
-    # c = 0.9 m1 + 0.1 g = (-1.1, 1.1): sign from the gradient side; m2 = 0.99 m1 + 0.01 g keeps m1's sign
+    p = np.zeros(4, np.float32)
+    m1 = np.array([1.0, -1.0, 1.0, -1.0], np.float32)
+    g = np.array([-20.0, 20.0, -8.5, 8.5], np.float32)
+    # c = 0.9 m1 + 0.1 g = (-1.1, 1.1, 0.05, -0.05); m2 = 0.99 m1 + 0.01 g keeps m1's sign;
+    # 0.9 m2 + 0.1 g would be (.., .., -0.0355, 0.0355)
     m2, pn = lion_update(p, g, m1, s)
     assert np.array_equal(np.sign(m2), np.sign(m1))
-    assert np.array_equal(pn, np.array([1e-3, -1e-3], np.float32))
+    lr = np.float32(1e-3)
+    assert np.array_equal(pn, np.array([lr, -lr, -lr, lr], np.float32))
 
 
 @pytest.mark.parametrize("wd", [0.0])

@@ -63,9 +63,10 @@ def test_codes_are_the_two_neighbours_and_entries_stay(which):
     k = np.array([max(0, min(254, int(np.searchsorted(t64, float(v), side="right")) - 1)) for v in x])
     assert np.all((codes == k) | (codes == k + 1))
     assert np.all(t64[codes] <= np.maximum(x.astype(np.float64), t64[k + 1]))
-    # a value equal to an entry is stored as that entry whatever the draw
+    # a value equal to an entry is stored as that entry whatever the draw, the draw 0 included
     ent = np.repeat(table, 64)
     rr = rng.integers(0, 65536, ent.size).astype(np.uint32)
+    rr[::2] = 0
     assert np.array_equal(table[sr_codes(ent, table, gap_weights(table), rr)], ent)
 
 
