@@ -195,9 +195,19 @@ def main():
         step_fn(lists[(t - 1) % pool], hp)
 
     # ---------------------------------------------------------------- timing
+    # step 1 (zero state) is timed on its own inside the warmup: its blocks start from absmax 0
     t_step = 1
-    for _ in range(args.warmup):
-        step(t_step)
+    step1_ms = None
+    for w_i in range(args.warmup):
+        if w_i == 0:
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            step(t_step)
+            e1.record()
+            torch.cuda.synchronize()
+            step1_ms = e0.elapsed_time(e1)
+        else:
+            step(t_step)
         t_step += 1
     torch.cuda.synchronize()
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
@@ -296,6 +306,9 @@ def main():
                    "attainable_copy_GBps": attain.get("copy"),
                    "attainable_3r2w_GBps": attain.get("mix")},
         "roofline": roof,
+        "timing": {"median_ms": round(sorted(ev_ms)[len(ev_ms) // 2], 4), "min_ms": round(min(ev_ms), 4),
+                   "max_ms": round(max(ev_ms), 4),
+                   "step1_ms": round(step1_ms, 4) if step1_ms is not None else None},
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
