@@ -393,7 +393,9 @@ __device__ __forceinline__ uint32_t code_sr(float n, const uint8_t* lds, uint32_
 }
 
 // A full block; returns false (having written nothing) when the block must
-// take the plain path instead.
+// take the plain path instead.  Everything that could make a result NaN or
+// leave the range of the fast sequences is checked after pass 1, so pass 2
+// stores each group's parameters and codes as soon as they are formed.
 template <bool kNearest, bool kSS>
 __device__ __forceinline__ bool block_8bit_fast(const DevTensor& d, int64_t blk, int lane,
                                                 const StepScalars& sc, const uint8_t* lds, bool range_ok) {
@@ -414,17 +416,16 @@ __device__ __forceinline__ bool block_8bit_fast(const DevTensor& d, int64_t blk,
     QM[r] = ld_stream8(mp + off);
     QV[r] = ld_stream8(vp + off);
   }
-  // the parameters are needed from pass 2 on; loading them here keeps their
-  // registers free during pass 1 while the wave's other loads are in flight
 #pragma unroll
   for (int r = 0; r < kGroups; ++r)
     P[r] = ld_stream16(pp + r * 512 + lane * 8);
 
-  // pass 1: moments, block maxima, smallest exponents
+  // pass 1: moments, block maxima (NaN-propagating), smallest exponents, and
+  // the largest parameter magnitude
   const float* cb_s = reinterpret_cast<const float*>(lds + kOffCbS);
   const float* cb_u = reinterpret_cast<const float*>(lds + kOffCbU);
   float M2[kGroups * 8], V2[kGroups * 8];
-  float mxm = 0.0f, mxv = 0.0f;
+  float mxm = 0.0f, mxv = 0.0f, mxp = 0.0f;
   int emin = 0;
 #pragma unroll
   for (int r = 0; r < kGroups; ++r) {
@@ -437,67 +438,33 @@ __device__ __forceinline__ bool block_8bit_fast(const DevTensor& d, int64_t blk,
       const float v2 = sc.beta2 * v1 + sc.w2 * (g * g);
       M2[r * 8 + j] = m2;
       V2[r * 8 + j] = v2;
-      mxm = fmaxf(mxm, fabsf(m2));
-      mxv = fmaxf(mxv, v2);
+      mxm = __builtin_elementwise_maximum(mxm, fabsf(m2));
+      mxv = __builtin_elementwise_maximum(mxv, v2);
+      mxp = __builtin_elementwise_maximum(mxp, fabsf(bf16_at(P[r], j)));
       // smallest exponent of any non-zero m2 or v2 (frexp gives 0 for zero)
       emin = min(min(emin, __builtin_amdgcn_frexp_expf(m2)), __builtin_amdgcn_frexp_expf(v2));
     }
   }
+  // finite parameters and moments (NaN fails every comparison)
+  const bool lane_finite = (mxm <= 3.0e38f) && (mxv <= 3.0e38f) && (mxp <= 3.4028235e38f);
   mxm = wave_max(mxm);
   mxv = wave_max(mxv);
 
-  // range check for sqrt_rn / div_rn (uniform): finite maxima, every non-zero
-  // v2 >= 2^-89, every non-zero m2 / den quotient far above 2^-126
-  const bool finite = (mxm <= 3.0e38f) && (mxv <= 3.0e38f);
+  // range check (uniform): finite inputs and moments; every non-zero v2 >=
+  // 2^-89 (sqrt_rn) and every non-zero m2 / den quotient far above 2^-126
+  // (div_rn).  With range_ok (eps in [2^-60, 2^60], rbc2 <= 2^20, lrwd <= 1,
+  // step_size <= 2^26) no step of pass 2 can then produce a NaN or overflow
+  // an intermediate: den >= eps, |u| <= 2^101, |p - lrwd p| <= |p|.
   const int e_den = __builtin_amdgcn_frexp_expf(sqrtf(mxv) * sc.rbc2 + sc.eps);
   const int e_mmax = __builtin_amdgcn_frexp_expf(mxm);
   const int e_eps = __builtin_amdgcn_frexp_expf(sc.eps);
   const int floor_e = max(-88, e_den - 98);
-  const bool lane_bad = emin < floor_e;
-  if (!range_ok || !finite || e_den > 100 || e_mmax - e_eps > 100 ||
-      __builtin_amdgcn_ballot_w64(lane_bad) != 0)
+  const bool lane_bad = !lane_finite || emin < floor_e;
+  if (!range_ok || e_den > 100 || e_mmax - e_eps > 100 || __builtin_amdgcn_ballot_w64(lane_bad) != 0)
     return false;
 
-  // pass 2: parameter update and its rounding (stores deferred)
-  uint32_t c0[4] = {0, 0, 0, 0}, c1[4] = {0, 0, 0, 0}, c2[4] = {0, 0, 0, 0}, c3[4] = {0, 0, 0, 0};
-  if (!kNearest) {
-    const uint64_t grp0 = (static_cast<uint64_t>(d.index_base + e0) >> 3) + static_cast<uint64_t>(lane);
-#pragma unroll
-    for (int r = 0; r < kGroups; ++r) {
-      const uint64_t grp = grp0 + static_cast<uint64_t>(r * 64);
-      c0[r] = static_cast<uint32_t>(grp);
-      c1[r] = static_cast<uint32_t>(grp >> 32);   // stream 0
-      c2[r] = sc.step_lo;
-      c3[r] = d.tensor_id;
-    }
-    philox10_n<4>(c0, c1, c2, c3, sc.seed_lo, sc.seed_hi);
-  }
-  uint64_t nan_lanes = 0;
-#pragma unroll
-  for (int r = 0; r < kGroups; ++r) {
-    const Rand4 rnd{{c0[r], c1[r], c2[r], c3[r]}};
-    uint32_t sums[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const float p = bf16_at(P[r], j);
-      const float den = sqrt_rn(V2[r * 8 + j]) * sc.rbc2 + sc.eps;
-      const float u = div_rn(M2[r * 8 + j], den);
-      const float pn = (p - sc.lrwd * p) - sc.step_size * u;
-      nan_lanes |= __builtin_amdgcn_ballot_w64(pn != pn);
-      const uint32_t b = __float_as_uint(pn);
-      sums[j] = b + (kNearest ? (0x7FFFu + ((b >> 16) & 1u)) : r16_of(rnd, j));
-    }
-    // keep the upper halves: bf16 pairs (element 2k in the low half)
-    P[r] = make_uint4(__builtin_amdgcn_perm(sums[1], sums[0], 0x07060302u),
-                      __builtin_amdgcn_perm(sums[3], sums[2], 0x07060302u),
-                      __builtin_amdgcn_perm(sums[5], sums[4], 0x07060302u),
-                      __builtin_amdgcn_perm(sums[7], sums[6], 0x07060302u));
-  }
-  if (nan_lanes != 0) return false;
-#pragma unroll
-  for (int r = 0; r < kGroups; ++r) st_stream16(pp + r * 512 + lane * 8, P[r]);
-
-  // pass 3: requantise (a block with absmax below 2^-126 stores the zero code;
+  // pass 2, group by group: parameter update, its rounding and store, then the
+  // requantised moments (a block with absmax below 2^-126 stores the zero code;
   // its codes are computed from n = 0 and then replaced)
   const float* mid_s = reinterpret_cast<const float*>(lds + kOffMidS);
   const float* mid_u = reinterpret_cast<const float*>(lds + kOffMidU);
@@ -505,14 +472,31 @@ __device__ __forceinline__ bool block_8bit_fast(const DevTensor& d, int64_t blk,
   const bool live_v = mxv >= kMinNormal;
   const float inv_m = live_m ? 1.0f / mxm : 0.0f;
   const float inv_v = live_v ? 1.0f / mxv : 0.0f;
+  const uint64_t grp0 = (static_cast<uint64_t>(d.index_base + e0) >> 3) + static_cast<uint64_t>(lane);
 #pragma unroll
   for (int r = 0; r < kGroups; ++r) {
     const int off = r * 512 + lane * 8;
+    const uint64_t grp = grp0 + static_cast<uint64_t>(r * 64);
+    Rand4 rnd{{0, 0, 0, 0}};
+    if (!kNearest) rnd = group_bits(grp, 0u, d.tensor_id, sc);
+    uint32_t sums[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float p = bf16_at(P[r], j);
+      const float den = sqrt_rn(V2[r * 8 + j]) * sc.rbc2 + sc.eps;
+      const float u = div_rn(M2[r * 8 + j], den);
+      const float pn = (p - sc.lrwd * p) - sc.step_size * u;
+      const uint32_t b = __float_as_uint(pn);
+      sums[j] = b + (kNearest ? (0x7FFFu + ((b >> 16) & 1u)) : r16_of(rnd, j));
+    }
+    // keep the upper halves: bf16 pairs (element 2k in the low half)
+    st_stream16(pp + off, make_uint4(__builtin_amdgcn_perm(sums[1], sums[0], 0x07060302u),
+                                     __builtin_amdgcn_perm(sums[3], sums[2], 0x07060302u),
+                                     __builtin_amdgcn_perm(sums[5], sums[4], 0x07060302u),
+                                     __builtin_amdgcn_perm(sums[7], sums[6], 0x07060302u)));
     uint32_t cm[2] = {0, 0}, cv[2] = {0, 0};
     Rand4 rm{{0, 0, 0, 0}}, rv{{0, 0, 0, 0}};
-    if constexpr (kSS)
-      state_bits((static_cast<uint64_t>(d.index_base + e0) >> 3) + static_cast<uint64_t>(lane + r * 64),
-                 d.tensor_id, sc, rm, rv);
+    if constexpr (kSS) state_bits(grp, d.tensor_id, sc, rm, rv);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       uint32_t qm, qv;
@@ -1112,9 +1096,11 @@ hipError_t upload_tables(const uint8_t* host_tables) {
 hipError_t launch_step(Kind kind, int algo, const DevTensor* list, int n, int64_t total_blocks,
                        const StepScalars& sc, hipStream_t stream, int grid_cap) {
   if (n <= 0 || total_blocks <= 0) return hipSuccess;
-  // the fast AdamW paths need eps well inside the normal range and a bounded
-  // second-moment correction (they then check each block's own values)
-  const int range_ok = (sc.eps >= 0x1p-60f && sc.eps <= 0x1p+60f && sc.rbc2 <= 0x1p+20f) ? 1 : 0;
+  // the fast AdamW paths need eps well inside the normal range, a bounded
+  // second-moment correction, decay and step size (they then check each
+  // block's own values)
+  const int range_ok = (sc.eps >= 0x1p-60f && sc.eps <= 0x1p+60f && sc.rbc2 <= 0x1p+20f &&
+                        sc.lrwd <= 1.0f && sc.step_size <= 0x1p+26f) ? 1 : 0;
   const bool ss = sc.state_round != 0;
   switch (kind) {
     case Kind::k8bit:
