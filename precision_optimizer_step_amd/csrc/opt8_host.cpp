@@ -128,11 +128,12 @@ int count_at_or_below(const float* table, float x) {
   return c;
 }
 
-// Floor LUT entry: the largest entry at or below the bucket's smallest value
-// (0 when the bucket starts below the table); false if a bucket holds two entries.
+// Floor LUT entry: the largest entry at or below the bucket's smallest value,
+// clamped to [0, 254] (the lower end of the last gap); false if a bucket holds
+// two entries.
 bool floor_entry(const float* table, float least, float most, uint8_t& out) {
-  const int base = std::max(count_at_or_below(table, least) - 1, 0);
-  const int top = std::max(count_at_or_below(table, most) - 1, 0);
+  const int base = std::min(std::max(count_at_or_below(table, least) - 1, 0), kCodes - 2);
+  const int top = std::min(std::max(count_at_or_below(table, most) - 1, 0), kCodes - 2);
   out = static_cast<uint8_t>(base);
   return top - base <= 1;
 }
@@ -151,10 +152,12 @@ bool build_sr_tables(uint8_t* bytes) {
     const float least = key == kKeyLo ? 0.0f : bits_f32(key << 16);
     if (!floor_entry(cb_u, least, bits_f32((key << 16) | 0xFFFFu), bytes[kOffFloor + key])) return false;
   }
+  // the last pair holds +inf as its entry, so the comparison with the entry
+  // after a floor of 254 never moves k past 254
   auto pairs = [&](const float* table, int off) {
     float pr[2 * kCodes];
     for (int k = 0; k < kCodes; ++k) {
-      pr[2 * k] = table[k];
+      pr[2 * k] = k + 1 < kCodes ? table[k] : INFINITY;
       pr[2 * k + 1] = k + 1 < kCodes
           ? static_cast<float>(65536.0 / (static_cast<double>(table[k + 1]) - static_cast<double>(table[k])))
           : 0.0f;

@@ -74,9 +74,10 @@ static_assert(kOffCbS >= static_cast<int>(kKeySPosEnd) && kKeyHi < kKeySNeg, "LU
 //   [0x9200, 0xA000)  unsigned floor LUT at kOffFloor + max(bits(n) >> 16, kKeyLo)
 //   [0xA000, 0xC000)  signed floor LUT for -2 < n <= -0 at kOffFloor + (bits(n) >> 17)
 // A floor entry is the index of the largest codebook entry at or below the
-// bucket's smallest value (0 below the table); no bucket holds more than one
+// bucket's smallest value, clamped to [0, 254]; no bucket holds more than one
 // entry (checked), so the entry at or below n is floor + (C[floor + 1] <= n).
-// W[k] = 65536 / (C[k+1] - C[k]) in double rounded once to fp32 (W[255] = 0).
+// Pair k holds (C[k], W[k]), W[k] = 65536 / (C[k+1] - C[k]) in double rounded
+// once to fp32; pair 255 holds (+inf, 0), so k never passes 254.
 constexpr int kOffFloor = 0x6000;
 constexpr int kOffPairS = 0x8000, kOffPairU = 0x8800;
 constexpr int kTableBytesSR = 0xC000;

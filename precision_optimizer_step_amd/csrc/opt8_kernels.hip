@@ -380,14 +380,15 @@ __device__ __forceinline__ uint32_t code_s(float n, const uint8_t* lds, const fl
 }
 
 // Stochastic state rounding through the floor LUTs (finite -2 < n < 2): the
-// entry at or below n is floor + (C[floor + 1] <= n), clamped to 254.
+// entry at or below n is floor + (C[floor + 1] <= n); floors stop at 254 and
+// the last pair's entry is +inf, so k stays in [0, 254].
 template <bool kSigned>
 __device__ __forceinline__ uint32_t code_sr(float n, const uint8_t* lds, uint32_t r16) {
   const uint32_t b = __float_as_uint(n);
   const uint32_t key = kSigned ? (b >> 17) : max(b >> 16, kKeyLo);
   const float* pair = reinterpret_cast<const float*>(lds + (kSigned ? kOffPairS : kOffPairU));
   const uint32_t c = lds[kOffFloor + key];
-  const uint32_t k = min(c + ((pair[2 * c + 2] <= n) ? 1u : 0u), 254u);
+  const uint32_t k = c + ((pair[2 * c + 2] <= n) ? 1u : 0u);
   const float f = (n - pair[2 * k]) * pair[2 * k + 1];
   return k + ((f > static_cast<float>(r16)) ? 1u : 0u);
 }
