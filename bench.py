@@ -96,8 +96,8 @@ def probe_bandwidth(dev, words=1 << 27, reps=5):
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="gptneo-6.7b")
     ap.add_argument("--grad-pool", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
