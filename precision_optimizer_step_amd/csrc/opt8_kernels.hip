@@ -1,14 +1,15 @@
-// gfx950 kernels of the fused AdamW step (8-bit, bf16-SR and fp32 state).
+// gfx950 kernels of the fused optimizer steps: AdamW, Lion and SGD with
+// momentum over 8-bit block-wise, bf16 (stochastically rounded) or fp32 state.
 //
 // Work unit: one 2048-element quantisation block per wave64 ("8-bit Optimizers
 // via Block-wise Quantization", method bullets: 2048-element blocks normalised
 // by their own absolute maximum).  Lane l of the wave owns elements
 // r*512 + 8l .. r*512 + 8l + 7 for r = 0..3, so every global access of a wave
 // is one contiguous 1 KiB (bf16, 16 B per lane) or 512 B (codes, 8 B per lane)
-// segment, and one Philox call per lane and r yields the 8 random 16-bit words
-// of those 8 elements.  A block's absmax is a max, reduced across the wave
-// with cross-lane shuffles, so it is exact and independent of order; no
-// workgroup barrier is needed inside the block loop.
+// segment, and one Philox call per lane, r and stream yields the 8 random
+// 16-bit words of those 8 elements.  A block's absmax is a max, reduced across
+// the wave with cross-lane shuffles, so it is exact and independent of order;
+// no workgroup barrier is needed inside the block loop.
 //
 // Waves of a persistent grid take contiguous runs of blocks over the whole
 // tensor list; each workgroup stages the codebooks, midpoints and code LUTs in
@@ -16,9 +17,9 @@
 //
 // Arithmetic is the step exactly as the oracle states it: fp32, one rounding
 // per operation (built with -ffp-contract=off), IEEE sqrt and divide,
-// denormals kept.  The fast 8-bit path reaches the same bits with cheaper
-// instruction sequences whose exactness holds inside a range the block is
-// checked against; a block outside it takes the plain path.
+// denormals kept.  The fast paths reach the same bits with cheaper instruction
+// sequences whose exactness holds inside a range the block is checked
+// against; a block outside it takes the plain path.
 #include "opt8_internal.h"
 
 namespace opt8 {
