@@ -1,0 +1,99 @@
+"""Streams and the per-device descriptor cache.
+
+The library keeps up to four descriptor lists on each device and reuses one
+when the same list is passed again; a list moved to another stream waits for
+the last launch that read it.  These tests run steps on side streams and
+cycle more lists than the cache holds, and check every result against the
+oracle.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_helpers import DevTensorSet, compare_state, log, oracle_step
+from precision_optimizer_step_amd import opt8
+from workloads import gen
+
+pytestmark = pytest.mark.gpu
+
+M8 = oracle.MODE_8BIT
+
+
+@pytest.fixture(scope="module", autouse=True)
+def device():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a visible AMD GPU")
+    torch.cuda.set_device(0)
+    opt8.opt8_init_codebooks()
+
+
+def _bf16(rng, n, sigma):
+    return gen.to_bf16_bits((rng.standard_normal(n) * sigma).astype(np.float32))
+
+
+def _make(rng, n, tid, seed):
+    p, g = _bf16(rng, n, 0.02), _bf16(rng, n, 1e-3)
+    m, v, am, av = gen.random_state_8bit(seed, tid, n)
+    return DevTensorSet(M8, p, g, m, v, am, av, tensor_id=tid), [p, m, v, am, av]
+
+
+def _hp(step):
+    return oracle.Hparams(lr=1e-3, weight_decay=0.01, step=step, seed=77)
+
+
+def _launch(sets, hp, stream):
+    descs = [s.desc() for s in sets]
+    opt8.opt8_adamw_step(descs, opt8.make_hparams(hp.lr, hp.beta1, hp.beta2, hp.eps, hp.weight_decay,
+                                                  hp.step, hp.seed), stream=stream)
+
+
+def test_side_streams_and_a_list_moving_between_streams():
+    """One list stepped on side stream 1 and, with no host synchronisation in between, on side
+    stream 2: the second launch must wait for the first through the library's event (the
+    streams themselves are unordered).  Another list runs on the current stream.  Results are
+    checked against two oracle steps."""
+    rng = np.random.default_rng(5)
+    a = [_make(rng, 2048 * 6 + 100, 10 + i, 3) for i in range(3)]
+    b = [_make(rng, 2048 * 4, 20 + i, 4) for i in range(2)]
+    sa, sta = [x[0] for x in a], [x[1] for x in a]
+    sb, stb = [x[0] for x in b], [x[1] for x in b]
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    torch.cuda.synchronize()
+    stats = {}
+    for t in range(1, 7, 2):
+        _launch(sa, _hp(t), s1)
+        _launch(sa, _hp(t + 1), s2)          # ordered after the s1 launch by the library
+        _launch(sb, _hp(t), None)
+        _launch(sb, _hp(t + 1), None)
+        torch.cuda.synchronize()
+        for sets, states in ((sa, sta), (sb, stb)):
+            for k, (s, st) in enumerate(zip(sets, states)):
+                want = oracle_step(s, oracle_step(s, st, _hp(t)), _hp(t + 1))
+                compare_state(f"streams steps {t},{t + 1}/t{s.tensor_id}", s.read(), want, M8, stats)
+                states[k] = want
+    log(f"side streams: mismatches {sum(stats.values())}")
+    assert sum(stats.values()) == 0
+
+
+def test_more_lists_than_cached_slots():
+    """Six lists (the cache holds four) stepped round-robin for three rounds, so every list is
+    evicted and uploaded again; results equal the oracle's."""
+    rng = np.random.default_rng(6)
+    lists = []
+    for li in range(6):
+        items = [_make(rng, 2048 * (1 + li) + 37 * li, 100 + 10 * li + k, 8 + li) for k in range(2)]
+        lists.append(([x[0] for x in items], [x[1] for x in items]))
+    stats = {}
+    for rnd in range(3):
+        for li, (sets, states) in enumerate(lists):
+            hp = _hp(rnd + 1)
+            _launch(sets, hp, None)
+            torch.cuda.synchronize()
+            for k, (s, st) in enumerate(zip(sets, states)):
+                want = oracle_step(s, st, hp)
+                compare_state(f"cache round {rnd} list {li}/t{s.tensor_id}", s.read(), want, M8, stats)
+                states[k] = want
+    log(f"descriptor cache: mismatches {sum(stats.values())}")
+    assert sum(stats.values()) == 0
