@@ -305,3 +305,27 @@ def test_non_finite_inputs():
         assert np.array_equal(got[k][ok], want[k][ok])
     # the third block is untouched by the bad values and matches bit for bit
     assert np.array_equal(got[0][4096:], want[0][4096:])
+
+
+@pytest.mark.parametrize("label,hp_kw", [
+    ("eps below 2^-60", dict(eps=1e-20)),
+    ("eps above 2^60", dict(eps=1e20)),
+    ("lr*wd above 1", dict(lr=0.5, weight_decay=4.0)),
+    ("huge step size", dict(lr=1e9)),
+])
+def test_hyperparameters_outside_the_fast_range(label, hp_kw):
+    """Hyperparameters that switch the fast AdamW sequences off for the whole launch (every
+    block then takes the plain path) on a list of all three modes: still equal to the oracle."""
+    rng = np.random.default_rng(31)
+    sets, states = [], []
+    for tid, (n, mode) in enumerate([(2048 * 5 + 19, M8), (2048 * 3, MB), (1000, MF), (4096, M8)]):
+        p, g = _rand_bf16(rng, n, 0.02), _rand_bf16(rng, n, 1e-3)
+        st = _rand_state(mode, n, 40, tid)
+        sets.append(DevTensorSet(mode, p, g, *st, tensor_id=tid))
+        states.append([p, *st])
+    kw = dict(lr=1e-3, weight_decay=0.01, step=3, seed=5)
+    kw.update(hp_kw)
+    hp = oracle.Hparams(**kw)
+    stats = {}
+    _run_and_compare(sets, states, hp, label, stats)
+    log(f"{label}: mismatches {sum(stats.values())}")
