@@ -188,10 +188,12 @@ __device__ __forceinline__ float adamw(float p, float g, float m1, float v1, con
 // s0 = x*y, the residual exact in an fma.  Checked against the correctly
 // rounded root for every fp32 in [2^-96, inf) on gfx950 (v_sqrt_f32 alone is
 // one ulp off for about 15% of them).  Below 2^-96 the residual can underflow;
-// the input floor keeps y finite so that x = 0 gives 0.  Outside that range
-// the plain sqrtf is used.
+// the input floor 2^-126 (an integer max on the bits, equal to the float max
+// for x >= +0) keeps y finite so that x = 0 gives 0, and a negative x keeps its
+// bits, so its root is NaN as the IEEE one.  Outside that range the plain
+// sqrtf is used.
 __device__ __forceinline__ float sqrt_rn(float x) {
-  const float y = __builtin_amdgcn_rsqf(fmaxf(x, 0x1p-126f));
+  const float y = __builtin_amdgcn_rsqf(__uint_as_float(max(__float_as_uint(x), 0x00800000u)));
   const float s0 = x * y;
   const float h = 0.5f * y;
   const float r = __builtin_fmaf(-s0, s0, x);
@@ -310,7 +312,7 @@ __device__ __forceinline__ void block_8bit_plain(const DevTensor& d, int64_t blk
       M2[r * 8 + j] = ok ? m2 : 0.0f;
       V2[r * 8 + j] = ok ? v2 : 0.0f;
       mxm = nan_max(mxm, fabsf(M2[r * 8 + j]));
-      mxv = nan_max(mxv, V2[r * 8 + j]);
+      mxv = nan_max(mxv, fabsf(V2[r * 8 + j]));   // |v2|: a negative v2 is possible from a negative absmax_v
     }
     if (kFull) {
       *reinterpret_cast<uint4*>(pp + off) = make_uint4(outw[0], outw[1], outw[2], outw[3]);
@@ -462,7 +464,9 @@ __device__ __forceinline__ bool block_8bit_fast(const DevTensor& d, int64_t blk,
   const int e_eps = __builtin_amdgcn_frexp_expf(sc.eps);
   const int floor_e = max(-88, e_den - 98);
   const bool lane_bad = !lane_finite || emin < floor_e;
-  if (!range_ok || e_den > 100 || e_mmax - e_eps > 100 || __builtin_amdgcn_ballot_w64(lane_bad) != 0)
+  // a negative (or NaN) absmax_v could make v2 negative, whose root is NaN
+  if (!range_ok || !(av >= 0.0f) || e_den > 100 || e_mmax - e_eps > 100 ||
+      __builtin_amdgcn_ballot_w64(lane_bad) != 0)
     return false;
 
   // pass 2, group by group: parameter update, its rounding and store, then the

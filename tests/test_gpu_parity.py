@@ -329,3 +329,41 @@ def test_hyperparameters_outside_the_fast_range(label, hp_kw):
     stats = {}
     _run_and_compare(sets, states, hp, label, stats)
     log(f"{label}: mismatches {sum(stats.values())}")
+
+
+def test_negative_second_moment_state():
+    """Invalid but defined: a negative absmax_v (8-bit) or negative bf16 v makes v2 negative,
+    its square root NaN and the parameter NaN, as in the oracle; the fast paths must hand
+    such blocks to the plain path.  NaN is compared as NaN, everything else bit for bit."""
+    rng = np.random.default_rng(41)
+    n = 2048 * 3
+    p, g = _rand_bf16(rng, n, 0.02), _rand_bf16(rng, n, 1e-4)
+    m8, v8, am8, av8 = _rand_state(M8, n, 42, 0)
+    av8 = av8.copy()
+    av8[1] = -av8[1] - 1e-6                       # block 1: negative second-moment scale
+    mb, vb, _, _ = _rand_state(MB, n, 43, 1)
+    vb = vb.copy()
+    vb[2048 + 5] = gen.to_bf16_bits(np.float32([-1e-2]))[0]   # one negative bf16 v in block 1
+    hp = oracle.Hparams(lr=1e-3, weight_decay=0.01, step=2, seed=7)
+    for mode, st in ((M8, (m8, v8, am8, av8)), (MB, (mb, vb, None, None))):
+        want = oracle_step(DevTensorSet(mode, p, g, *st, tensor_id=3), [p, *st], hp)
+        s = DevTensorSet(mode, p, g, *st, tensor_id=3)
+        gpu_step([s], hp)
+        got = s.read()
+        wp, gp = oracle.rounding.bf16_to_f32(want[0]), oracle.rounding.bf16_to_f32(got[0])
+        assert np.isnan(wp).any(), "the case must produce NaN parameters"
+        assert np.array_equal(np.isnan(wp), np.isnan(gp))
+        assert np.array_equal(got[0][~np.isnan(wp)], want[0][~np.isnan(wp)])
+        for k in (1, 2):
+            if mode == MB:
+                wk = oracle.rounding.bf16_to_f32(want[k])
+                gk = oracle.rounding.bf16_to_f32(got[k])
+                assert np.array_equal(np.isnan(wk), np.isnan(gk))
+                assert np.array_equal(got[k][~np.isnan(wk)], want[k][~np.isnan(wk)])
+            else:
+                assert np.array_equal(got[k], want[k])
+        if mode == M8:
+            for k in (3, 4):
+                assert np.array_equal(np.isnan(got[k]), np.isnan(want[k]))
+                ok = ~np.isnan(want[k])
+                assert np.array_equal(got[k][ok], want[k][ok])
