@@ -8,12 +8,12 @@
 // is one contiguous 1 KiB (bf16, 16 B per lane) or 512 B (codes, 8 B per lane)
 // segment, and one Philox call per lane, r and stream yields the 8 random
 // 16-bit words of those 8 elements.  A block's absmax is a max, reduced across
-// the wave with cross-lane shuffles, so it is exact and independent of order;
-// no workgroup barrier is needed inside the block loop.
+// the wave with cross-lane (DPP or shuffle) steps, so it is exact and
+// independent of order; no workgroup barrier is needed inside the block loop.
 //
-// Waves of a persistent grid take contiguous runs of blocks over the whole
-// tensor list; each workgroup stages the codebooks, midpoints and code LUTs in
-// LDS once.
+// The waves of a persistent grid stride over the blocks of the whole tensor
+// list (wave w takes blocks w, w + W, w + 2W, ... for W waves in the grid);
+// each workgroup stages the codebooks, midpoints and code LUTs in LDS once.
 //
 // Arithmetic is the step exactly as the oracle states it: fp32, one rounding
 // per operation (built with -ffp-contract=off), IEEE sqrt and divide,
@@ -237,16 +237,26 @@ __device__ __forceinline__ uint32_t code_sr_search(float n, const float* pair, u
   return (n != n) ? 255u : code;
 }
 
-__device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
-  return x;
-}
-
 __device__ __forceinline__ float wave_nan_max(float x) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) x = nan_max(x, __shfl_xor(x, o, 64));
   return x;
+}
+
+// Wave max of values that are +0, positive or NaN, returned as a uniform
+// value: the unsigned max of the bit patterns (which orders such floats as
+// their values) through DPP quad, half-row, row and row-broadcast steps, read
+// from lane 63.  Unlike the shuffle reduction above it moves nothing through
+// LDS.
+__device__ __forceinline__ float wave_max_nonneg(float x) {
+  uint32_t u = __float_as_uint(x);
+  u = max(u, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(u), 0xB1, 0xF, 0xF, false)));
+  u = max(u, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(u), 0x4E, 0xF, 0xF, false)));
+  u = max(u, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(u), 0x141, 0xF, 0xF, false)));
+  u = max(u, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(u), 0x140, 0xF, 0xF, false)));
+  u = max(u, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(u), 0x142, 0xA, 0xF, false)));
+  u = max(u, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(u), 0x143, 0xC, 0xF, false)));
+  return __uint_as_float(__builtin_amdgcn_readlane(static_cast<int>(u), 63));
 }
 
 // ----------------------------------------------------------------------------- 8-bit, plain path
@@ -451,8 +461,8 @@ __device__ __forceinline__ bool block_8bit_fast(const DevTensor& d, int64_t blk,
   }
   // finite parameters and moments (NaN fails every comparison)
   const bool lane_finite = (mxm <= 3.0e38f) && (mxv <= 3.0e38f) && (mxp <= 3.4028235e38f);
-  mxm = wave_max(mxm);
-  mxv = wave_max(mxv);
+  mxm = wave_max_nonneg(mxm);
+  mxv = wave_max_nonneg(mxv);
 
   // range check (uniform): finite inputs and moments; every non-zero v2 >=
   // 2^-89 (sqrt_rn) and every non-zero m2 / den quotient far above 2^-126
@@ -908,7 +918,7 @@ __device__ __forceinline__ bool block_1s_8bit_fast(const DevTensor& d, int64_t b
                       __builtin_amdgcn_perm(sums[5], sums[4], 0x07060302u),
                       __builtin_amdgcn_perm(sums[7], sums[6], 0x07060302u));
   }
-  mxm = wave_max(mxm);
+  mxm = wave_max_nonneg(mxm);
   if (nan_lanes != 0 || !(mxm <= 3.0e38f)) return false;
 #pragma unroll
   for (int r = 0; r < kGroups; ++r) st_stream16(pp + r * 512 + lane * 8, P[r]);
@@ -1058,9 +1068,11 @@ step_kernel(const DevTensor* __restrict__ list, int ntensors, int64_t total_bloc
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
   const int64_t gw = static_cast<int64_t>(blockIdx.x) * kWaves + wave;
   const int64_t nw = static_cast<int64_t>(gridDim.x) * kWaves;
-  int64_t b = total_blocks * gw / nw;
-  const int64_t bend = total_blocks * (gw + 1) / nw;
-  if (b >= bend) return;
+  // wave gw takes blocks gw, gw + nw, gw + 2 nw, ...: the waves in flight
+  // stream through one window of adjacent blocks, which the memory system
+  // serves faster than as many separate runs
+  int64_t b = gw;
+  if (b >= total_blocks) return;
 
   // the tensor holding block b: the last one whose first block is <= b
   int lo = 0, hi = ntensors - 1;
@@ -1070,7 +1082,7 @@ step_kernel(const DevTensor* __restrict__ list, int ntensors, int64_t total_bloc
   }
   int t = lo;
   DevTensor d = list[t];
-  for (; b < bend; ++b) {
+  for (; b < total_blocks; b += nw) {
     while (b >= d.block_begin + static_cast<int64_t>(d.nblocks)) d = list[++t];
     const int64_t blk = b - d.block_begin;
     if constexpr (A != kAdamW) {

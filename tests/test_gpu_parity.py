@@ -367,3 +367,98 @@ def test_negative_second_moment_state():
                 assert np.array_equal(np.isnan(got[k]), np.isnan(want[k]))
                 ok = ~np.isnan(want[k])
                 assert np.array_equal(got[k][ok], want[k][ok])
+
+
+
+def _edge(cond):
+    """Smallest bf16 magnitude pattern h (a positive bf16 value g) with cond(g) true, for a
+    condition that is false below some magnitude and true from there on."""
+    h = np.arange(1, 0x7F80, dtype=np.uint32)
+    with np.errstate(over="ignore", invalid="ignore"):
+        ok = cond((h << 16).view(np.float32))
+    assert ok.any() and ok[-1]
+    return int(h[np.argmax(ok)])
+
+
+def _frexp_e(x):
+    return np.frexp(np.asarray(x, np.float32))[1]
+
+
+@pytest.mark.parametrize("betas", [(0.9, 0.999), (0.0, 0.5), (0.99, 0.0)])
+def test_fast_path_range_edges(betas):
+    """Blocks on both sides of each bound of the 8-bit AdamW fast path's range check, found
+    with the oracle's fp32 arithmetic at step 1: a lone gradient whose v2 or m2 sits at the
+    smallest admitted exponent (2^-89) and one bf16 pattern below it, of either sign; a small
+    m2 against a large denominator at the quotient bound (e(m2) >= e(den) - 98); a tiny
+    absmax_m with zero gradients; and, with eps = 1e-18, the largest moment at the
+    max|m2| / eps bound.  Every block must equal the oracle bit for bit, whichever path it
+    takes."""
+    rng = np.random.default_rng(57)
+    kw = dict(lr=1e-3, beta1=betas[0], beta2=betas[1], weight_decay=0.01, seed=9)
+    s1 = oracle.adamw.host_scalars(oracle.Hparams(step=1, **kw))
+    w1, w2, rbc2, eps = s1.w1, s1.w2, s1.rbc2, s1.eps
+    f = np.float32
+    nb = 14
+    n = 2048 * nb
+    blk = [slice(2048 * b, 2048 * (b + 1)) for b in range(nb)]
+    p = _rand_bf16(rng, n, 0.02)
+    g = _rand_bf16(rng, n, 1e-3)
+    qm, qv, am, av = (a.copy() for a in gen.random_state_8bit(58, 0, n))
+
+    def zero_state(b):
+        qm[blk[b]], qv[blk[b]], am[b], av[b] = 127, 0, 0.0, 0.0
+
+    def lone(b, h, at=5):
+        g[2048 * b + at] = np.uint16(h)
+
+    # v2 = w2 * g^2 at the 2^-89 floor (zero state: m2 = w1 g, v2 = w2 g^2)
+    lim = f(2.0 ** -89)
+    if w2 != 0:
+        hv = _edge(lambda x: (w2 * (x * x) >= lim) & (np.abs(w1 * x) >= lim))
+        for b, h in ((0, hv), (1, hv - 1), (2, hv | 0x8000), (3, (hv - 1) | 0x8000)):
+            zero_state(b)
+            lone(b, h)
+    # m2 = w1 * g at the floor; v2 held up by a non-zero second-moment state
+    if w1 != 0:
+        hm = _edge(lambda x: np.abs(w1 * x) >= lim)
+        for b, h in ((4, hm), (5, hm - 1), (6, (hm - 1) | 0x8000)):
+            qm[blk[b]], am[b], av[b] = 127, 1.0, 1e-6
+            qv[blk[b]] = np.maximum(qv[blk[b]], 1)
+            lone(b, h)
+    # quotient bound: one large gradient sets den, a small m2 sits at e(den) - 98
+    for b, side in ((7, 0), (8, 1)):
+        qm[blk[b]], am[b], av[b] = 127, 1.0, 1e-6
+        qv[blk[b]] = np.maximum(qv[blk[b]], 1)
+        g[2048 * b] = gen.to_bf16_bits(f([3e4]))[0]
+        gb = oracle.rounding.bf16_to_f32(g[blk[b]])
+        v1 = oracle.codebook.tables()[2][qv[blk[b]]] * f(av[b])
+        v2 = s1.beta2 * v1 + w2 * (gb * gb)
+        e_den = _frexp_e(np.sqrt(np.max(v2)) * rbc2 + eps)
+        if w1 != 0:
+            h = _edge(lambda x: _frexp_e(w1 * x) >= e_den - 98)
+            lone(b, h - side, at=9)
+    # tiny absmax_m: m1 = Cs[q] * am far below the floor where the gradient is zero
+    for b, a in ((9, 2.0 ** -80), (10, 2.0 ** -60)):
+        am[b] = a
+        g[blk[b]][::5] = 0
+    stats = {}
+    for step in (1, 3):
+        hp = oracle.Hparams(step=step, **kw)
+        sets = [DevTensorSet(M8, p, g, qm, qv, am, av, tensor_id=2)]
+        _run_and_compare(sets, [[p, qm, qv, am, av]], hp, f"edges {betas} step {step}", stats)
+    # max|m2| / eps at 2^100: eps = 1e-18, zero state, one large gradient per block
+    kw_e = dict(kw, eps=1e-18)
+    se = oracle.adamw.host_scalars(oracle.Hparams(step=1, **kw_e))
+    if se.w1 != 0:
+        e_eps = _frexp_e(se.eps)
+        h = _edge(lambda x: _frexp_e(se.w1 * x) - e_eps > 100)
+        g2 = g.copy()
+        for b, hh in ((11, h), (12, h - 1), (13, (h - 1) | 0x8000)):
+            zero_state(b)
+            g2[2048 * b + 3] = np.uint16(hh)
+        sets = [DevTensorSet(M8, p, g2, qm, qv, am, av, tensor_id=2)]
+        _run_and_compare(sets, [[p, qm, qv, am, av]], oracle.Hparams(step=1, **kw_e),
+                         f"edges {betas} eps 1e-18", stats)
+    log(f"range edges {betas}: mismatches {sum(stats.values())}")
+    assert sum(stats.values()) == 0
+
