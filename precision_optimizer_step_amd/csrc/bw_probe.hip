@@ -1,10 +1,11 @@
-// Attainable-bandwidth probe: plain streaming kernels with a chosen number of
-// read and write streams of 16-byte words and no arithmetic beyond a xor.
-// Each thread moves four words per stream and iteration (a wave touches 4
-// contiguous 1 KiB segments per stream), with non-temporal loads and stores,
-// over a grid-stride loop.  It gives the practical HBM ceiling the step
-// kernels are compared with.  Measurement infrastructure only: not part of
-// the optimizer's C ABI.
+// Attainable-bandwidth probes: plain streaming kernels with a chosen number of
+// read and write streams of 16-byte words and no arithmetic beyond a xor
+// (each thread moves four words per stream and iteration, a wave touching 4
+// contiguous 1 KiB segments per stream, non-temporal loads and stores, a
+// grid-stride loop), and a kernel with the 8-bit step's own access pattern and
+// no arithmetic.  They give the practical HBM ceilings the step kernels are
+// compared with.  Measurement infrastructure only: not part of the
+// optimizer's C ABI.
 #include <hip/hip_runtime.h>
 #include <cstdint>
 
@@ -39,6 +40,45 @@ stream_kernel(const u32x4* __restrict__ in, u32x4* __restrict__ out, int64_t n, 
   }
 }
 
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(1))) u32x4 g_u32x4;
+typedef __attribute__((address_space(1))) u32x2 g_u32x2;
+
+// The 8-bit step's memory traffic without its arithmetic: one wave per
+// 2048-element block, lane l holding elements r*512 + 8l .. +7 (r = 0..3);
+// per block it reads 4 KiB of bf16 gradient, 4 KiB of bf16 parameter and
+// 2 KiB each of m and v codes, and writes the parameter and both code arrays
+// back (a xor of what it read), non-temporally, through the global address
+// space; waves stride over the blocks.
+__global__ void __launch_bounds__(kThreads)
+pattern_kernel(const uint16_t* __restrict__ g, uint16_t* __restrict__ p, uint8_t* __restrict__ m,
+               uint8_t* __restrict__ v, int64_t nblocks) {
+  const int lane = threadIdx.x & 63;
+  const int64_t nw = static_cast<int64_t>(gridDim.x) * (kThreads / 64);
+  for (int64_t b = static_cast<int64_t>(blockIdx.x) * (kThreads / 64) + (threadIdx.x >> 6); b < nblocks;
+       b += nw) {
+    const int64_t e0 = b * 2048;
+    u32x4 G[4], P[4];
+    u32x2 M[4], V[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int64_t e = e0 + r * 512 + lane * 8;
+      G[r] = __builtin_nontemporal_load((const g_u32x4*)(g + e));
+      M[r] = __builtin_nontemporal_load((const g_u32x2*)(m + e));
+      V[r] = __builtin_nontemporal_load((const g_u32x2*)(v + e));
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) P[r] = __builtin_nontemporal_load((const g_u32x4*)(p + e0 + r * 512 + lane * 8));
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int64_t e = e0 + r * 512 + lane * 8;
+      __builtin_nontemporal_store(P[r] ^ G[r], (g_u32x4*)(p + e));
+      __builtin_nontemporal_store(M[r] ^ G[r].xy, (g_u32x2*)(m + e));
+      __builtin_nontemporal_store(V[r] ^ G[r].zw, (g_u32x2*)(v + e));
+    }
+  }
+}
+
 }  // namespace
 
 // in: nin streams of `words` 16-byte words back to back; out: nout streams likewise.
@@ -47,5 +87,15 @@ extern "C" int opt8_probe_stream(const void* in, void* out, int64_t words, int n
   if (!in || !out || words <= 0 || nin < 1 || nout < 1 || nin > 8 || nout > 8 || grid < 1) return -1;
   hipLaunchKernelGGL(stream_kernel, dim3(grid), dim3(kThreads), 0, static_cast<hipStream_t>(stream),
                      static_cast<const u32x4*>(in), static_cast<u32x4*>(out), words, nin, nout);
+  return hipGetLastError() == hipSuccess ? 0 : -9;
+}
+
+// g, p: bf16[nblocks * 2048]; m, v: u8[nblocks * 2048]; p, m and v are rewritten.
+extern "C" int opt8_probe_pattern(const void* g, void* p, void* m, void* v, int64_t nblocks, int grid,
+                                  void* stream) {
+  if (!g || !p || !m || !v || nblocks <= 0 || grid < 1) return -1;
+  hipLaunchKernelGGL(pattern_kernel, dim3(grid), dim3(kThreads), 0, static_cast<hipStream_t>(stream),
+                     static_cast<const uint16_t*>(g), static_cast<uint16_t*>(p), static_cast<uint8_t*>(m),
+                     static_cast<uint8_t*>(v), nblocks);
   return hipGetLastError() == hipSuccess ? 0 : -9;
 }

@@ -1066,7 +1066,15 @@ step_kernel(const DevTensor* __restrict__ list, int ntensors, int64_t total_bloc
   if constexpr (kQ8) stage_tables<kLds>(lds);
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
-  const int64_t gw = static_cast<int64_t>(blockIdx.x) * kWaves + wave;
+  // workgroups are dispatched to the 8 XCDs round-robin (workgroup i on XCD
+  // i mod 8); the waves are renumbered so that each run of 16 consecutive
+  // numbers (four workgroups) lies on one XCD, so the 16 blocks sharing a
+  // 64-byte line of absmax values are handled by one XCD's L2
+  int64_t gw = static_cast<int64_t>(blockIdx.x) * kWaves + wave;
+  if ((gridDim.x & 31u) == 0) {
+    const int64_t x = blockIdx.x & 7u, i = blockIdx.x >> 3;   // XCD, workgroup within it
+    gw = (((i >> 2) * 8 + x) * 4 + (i & 3)) * kWaves + wave;
+  }
   const int64_t nw = static_cast<int64_t>(gridDim.x) * kWaves;
   // wave gw takes blocks gw, gw + nw, gw + 2 nw, ...: the waves in flight
   // stream through one window of adjacent blocks, which the memory system
