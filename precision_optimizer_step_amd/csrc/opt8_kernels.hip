@@ -156,6 +156,18 @@ __device__ __forceinline__ void st_stream8(void* p, const uint2& q) {
   __builtin_nontemporal_store(v, (g_u32x2_t*)(p));
 }
 
+// A block's absmax through the scalar cache (the address is uniform across the
+// wave).  Each wave reads its block's absmax before writing it back and no
+// other wave touches that word, and the scalar cache starts every dispatch
+// empty, so the read sees the value the step began with.  A scalar load waits
+// on its own counter; a generic (flat) load here would count against the
+// vector-memory loads of the block's data and make the first use of the
+// absmax wait for all of them.
+__device__ __forceinline__ float ld_absmax(const float* p, int64_t blk) {
+  typedef const __attribute__((address_space(4))) float c_f32_t;
+  return ((c_f32_t*)p)[blk];
+}
+
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 __device__ __forceinline__ uint32_t word_of(const uint4& q, int k) {
@@ -275,8 +287,8 @@ __device__ __forceinline__ void block_8bit_plain(const DevTensor& d, int64_t blk
   uint16_t* pp = d.param + e0;
   uint8_t* mp = static_cast<uint8_t*>(d.m) + e0;
   uint8_t* vp = static_cast<uint8_t*>(d.v) + e0;
-  const float am = d.amax_m[blk];
-  const float av = d.amax_v[blk];
+  const float am = ld_absmax(d.amax_m, blk);
+  const float av = ld_absmax(d.amax_v, blk);
   const bool nearest = sc.param_round != 0;
 
   float M2[kGroups * 8], V2[kGroups * 8];
@@ -418,8 +430,8 @@ __device__ __forceinline__ bool block_8bit_fast(const DevTensor& d, int64_t blk,
   uint16_t* pp = d.param + e0;
   uint8_t* mp = static_cast<uint8_t*>(d.m) + e0;
   uint8_t* vp = static_cast<uint8_t*>(d.v) + e0;
-  const float am = d.amax_m[blk];
-  const float av = d.amax_v[blk];
+  const float am = ld_absmax(d.amax_m, blk);
+  const float av = ld_absmax(d.amax_v, blk);
 
   uint4 G[kGroups], P[kGroups];
   uint2 QM[kGroups], QV[kGroups];
@@ -781,7 +793,7 @@ __device__ __forceinline__ void block_1s_8bit_plain(const DevTensor& d, int64_t 
   const uint16_t* gp = d.grad + e0;
   uint16_t* pp = d.param + e0;
   uint8_t* mp = static_cast<uint8_t*>(d.m) + e0;
-  const float am = d.amax_m[blk];
+  const float am = ld_absmax(d.amax_m, blk);
   const bool nearest = sc.param_round != 0;
   float M2[kGroups * 8];
   float mxm = 0.0f;
@@ -871,7 +883,7 @@ __device__ __forceinline__ bool block_1s_8bit_fast(const DevTensor& d, int64_t b
   const uint16_t* gp = d.grad + e0;
   uint16_t* pp = d.param + e0;
   uint8_t* mp = static_cast<uint8_t*>(d.m) + e0;
-  const float am = d.amax_m[blk];
+  const float am = ld_absmax(d.amax_m, blk);
   uint4 G[kGroups], P[kGroups];
   uint2 QM[kGroups];
 #pragma unroll
