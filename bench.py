@@ -140,7 +140,7 @@ def parse():
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build measures one GPU only; run with --gpus 1",
+        print(json.dumps({"error": "bench.py measures one GPU only; run with --gpus 1",
                           "n_gpus": args.gpus}))
         sys.exit(2)
 

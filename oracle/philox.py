@@ -26,7 +26,8 @@ index, stream) and never on a rank or a launch shape.
   streams: 0 = parameter, 1 = first moment, 2 = second moment.
 
 Parity: the generator is pinned against rocRAND's host-side Philox4x32-10
-(a library routine, test side only); the keying is this build's definition.
+(a library routine, test side only); the keying above is a definition of this
+library (the pages fix none).
 """
 
 import numpy as np
