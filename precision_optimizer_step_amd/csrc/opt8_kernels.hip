@@ -12,8 +12,9 @@
 // independent of order; no workgroup barrier is needed inside the block loop.
 //
 // The waves of a persistent grid stride over the blocks of the whole tensor
-// list (wave w takes blocks w, w + W, w + 2W, ... for W waves in the grid);
-// each workgroup stages the codebooks, midpoints and code LUTs in LDS once.
+// list (wave w takes blocks w, w + W, w + 2W, ... for W waves in the grid,
+// the waves numbered so that runs of 16 lie on one XCD); each workgroup
+// stages the codebooks, midpoints and code LUTs in LDS once.
 //
 // Arithmetic is the step exactly as the oracle states it: fp32, one rounding
 // per operation (built with -ffp-contract=off), IEEE sqrt and divide,
@@ -1080,8 +1081,9 @@ step_kernel(const DevTensor* __restrict__ list, int ntensors, int64_t total_bloc
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
   // workgroups are dispatched to the 8 XCDs round-robin (workgroup i on XCD
   // i mod 8); the waves are renumbered so that each run of 16 consecutive
-  // numbers (four workgroups) lies on one XCD, so the 16 blocks sharing a
-  // 64-byte line of absmax values are handled by one XCD's L2
+  // numbers (four workgroups) lies on one XCD, so 16 adjacent blocks, and
+  // with them most 64-byte lines of absmax values, go through one XCD's L2
+  // (any grid size that is a multiple of 32 keeps the numbering a bijection)
   int64_t gw = static_cast<int64_t>(blockIdx.x) * kWaves + wave;
   if ((gridDim.x & 31u) == 0) {
     const int64_t x = blockIdx.x & 7u, i = blockIdx.x >> 3;   // XCD, workgroup within it
