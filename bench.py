@@ -60,7 +60,7 @@ def probe_bandwidth(dev, words=1 << 27, reps=5):
     """Best GB/s of the streaming probe over three grid sizes: 1 read + 1 write stream, and
     3 read + 2 write streams (the 8-bit step's 6 B read : 4 B written per element); and of the
     probe with the 8-bit step's own access pattern (four read and three write streams in
-    2048-element blocks, one wave per block, no arithmetic)."""
+    2048-element blocks, no arithmetic), the best of one and two adjacent blocks per wave."""
     import ctypes
     import torch
     path = os.path.join(ROOT, "precision_optimizer_step_amd", "libopt8_probe.so")
@@ -92,28 +92,31 @@ def probe_bandwidth(dev, words=1 << 27, reps=5):
         res[name] = round(best, 1)
     del inp, out
     # the 8-bit step's own access pattern (10 B per element, no arithmetic)
-    lib.opt8_probe_pattern.argtypes = [ctypes.c_void_p] * 4 + [ctypes.c_int64, ctypes.c_int, ctypes.c_void_p]
+    lib.opt8_probe_pattern.argtypes = [ctypes.c_void_p] * 4 + [ctypes.c_int64, ctypes.c_int, ctypes.c_int,
+                                                                 ctypes.c_void_p]
     nblocks = 1 << 18
     n = nblocks * BLOCK
     g = torch.empty(n, dtype=torch.int16, device=dev).random_(-32768, 32767)
     p = torch.empty(n, dtype=torch.int16, device=dev).random_(-32768, 32767)
     m = torch.empty(n, dtype=torch.uint8, device=dev).random_(0, 255)
     v = torch.empty(n, dtype=torch.uint8, device=dev).random_(0, 255)
-    best = 0.0
-    for grid in (cus * 3, cus * 4, cus * 8):
-        def run():
-            assert lib.opt8_probe_pattern(g.data_ptr(), p.data_ptr(), m.data_ptr(), v.data_ptr(), nblocks,
-                                          grid, stream) == 0
-        run()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(reps):
+    for per_wave in (1, 2):
+        best = 0.0
+        for grid in (cus * 2, cus * 3, cus * 4, cus * 8):
+            def run():
+                assert lib.opt8_probe_pattern(g.data_ptr(), p.data_ptr(), m.data_ptr(), v.data_ptr(), nblocks,
+                                              grid, per_wave, stream) == 0
             run()
-        e1.record()
-        torch.cuda.synchronize()
-        best = max(best, 10 * n * reps / (e0.elapsed_time(e1) / 1000.0) / 1e9)
-    res["pattern_8bit"] = round(best, 1)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                run()
+            e1.record()
+            torch.cuda.synchronize()
+            best = max(best, 10 * n * reps / (e0.elapsed_time(e1) / 1000.0) / 1e9)
+        res[f"pattern_8bit_{per_wave}"] = round(best, 1)
+    res["pattern_8bit"] = max(res["pattern_8bit_1"], res["pattern_8bit_2"])
     del g, p, m, v
     torch.cuda.empty_cache()
     return res
@@ -333,7 +336,8 @@ def main():
                                                               / 1e9 / HBM_PEAK_GBPS, 2),
                    "attainable_copy_GBps": attain.get("copy"),
                    "attainable_3r2w_GBps": attain.get("mix"),
-                   "attainable_8bit_step_pattern_GBps": attain.get("pattern_8bit")},
+                   "attainable_8bit_step_pattern_GBps": attain.get("pattern_8bit"),
+                   "attainable_8bit_step_pattern_one_block_per_wave_GBps": attain.get("pattern_8bit_1")},
         "roofline": roof,
         "timing": {"median_ms": round(sorted(ev_ms)[len(ev_ms) // 2], 4), "min_ms": round(min(ev_ms), 4),
                    "max_ms": round(max(ev_ms), 4),

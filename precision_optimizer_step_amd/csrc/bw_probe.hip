@@ -44,37 +44,38 @@ typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(1))) u32x4 g_u32x4;
 typedef __attribute__((address_space(1))) u32x2 g_u32x2;
 
-// The 8-bit step's memory traffic without its arithmetic: one wave per
-// 2048-element block, lane l holding elements r*512 + 8l .. +7 (r = 0..3);
-// per block it reads 4 KiB of bf16 gradient, 4 KiB of bf16 parameter and
-// 2 KiB each of m and v codes, and writes the parameter and both code arrays
-// back (a xor of what it read), non-temporally, through the global address
-// space; waves stride over the blocks.
+// The 8-bit step's memory traffic without its arithmetic: lane l holding
+// elements r*512 + 8l .. +7 (r = 0..3) of a 2048-element block; per block it
+// reads 4 KiB of bf16 gradient, 4 KiB of bf16 parameter and 2 KiB each of m
+// and v codes, and writes the parameter and both code arrays back (a xor of
+// what it read), non-temporally, through the global address space.  Each wave
+// takes kB adjacent blocks per iteration (1 as the step kernel does; 2 moves
+// more bytes per wave and is faster without arithmetic) and the waves stride
+// over the blocks.
+template <int kB>
 __global__ void __launch_bounds__(kThreads)
 pattern_kernel(const uint16_t* __restrict__ g, uint16_t* __restrict__ p, uint8_t* __restrict__ m,
                uint8_t* __restrict__ v, int64_t nblocks) {
   const int lane = threadIdx.x & 63;
   const int64_t nw = static_cast<int64_t>(gridDim.x) * (kThreads / 64);
-  for (int64_t b = static_cast<int64_t>(blockIdx.x) * (kThreads / 64) + (threadIdx.x >> 6); b < nblocks;
-       b += nw) {
-    const int64_t e0 = b * 2048;
-    u32x4 G[4], P[4];
-    u32x2 M[4], V[4];
+  const int64_t w = static_cast<int64_t>(blockIdx.x) * (kThreads / 64) + (threadIdx.x >> 6);
+  for (int64_t b = w * kB; b + kB <= nblocks; b += nw * kB) {
+    u32x4 G[4 * kB], P[4 * kB];
+    u32x2 M[4 * kB], V[4 * kB];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int64_t e = e0 + r * 512 + lane * 8;
-      G[r] = __builtin_nontemporal_load((const g_u32x4*)(g + e));
-      M[r] = __builtin_nontemporal_load((const g_u32x2*)(m + e));
-      V[r] = __builtin_nontemporal_load((const g_u32x2*)(v + e));
+    for (int i = 0; i < 4 * kB; ++i) {
+      const int64_t e = (b + i / 4) * 2048 + (i % 4) * 512 + lane * 8;
+      G[i] = __builtin_nontemporal_load((const g_u32x4*)(g + e));
+      M[i] = __builtin_nontemporal_load((const g_u32x2*)(m + e));
+      V[i] = __builtin_nontemporal_load((const g_u32x2*)(v + e));
+      P[i] = __builtin_nontemporal_load((const g_u32x4*)(p + e));
     }
 #pragma unroll
-    for (int r = 0; r < 4; ++r) P[r] = __builtin_nontemporal_load((const g_u32x4*)(p + e0 + r * 512 + lane * 8));
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int64_t e = e0 + r * 512 + lane * 8;
-      __builtin_nontemporal_store(P[r] ^ G[r], (g_u32x4*)(p + e));
-      __builtin_nontemporal_store(M[r] ^ G[r].xy, (g_u32x2*)(m + e));
-      __builtin_nontemporal_store(V[r] ^ G[r].zw, (g_u32x2*)(v + e));
+    for (int i = 0; i < 4 * kB; ++i) {
+      const int64_t e = (b + i / 4) * 2048 + (i % 4) * 512 + lane * 8;
+      __builtin_nontemporal_store(P[i] ^ G[i], (g_u32x4*)(p + e));
+      __builtin_nontemporal_store(M[i] ^ G[i].xy, (g_u32x2*)(m + e));
+      __builtin_nontemporal_store(V[i] ^ G[i].zw, (g_u32x2*)(v + e));
     }
   }
 }
@@ -91,11 +92,19 @@ extern "C" int opt8_probe_stream(const void* in, void* out, int64_t words, int n
 }
 
 // g, p: bf16[nblocks * 2048]; m, v: u8[nblocks * 2048]; p, m and v are rewritten.
+// blocks_per_wave: 1 or 2 adjacent blocks per wave and iteration (nblocks must
+// then be a multiple of it).
 extern "C" int opt8_probe_pattern(const void* g, void* p, void* m, void* v, int64_t nblocks, int grid,
-                                  void* stream) {
+                                  int blocks_per_wave, void* stream) {
   if (!g || !p || !m || !v || nblocks <= 0 || grid < 1) return -1;
-  hipLaunchKernelGGL(pattern_kernel, dim3(grid), dim3(kThreads), 0, static_cast<hipStream_t>(stream),
-                     static_cast<const uint16_t*>(g), static_cast<uint16_t*>(p), static_cast<uint8_t*>(m),
-                     static_cast<uint8_t*>(v), nblocks);
+  if (blocks_per_wave != 1 && blocks_per_wave != 2) return -1;
+  if (nblocks % blocks_per_wave) return -1;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  if (blocks_per_wave == 1)
+    hipLaunchKernelGGL(pattern_kernel<1>, dim3(grid), dim3(kThreads), 0, st, static_cast<const uint16_t*>(g),
+                       static_cast<uint16_t*>(p), static_cast<uint8_t*>(m), static_cast<uint8_t*>(v), nblocks);
+  else
+    hipLaunchKernelGGL(pattern_kernel<2>, dim3(grid), dim3(kThreads), 0, st, static_cast<const uint16_t*>(g),
+                       static_cast<uint16_t*>(p), static_cast<uint8_t*>(m), static_cast<uint8_t*>(v), nblocks);
   return hipGetLastError() == hipSuccess ? 0 : -9;
 }
