@@ -132,7 +132,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--round", choices=("stochastic", "nearest"), default="stochastic",
                     help="parameter rounding (nearest: the deterministic baseline, for the SR overhead)")
-    ap.add_argument("--cpu-sample-elems", type=int, default=96 * 1024 * 1024)
+    ap.add_argument("--cpu-sample-elems", type=int, default=128 * 1024 * 1024)
     ap.add_argument("--algo", choices=("adamw", "lion", "momentum"), default="adamw",
                     help="update rule (lion / momentum: one 8-bit state, the same machinery)")
     ap.add_argument("--state-round", choices=("nearest", "stochastic"), default="nearest",

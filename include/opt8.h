@@ -78,7 +78,7 @@ typedef enum {
   OPT8_OK = 0,
   OPT8_E_NULL = -1,      /* a required pointer is NULL                               */
   OPT8_E_ALIGN = -2,     /* param/grad/m/v not 16-byte aligned, absmax not 4-byte    */
-  OPT8_E_SIZE = -3,      /* n < 0, numel <= 0, bad index_base, size overflow         */
+  OPT8_E_SIZE = -3,      /* n < 0, numel <= 0 or > 2^42, bad index_base              */
   OPT8_E_MODE = -4,      /* unknown state mode, rounding mode or state rounding      */
   OPT8_E_HPARAM = -5,    /* lr/betas/eps/weight_decay/step outside their ranges      */
   OPT8_E_ALIAS = -6,     /* two buffers of the list overlap                          */
@@ -115,9 +115,11 @@ typedef struct opt8_tensor {
   void* v;                /*   second moment likewise; in/out, 16-byte aligned         */
   float* absmax_m;        /* f32[ceil(numel/2048)], in/out, 8-bit mode only (else     */
   float* absmax_v;        /*   ignored and may be NULL); 4-byte aligned               */
-  int64_t numel;          /* > 0                                                       */
+  int64_t numel;          /* > 0 and <= 2^42                                           */
   int64_t index_base;     /* global index of element 0 in the unsharded tensor (RNG   */
-                          /*   counter); >= 0 and a multiple of 2048; 0 if unsharded  */
+                          /*   counter); >= 0, <= 2^60 and a multiple of 2048 (so     */
+                          /*   hi32(j/8) < 2^30 stays clear of the stream bits); 0 if */
+                          /*   unsharded                                              */
   uint32_t tensor_id;     /* RNG stream id; unique in the list, stable over steps     */
   int32_t mode;           /* opt8_state_mode                                           */
 } opt8_tensor;

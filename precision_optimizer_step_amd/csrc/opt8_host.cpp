@@ -289,7 +289,9 @@ int validate_tensors(const opt8_tensor* t, int32_t n, bool two_state) {
       return fail(OPT8_E_NULL, two_state ? "tensor %d: 8-bit mode needs absmax_m/absmax_v"
                                          : "tensor %d: 8-bit mode needs absmax_m", i);
     if (x.numel <= 0) return fail(OPT8_E_SIZE, "tensor %d: numel must be > 0", i);
-    if (x.numel > (int64_t(1) << 46)) return fail(OPT8_E_SIZE, "tensor %d: numel too large", i);
+    // the kernels hold a tensor's block count in 32 bits: at most 2^42 elements (2^31 blocks)
+    if (x.numel > (int64_t(1) << 42))
+      return fail(OPT8_E_SIZE, "tensor %d: numel %lld exceeds 2^42", i, static_cast<long long>(x.numel));
     if (x.index_base < 0 || x.index_base % kBlock != 0 || x.index_base > (int64_t(1) << 60))
       return fail(OPT8_E_SIZE, "tensor %d: index_base must be >= 0 and a multiple of 2048", i);
     auto al = [](const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; };

@@ -127,6 +127,11 @@ def test_null_and_size_errors(L):
     expect(step([fake_tensor(0), fake_tensor(1, absmax_v=None)]), opt8.OPT8_E_NULL, "tensor 1")
     expect(step([fake_tensor(0, numel=0)]), opt8.OPT8_E_SIZE)
     expect(step([fake_tensor(0, numel=-5)]), opt8.OPT8_E_SIZE)
+    expect(step([fake_tensor(0, numel=(1 << 42) + 1)]), opt8.OPT8_E_SIZE, "2^42")
+    # at the bound the size check passes and validation goes on (to the missing device / init)
+    rc = step([fake_tensor(0, numel=1 << 42, param=1 << 50, grad=2 << 50, m=3 << 50, v=4 << 50,
+                           absmax_m=5 << 50, absmax_v=6 << 50)])
+    assert rc in (opt8.OPT8_E_HIP, opt8.OPT8_E_NOT_INIT), opt8.opt8_last_error()
     expect(step([fake_tensor(0, index_base=1024)]), opt8.OPT8_E_SIZE, "index_base")
     expect(step([fake_tensor(0, index_base=-2048)]), opt8.OPT8_E_SIZE)
 
