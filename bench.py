@@ -273,7 +273,7 @@ def main():
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": int(traffic) if traffic else None,
                 "valu_issue_frac": profiled_traffic(kname, w.name, "valu_issue_frac"),
-                # rocprofv3's VALU-busy figure (SQ_ACTIVE_INST_VALU x 4 / SIMDs / cycles) of this build
+                # rocprofv3's VALU-busy figure (SQ_ACTIVE_INST_VALU x 4 / SIMDs / cycles), from the profile of the same kernel fingerprint
                 "valu_busy": profiled_traffic(kname, w.name, "valu_busy"),
                 "frac_of_attainable": None,
                 "kernel": kname,
