@@ -97,3 +97,50 @@ def test_more_lists_than_cached_slots():
                 states[k] = want
     log(f"descriptor cache: mismatches {sum(stats.values())}")
     assert sum(stats.values()) == 0
+
+
+def test_concurrent_host_threads():
+    """Two host threads, each with its own stream and three lists of its own (six lists, the
+    cache holds four), launch four rounds of steps with no host synchronisation until both
+    have finished: the calls share the device's descriptor cache (evicting each other's lists)
+    and must still give each list the oracle's result."""
+    import threading
+
+    rng = np.random.default_rng(9)
+    groups = []
+    for th in range(2):
+        lists = []
+        for li in range(3):
+            items = [_make(rng, 2048 * (2 + li) + 501 * th + 13, 300 + 20 * (3 * th + li) + k, 30 + li)
+                     for k in range(2)]
+            lists.append(([x[0] for x in items], [x[1] for x in items]))
+        groups.append(lists)
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    torch.cuda.synchronize()
+    errors = []
+
+    def worker(th):
+        try:
+            for rnd in range(4):
+                for sets, _ in groups[th]:
+                    _launch(sets, _hp(rnd + 1), streams[th])
+        except Exception as e:   # re-raised in the main thread
+            errors.append(e)
+
+    threads = [threading.Thread(target=worker, args=(th,)) for th in range(2)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    torch.cuda.synchronize()
+    assert not errors, errors
+    stats = {}
+    for th, lists in enumerate(groups):
+        for li, (sets, states) in enumerate(lists):
+            for s, st in zip(sets, states):
+                want = st
+                for rnd in range(4):
+                    want = oracle_step(s, want, _hp(rnd + 1))
+                compare_state(f"thread {th} list {li}/t{s.tensor_id}", s.read(), want, M8, stats)
+    log(f"concurrent host threads: mismatches {sum(stats.values())}")
+    assert sum(stats.values()) == 0
