@@ -84,7 +84,8 @@ typedef enum {
   OPT8_E_ALIAS = -6,     /* two buffers of the list overlap                          */
   OPT8_E_DUPID = -7,     /* tensor_id repeated in one list                           */
   OPT8_E_NOT_INIT = -8,  /* opt8_init_codebooks not called on the current device     */
-  OPT8_E_HIP = -9        /* a HIP runtime call or a kernel launch failed             */
+  OPT8_E_HIP = -9,       /* a HIP runtime call or a kernel launch failed             */
+  OPT8_E_CAPTURE = -10   /* hip_stream is being captured into a graph (see below)    */
 } opt8_status;
 
 typedef enum {
@@ -154,7 +155,10 @@ int32_t opt8_default_mode(int64_t numel);
  * nothing is queued and nothing is modified.  n == 0 is a no-op.  Tensors of
  * different modes may be mixed.  Concurrent calls on different streams must
  * use disjoint buffers.  Device faults surface at the caller's next
- * synchronisation.  Returns OPT8_OK or a negative opt8_status.              */
+ * synchronisation.  A stream that is being captured into a HIP graph is
+ * refused with OPT8_E_CAPTURE before anything is queued: a step may upload
+ * its descriptor list into a cache slot that later calls reuse, which a
+ * graph replay would not follow.  Returns OPT8_OK or a negative opt8_status. */
 int opt8_adamw_step(const opt8_tensor* tensors, int32_t n, const opt8_hparams* hp,
                     void* hip_stream);
 

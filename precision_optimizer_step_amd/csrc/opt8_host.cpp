@@ -492,6 +492,14 @@ int run_step(int algo, const opt8_tensor* tensors, int32_t n, const opt8_hparams
   if (rc != OPT8_OK) return rc;
   DeviceState& ds = g_dev[dev];
   if (!ds.init) return fail(OPT8_E_NOT_INIT, "opt8_init_codebooks has not run on device %d", dev);
+  const hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+  // a graph replay would repeat the launches but not the descriptor upload or the cache
+  // bookkeeping, and a later call may rewrite the slot the graph's kernels read
+  hipStreamCaptureStatus capture = hipStreamCaptureStatusNone;
+  const hipError_t ce = hipStreamIsCapturing(stream, &capture);
+  if (ce != hipSuccess) return hip_fail(ce, "hipStreamIsCapturing");
+  if (capture != hipStreamCaptureStatusNone)
+    return fail(OPT8_E_CAPTURE, "hip_stream is being captured into a graph; the step cannot be captured");
 
   // one sub-list per kernel, each with its own block numbering: full blocks of
   // 8-bit tensors, bf16-state tensors, fp32-state tensors, and the partial last
@@ -528,7 +536,6 @@ int run_step(int algo, const opt8_tensor* tensors, int32_t n, const opt8_hparams
       list.push_back(d);
     }
   }
-  const hipStream_t stream = static_cast<hipStream_t>(hip_stream);
   Slot* slot = nullptr;
   rc = acquire_slot(ds, list, stream, slot);
   if (rc != OPT8_OK) return rc;

@@ -73,6 +73,30 @@ def test_struct_layout_matches_header(tmp_path):
         assert getattr(cls, name).offset == int(off), name
 
 
+def test_constants_match_header(tmp_path):
+    """Every enum constant and macro of the header has the binding's value."""
+    if shutil.which("gcc") is None:
+        pytest.skip("gcc not available")
+    text = open(HEADER).read()
+    names = sorted(set(re.findall(r"\b(OPT8_[A-Z0-9_]+)\s*=", text)) |
+                   set(re.findall(r"#define\s+(OPT8_[A-Z0-9_]+)\s+\d", text)))
+    assert "OPT8_E_CAPTURE" in names and "OPT8_BLOCK" in names
+    src = tmp_path / "consts.c"
+    lines = ['#include <stdio.h>', f'#include "{HEADER}"', "int main(void){"]
+    lines += [f'printf("{n} %ld\\n", (long){n});' for n in names]
+    lines.append("return 0;}")
+    src.write_text("\n".join(lines))
+    exe = tmp_path / "consts"
+    subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", str(src), "-o", str(exe)], check=True)
+    out = subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split()
+    got = dict(zip(out[0::2], (int(x) for x in out[1::2])))
+    assert len(got) == len(names)
+    for n, val in got.items():
+        assert getattr(opt8, n) == val, n
+    for val in (v for n, v in got.items() if n.startswith("OPT8_E_")):
+        assert val in opt8.STATUS_NAMES
+
+
 def test_default_mode_threshold(L):
     assert opt8.opt8_default_mode(1) == opt8.OPT8_STATE_FP32
     assert opt8.opt8_default_mode(4095) == opt8.OPT8_STATE_FP32

@@ -144,3 +144,40 @@ def test_concurrent_host_threads():
                 compare_state(f"thread {th} list {li}/t{s.tensor_id}", s.read(), want, M8, stats)
     log(f"concurrent host threads: mismatches {sum(stats.values())}")
     assert sum(stats.values()) == 0
+
+
+def test_graph_capture_is_refused():
+    """A step called on a stream that is being captured into a HIP graph returns
+    OPT8_E_CAPTURE before anything is queued (the capture ends empty and nothing changes);
+    the same step called eagerly afterwards gives the oracle's result."""
+    import ctypes
+
+    hip = ctypes.CDLL("libamdhip64.so")
+    hip.hipStreamBeginCapture.argtypes = [ctypes.c_void_p, ctypes.c_int]
+    hip.hipStreamEndCapture.argtypes = [ctypes.c_void_p, ctypes.POINTER(ctypes.c_void_p)]
+    hip.hipGraphDestroy.argtypes = [ctypes.c_void_p]
+    rng = np.random.default_rng(11)
+    s, st = _make(rng, 2048 * 2 + 5, 900, 12)
+    hp = _hp(1)
+    side = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    relaxed = 2   # hipStreamCaptureModeRelaxed
+    assert hip.hipStreamBeginCapture(side.cuda_stream, relaxed) == 0
+    rc = opt8.opt8_adamw_step([s.desc()], opt8.make_hparams(hp.lr, hp.beta1, hp.beta2, hp.eps,
+                                                             hp.weight_decay, hp.step, hp.seed),
+                              stream=side, check=False)
+    msg = opt8.opt8_last_error()
+    graph = ctypes.c_void_p()
+    assert hip.hipStreamEndCapture(side.cuda_stream, ctypes.byref(graph)) == 0
+    if graph.value:
+        assert hip.hipGraphDestroy(graph) == 0
+    assert rc == opt8.OPT8_E_CAPTURE, (rc, msg)
+    assert "captured" in msg, msg
+    torch.cuda.synchronize()
+    for got, want in zip(s.read(), st):
+        assert np.array_equal(got, want), "a refused step must leave every buffer unchanged"
+    _launch([s], hp, None)
+    torch.cuda.synchronize()
+    stats = {}
+    compare_state("after a refused capture", s.read(), oracle_step(s, st, hp), M8, stats)
+    assert sum(stats.values()) == 0
