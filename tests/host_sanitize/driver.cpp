@@ -1,0 +1,267 @@
+// Drives libopt8's host code (linked with the host-only HIP stand-in) through
+// its tables, every validation error, capture refusal, launch planning, the
+// scalar prologue and the descriptor cache.  Built with AddressSanitizer and
+// UBSan by tests/test_host_sanitizers.py; prints "all host checks passed".
+#include <cmath>
+#include <cstdint>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <vector>
+
+#include "fake_hip.h"
+#include "opt8.h"
+
+using fake::g;
+
+static int failures = 0;
+#define CHECK(cond)                                                      \
+  do {                                                                   \
+    if (!(cond)) {                                                       \
+      std::printf("FAILED line %d: %s (%s)\n", __LINE__, #cond, opt8_last_error()); \
+      ++failures;                                                        \
+    }                                                                    \
+  } while (0)
+
+// Fake device addresses: tensor i owns a 2 GiB window, its six buffers 256 MiB apart
+static uintptr_t base_of(int i, int k) { return (uintptr_t(1) << 40) + (uintptr_t(i) << 31) + (uintptr_t(k) << 28); }
+
+static opt8_tensor tensor(int i, int64_t numel, int mode, uint32_t id) {
+  opt8_tensor t;
+  std::memset(&t, 0, sizeof t);
+  t.param = reinterpret_cast<uint16_t*>(base_of(i, 0));
+  t.grad = reinterpret_cast<const uint16_t*>(base_of(i, 1));
+  t.m = reinterpret_cast<void*>(base_of(i, 2));
+  t.v = reinterpret_cast<void*>(base_of(i, 3));
+  t.absmax_m = mode == OPT8_STATE_8BIT ? reinterpret_cast<float*>(base_of(i, 4)) : nullptr;
+  t.absmax_v = mode == OPT8_STATE_8BIT ? reinterpret_cast<float*>(base_of(i, 5)) : nullptr;
+  t.numel = numel;
+  t.index_base = 0;
+  t.tensor_id = id;
+  t.mode = mode;
+  return t;
+}
+
+static opt8_hparams hparams(int64_t step) {
+  opt8_hparams h;
+  std::memset(&h, 0, sizeof h);
+  h.lr = 1e-3;
+  h.beta1 = 0.9;
+  h.beta2 = 0.999;
+  h.eps = 1e-8;
+  h.weight_decay = 0.01;
+  h.step = step;
+  h.seed = 0x0123456789ABCDEFull;
+  return h;
+}
+
+// The scalar prologue as defined: beta^t by t - 1 repeated double
+// multiplications, each derived scalar rounded once to fp32.
+static void expect_scalars(const opt8::StepScalars& s, const opt8_hparams& h, bool adamw) {
+  double p1 = 1.0, p2 = 1.0;
+  if (adamw) {
+    p1 = h.beta1;
+    p2 = h.beta2;
+    // once 1 - p is exactly 1.0 for both, every later (smaller) power leaves it there
+    for (int64_t k = 1; k < h.step && !(1.0 - p1 == 1.0 && 1.0 - p2 == 1.0); ++k) {
+      p1 *= h.beta1;
+      p2 *= h.beta2;
+    }
+  } else {
+    p1 = p2 = 0.0;
+  }
+  CHECK(s.beta1 == static_cast<float>(h.beta1));
+  CHECK(s.beta2 == static_cast<float>(h.beta2));
+  CHECK(s.w1 == static_cast<float>(1.0 - h.beta1));
+  CHECK(s.w2 == static_cast<float>(1.0 - h.beta2));
+  CHECK(s.eps == static_cast<float>(h.eps));
+  CHECK(s.step_size == static_cast<float>(h.lr / (1.0 - p1)));
+  CHECK(s.rbc2 == static_cast<float>(1.0 / std::sqrt(1.0 - p2)));
+  CHECK(s.lrwd == static_cast<float>(h.lr * h.weight_decay));
+  CHECK(s.seed_lo == static_cast<uint32_t>(h.seed) && s.seed_hi == static_cast<uint32_t>(h.seed >> 32));
+  CHECK(s.step_lo == static_cast<uint32_t>(h.step));
+  CHECK(s.param_round == h.param_round && s.state_round == h.state_round);
+}
+
+static int step(const std::vector<opt8_tensor>& ts, const opt8_hparams& h, void* stream = nullptr) {
+  return opt8_adamw_step(ts.data(), static_cast<int32_t>(ts.size()), &h, stream);
+}
+
+int main() {
+  // ---------------------------------------------------------------- tables
+  g.have_device = false;
+  float cs[256], cu[256];
+  CHECK(opt8_init_codebooks(cs, cu) == OPT8_E_HIP);   // tables still copied out
+  CHECK(cs[0] == -1.0f && cs[127] == 0.0f && cs[255] == 1.0f);
+  CHECK(cu[0] == 0.0f && cu[255] == 1.0f);
+  for (int k = 1; k < 256; ++k) CHECK(cs[k - 1] < cs[k] && cu[k - 1] < cu[k]);
+  const opt8_hparams h1 = hparams(1);
+  std::vector<opt8_tensor> one = {tensor(0, 5000, OPT8_STATE_8BIT, 0)};
+  CHECK(step(one, h1) == OPT8_E_HIP);                  // no device
+  g.have_device = true;
+  CHECK(step(one, h1) == OPT8_E_NOT_INIT);
+  CHECK(opt8_init_codebooks(nullptr, nullptr) == OPT8_OK);
+  CHECK(opt8_init_codebooks(cs, cu) == OPT8_OK);       // idempotent: uploaded once
+  CHECK(g.table_uploads == 1);
+  g.device = 1;
+  CHECK(step(one, h1) == OPT8_E_NOT_INIT);             // another device needs its own init
+  g.device = 0;
+
+  // ---------------------------------------------------------------- validation
+  CHECK(opt8_adamw_step(one.data(), 1, nullptr, nullptr) == OPT8_E_NULL);
+  CHECK(opt8_adamw_step(nullptr, 1, &h1, nullptr) == OPT8_E_NULL);
+  CHECK(opt8_adamw_step(one.data(), -1, &h1, nullptr) == OPT8_E_SIZE);
+  CHECK(opt8_adamw_step(nullptr, 0, &h1, nullptr) == OPT8_OK);
+  auto bad = [&](void (*edit)(opt8_tensor&), int want) {
+    std::vector<opt8_tensor> ts = {tensor(0, 5000, OPT8_STATE_8BIT, 0), tensor(1, 3000, OPT8_STATE_BF16_SR, 1)};
+    edit(ts[1]);
+    const size_t before = g.launches.size();
+    CHECK(step(ts, h1) == want);
+    CHECK(g.launches.size() == before);                // nothing queued on an error
+  };
+  bad([](opt8_tensor& t) { t.param = nullptr; }, OPT8_E_NULL);
+  bad([](opt8_tensor& t) { t.v = nullptr; }, OPT8_E_NULL);
+  bad([](opt8_tensor& t) { t.mode = OPT8_STATE_8BIT; }, OPT8_E_NULL);          // no absmax arrays
+  bad([](opt8_tensor& t) { t.grad = reinterpret_cast<const uint16_t*>(reinterpret_cast<uintptr_t>(t.grad) + 8); }, OPT8_E_ALIGN);
+  bad([](opt8_tensor& t) { t.numel = 0; }, OPT8_E_SIZE);
+  bad([](opt8_tensor& t) { t.numel = (int64_t(1) << 42) + 1; }, OPT8_E_SIZE);
+  bad([](opt8_tensor& t) { t.index_base = 1024; }, OPT8_E_SIZE);
+  bad([](opt8_tensor& t) { t.index_base = (int64_t(1) << 60) + 2048; }, OPT8_E_SIZE);
+  bad([](opt8_tensor& t) { t.mode = 7; }, OPT8_E_MODE);
+  bad([](opt8_tensor& t) { t.tensor_id = 0; }, OPT8_E_DUPID);
+  bad([](opt8_tensor& t) { t.m = reinterpret_cast<void*>(base_of(0, 0) + 4096); }, OPT8_E_ALIAS);
+  {
+    std::vector<opt8_tensor> ts = {tensor(0, 5000, OPT8_STATE_8BIT, 0)};
+    opt8_hparams h = h1;
+    const double nan = std::nan("");
+    struct { double opt8_hparams::*f; double v; } cases[] = {
+        {&opt8_hparams::lr, -1.0}, {&opt8_hparams::lr, nan}, {&opt8_hparams::beta1, 1.0},
+        {&opt8_hparams::beta2, -0.1}, {&opt8_hparams::eps, 0.0}, {&opt8_hparams::weight_decay, -1.0},
+        {&opt8_hparams::weight_decay, INFINITY}};
+    for (auto& c : cases) {
+      h = h1;
+      h.*(c.f) = c.v;
+      CHECK(step(ts, h) == OPT8_E_HPARAM);
+    }
+    h = h1;
+    h.step = 0;
+    CHECK(step(ts, h) == OPT8_E_HPARAM);
+    h = h1;
+    h.param_round = 5;
+    CHECK(step(ts, h) == OPT8_E_MODE);
+    h = h1;
+    h.state_round = 3;
+    CHECK(step(ts, h) == OPT8_E_MODE);
+  }
+
+  // ---------------------------------------------------------------- capture refusal
+  g.capturing = true;
+  {
+    const size_t before = g.launches.size();
+    const long up = g.uploads;
+    CHECK(step(one, h1) == OPT8_E_CAPTURE);
+    CHECK(g.launches.size() == before && g.uploads == up);
+  }
+  g.capturing = false;
+
+  // ---------------------------------------------------------------- launch planning
+  std::vector<opt8_tensor> mixed = {
+      tensor(0, 100, OPT8_STATE_FP32, 10),  tensor(1, 4096, OPT8_STATE_8BIT, 11),
+      tensor(2, 5000, OPT8_STATE_8BIT, 12), tensor(3, 3 * 2048, OPT8_STATE_8BIT, 13),
+      tensor(4, 7, OPT8_STATE_BF16_SR, 14), tensor(5, 3000, OPT8_STATE_BF16_SR, 15),
+      tensor(6, 2047, OPT8_STATE_8BIT, 16)};
+  g.launches.clear();
+  CHECK(step(mixed, h1) == OPT8_OK);
+  CHECK(g.launches.size() == 4);
+  if (g.launches.size() == 4) {
+    const fake::Launch& a = g.launches[0];   // full 8-bit blocks: 2 + 2 + 3
+    CHECK(a.kind == 0 && a.n == 3 && a.total_blocks == 7 && a.ok);
+    const fake::Launch& b = g.launches[1];   // bf16 state: 1 + 2 blocks
+    CHECK(b.kind == 1 && b.n == 2 && b.total_blocks == 3 && b.ok);
+    const fake::Launch& c = g.launches[2];   // fp32 state
+    CHECK(c.kind == 2 && c.n == 1 && c.total_blocks == 1 && c.ok);
+    const fake::Launch& d = g.launches[3];   // partial last blocks of 5000 and 2047
+    CHECK(d.kind == 3 && d.n == 2 && d.total_blocks == 2 && d.ok);
+    for (const auto& L : g.launches) CHECK(L.grid_cap == 256 * 3 && L.algo == 0);
+    expect_scalars(a.sc, h1, true);
+  }
+
+  // ---------------------------------------------------------------- scalar prologue
+  {
+    const int64_t steps[] = {1, 2, 3, 10, 1000, 5, 200000, 1, (int64_t(1) << 32) + 7};
+    for (int64_t t : steps) {
+      g.launches.clear();
+      const opt8_hparams h = hparams(t);
+      CHECK(step(one, h) == OPT8_OK);
+      if (!g.launches.empty()) expect_scalars(g.launches[0].sc, h, true);
+    }
+    opt8_hparams h = hparams(3);
+    h.beta1 = 0.5;
+    h.beta2 = 0.25;
+    h.param_round = OPT8_ROUND_NEAREST;
+    h.state_round = OPT8_STATE_ROUND_STOCHASTIC;
+    g.launches.clear();
+    CHECK(step(one, h) == OPT8_OK);
+    if (!g.launches.empty()) expect_scalars(g.launches[0].sc, h, true);
+    g.launches.clear();
+    CHECK(opt8_lion_step(one.data(), 1, &h, nullptr) == OPT8_OK);
+    if (!g.launches.empty()) {
+      expect_scalars(g.launches[0].sc, h, false);
+      CHECK(g.launches[0].algo == 1);
+    }
+  }
+
+  // ---------------------------------------------------------------- descriptor cache
+  {
+    std::vector<std::vector<opt8_tensor>> lists;
+    for (int l = 0; l < 6; ++l)
+      lists.push_back({tensor(20 + 2 * l, 4096 + 64 * l, OPT8_STATE_8BIT, 0),
+                       tensor(21 + 2 * l, 9000, OPT8_STATE_BF16_SR, 1)});
+    for (int round = 0; round < 3; ++round)
+      for (auto& L : lists) {
+        const long up = g.uploads;
+        CHECK(step(L, h1) == OPT8_OK);
+        CHECK(g.uploads == up + 1);           // six lists round-robin through four slots: always a miss
+        const long up2 = g.uploads;
+        CHECK(step(L, h1) == OPT8_OK);
+        CHECK(g.uploads == up2);              // the same list again: reused, no upload
+      }
+    CHECK(g.event_syncs > 0);                 // evictions waited for the last reader
+    const long waits = g.stream_waits;
+    void* other = reinterpret_cast<void*>(uintptr_t(0x1000));
+    CHECK(step(lists[5], h1, other) == OPT8_OK);
+    CHECK(g.stream_waits == waits + 1);       // moved to another stream: ordered after the last launch
+    CHECK(step(lists[5], h1, other) == OPT8_OK);
+    CHECK(g.stream_waits == waits + 1);
+
+    // a list longer than any slot holds: the slot grows
+    std::vector<opt8_tensor> big;
+    for (int i = 0; i < 1000; ++i) big.push_back(tensor(100 + i, 2048 + i, OPT8_STATE_8BIT, static_cast<uint32_t>(i)));
+    const long mallocs = g.mallocs;
+    g.launches.clear();
+    CHECK(step(big, h1) == OPT8_OK);
+    CHECK(g.mallocs > mallocs);
+    CHECK(g.launches.size() == 2 && g.launches[0].n == 1000 && g.launches[0].ok);
+    if (g.launches.size() == 2) CHECK(g.launches[1].kind == 3 && g.launches[1].n == 999);
+    // an overlap far down a long list is found
+    big[999].grad = reinterpret_cast<const uint16_t*>(base_of(100 + 500, 1) + 1024);
+    CHECK(step(big, h1) == OPT8_E_ALIAS);
+    big[999] = tensor(100 + 999, 2048 + 999, OPT8_STATE_8BIT, 999);
+
+    // an allocation failure is reported and leaves the cache usable
+    std::vector<opt8_tensor> huge;
+    for (int i = 0; i < 3000; ++i) huge.push_back(tensor(2000 + i, 4096, OPT8_STATE_8BIT, static_cast<uint32_t>(i)));
+    g.fail_malloc = true;
+    CHECK(step(huge, h1) == OPT8_E_HIP);
+    g.fail_malloc = false;
+    for (auto& L : lists) CHECK(step(L, h1) == OPT8_OK);
+    CHECK(step(huge, h1) == OPT8_OK);
+  }
+
+  if (failures) {
+    std::printf("%d host checks failed\n", failures);
+    return 1;
+  }
+  std::printf("all host checks passed\n");
+  return 0;
+}

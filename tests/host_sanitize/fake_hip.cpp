@@ -1,0 +1,134 @@
+// A host-only stand-in for the HIP runtime calls and the kernel-side functions
+// that opt8_host.cpp uses, so the library's host code (codebook and LUT
+// construction, validation, the per-device descriptor cache, the scalar
+// prologue, launch planning) can run under AddressSanitizer and UBSan on a
+// machine without a GPU.  "Device" memory is host memory; launches are
+// recorded and their descriptor lists checked the way the kernels walk them.
+#include <cstdint>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <vector>
+
+#include "fake_hip.h"
+
+namespace fake {
+State g;
+}
+
+using fake::g;
+
+extern "C" {
+
+hipError_t hipGetDevice(int* device) {
+  if (!g.have_device) return hipErrorNoDevice;
+  *device = g.device;
+  return hipSuccess;
+}
+
+hipError_t hipDeviceGetAttribute(int* value, hipDeviceAttribute_t, int) {
+  *value = 256;
+  return hipSuccess;
+}
+
+hipError_t hipDeviceSynchronize(void) { return hipSuccess; }
+
+hipError_t hipEventCreateWithFlags(hipEvent_t* event, unsigned) {
+  *event = reinterpret_cast<hipEvent_t>(new int(0));
+  ++g.events;
+  return hipSuccess;
+}
+
+hipError_t hipEventRecord(hipEvent_t event, hipStream_t) {
+  ++*reinterpret_cast<int*>(event);
+  return hipSuccess;
+}
+
+hipError_t hipEventSynchronize(hipEvent_t event) {
+  (void)*reinterpret_cast<int*>(event);
+  ++g.event_syncs;
+  return hipSuccess;
+}
+
+hipError_t hipStreamWaitEvent(hipStream_t, hipEvent_t event, unsigned) {
+  (void)*reinterpret_cast<int*>(event);
+  ++g.stream_waits;
+  return hipSuccess;
+}
+
+hipError_t hipStreamIsCapturing(hipStream_t, hipStreamCaptureStatus* status) {
+  *status = g.capturing ? hipStreamCaptureStatusActive : hipStreamCaptureStatusNone;
+  return hipSuccess;
+}
+
+hipError_t hipMalloc(void** ptr, size_t size) {
+  if (g.fail_malloc) return hipErrorOutOfMemory;
+  *ptr = std::malloc(size);
+  ++g.mallocs;
+  return hipSuccess;
+}
+
+hipError_t hipFree(void* ptr) {
+  std::free(ptr);
+  ++g.frees;
+  return hipSuccess;
+}
+
+hipError_t hipHostMalloc(void** ptr, size_t size, unsigned) {
+  *ptr = std::malloc(size);
+  return hipSuccess;
+}
+
+hipError_t hipHostFree(void* ptr) {
+  std::free(ptr);
+  return hipSuccess;
+}
+
+hipError_t hipMemcpyAsync(void* dst, const void* src, size_t bytes, hipMemcpyKind, hipStream_t) {
+  std::memcpy(dst, src, bytes);
+  ++g.uploads;
+  return hipSuccess;
+}
+
+const char* hipGetErrorString(hipError_t) { return "error from the host-only HIP stand-in"; }
+
+}  // extern "C"
+
+namespace opt8 {
+
+hipError_t upload_tables(const uint8_t* host_tables) {
+  // read every byte of the image the kernels would stage (ASan checks the extent)
+  uint32_t sum = 0;
+  for (int i = 0; i < kTableBytesSR; ++i) sum += host_tables[i];
+  g.table_sum = sum;
+  ++g.table_uploads;
+  return hipSuccess;
+}
+
+hipError_t launch_step(Kind kind, int algo, const DevTensor* list, int n, int64_t total_blocks,
+                       const StepScalars& sc, hipStream_t, int grid_cap) {
+  fake::Launch L;
+  L.kind = static_cast<int>(kind);
+  L.algo = algo;
+  L.n = n;
+  L.total_blocks = total_blocks;
+  L.sc = sc;
+  L.grid_cap = grid_cap;
+  // the kernels find a block's tensor from block_begin and walk nblocks: the
+  // numbering must be a gap-free prefix sum ending at total_blocks
+  int64_t b = 0;
+  for (int i = 0; i < n; ++i) {
+    if (list[i].block_begin != b) L.ok = false;
+    if (list[i].nblocks == 0) L.ok = false;
+    b += list[i].nblocks;
+    L.numel += list[i].numel;
+    L.ids.push_back(list[i].tensor_id);
+  }
+  if (b != total_blocks) L.ok = false;
+  g.launches.push_back(L);
+  return hipSuccess;
+}
+
+int occupancy_per_cu(Kind, int, bool) { return 3; }
+
+}  // namespace opt8

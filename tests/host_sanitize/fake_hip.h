@@ -1,0 +1,32 @@
+// State of the host-only HIP stand-in (fake_hip.cpp), read by the driver.
+#pragma once
+
+#include <cstdint>
+#include <vector>
+
+#include "opt8_internal.h"
+
+namespace fake {
+
+struct Launch {
+  int kind = 0, algo = 0, n = 0, grid_cap = 0;
+  int64_t total_blocks = 0, numel = 0;
+  opt8::StepScalars sc{};
+  std::vector<uint32_t> ids;
+  bool ok = true;
+};
+
+struct State {
+  bool have_device = true;
+  int device = 0;
+  bool capturing = false;
+  bool fail_malloc = false;
+  long mallocs = 0, frees = 0, uploads = 0, events = 0, event_syncs = 0, stream_waits = 0;
+  long table_uploads = 0;
+  uint32_t table_sum = 0;
+  std::vector<Launch> launches;
+};
+
+extern State g;
+
+}  // namespace fake
