@@ -119,6 +119,24 @@ __device__ __forceinline__ void state_bits(uint64_t grp, uint32_t tensor_id, con
   rv = Rand4{{c0[1], c1[1], c2[1], c3[1]}};
 }
 
+// Random words of the parameter, first and second moment (streams 0, 1, 2) of
+// group grp in one call, so their shared products are computed once.
+__device__ __forceinline__ void all_bits(uint64_t grp, uint32_t tensor_id, const StepScalars& sc, Rand4& rp,
+                                         Rand4& rm, Rand4& rv) {
+  uint32_t c0[3], c1[3], c2[3], c3[3];
+#pragma unroll
+  for (int s = 0; s < 3; ++s) {
+    c0[s] = static_cast<uint32_t>(grp);
+    c1[s] = static_cast<uint32_t>(grp >> 32) | (static_cast<uint32_t>(s) << 30);
+    c2[s] = sc.step_lo;
+    c3[s] = tensor_id;
+  }
+  philox10_n<3>(c0, c1, c2, c3, sc.seed_lo, sc.seed_hi);
+  rp = Rand4{{c0[0], c1[0], c2[0], c3[0]}};
+  rm = Rand4{{c0[1], c1[1], c2[1], c3[1]}};
+  rv = Rand4{{c0[2], c1[2], c2[2], c3[2]}};
+}
+
 // fp32 -> bf16 bits: stochastic (add 16 random bits below the kept half, then
 // truncate) or nearest-even; NaN becomes the quiet NaN with its sign.
 __device__ __forceinline__ uint32_t to_bf16(float x, uint32_t r16, bool nearest) {
@@ -507,7 +525,9 @@ __device__ __forceinline__ bool block_8bit_fast(const DevTensor& d, int64_t blk,
     const int off = r * 512 + lane * 8;
     const uint64_t grp = grp0 + static_cast<uint64_t>(r * 64);
     Rand4 rnd{{0, 0, 0, 0}};
-    if (!kNearest) rnd = group_bits(grp, 0u, d.tensor_id, sc);
+    Rand4 rm{{0, 0, 0, 0}}, rv{{0, 0, 0, 0}};
+    if constexpr (kSS && !kNearest) all_bits(grp, d.tensor_id, sc, rnd, rm, rv);
+    else if (!kNearest) rnd = group_bits(grp, 0u, d.tensor_id, sc);
     uint32_t sums[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
@@ -524,8 +544,7 @@ __device__ __forceinline__ bool block_8bit_fast(const DevTensor& d, int64_t blk,
                                      __builtin_amdgcn_perm(sums[5], sums[4], 0x07060302u),
                                      __builtin_amdgcn_perm(sums[7], sums[6], 0x07060302u)));
     uint32_t cm[2] = {0, 0}, cv[2] = {0, 0};
-    Rand4 rm{{0, 0, 0, 0}}, rv{{0, 0, 0, 0}};
-    if constexpr (kSS) state_bits(grp, d.tensor_id, sc, rm, rv);
+    if constexpr (kSS && kNearest) state_bits(grp, d.tensor_id, sc, rm, rv);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       uint32_t qm, qv;
