@@ -327,6 +327,31 @@ int validate_tensors(const opt8_tensor* t, int32_t n, bool two_state) {
   return OPT8_OK;
 }
 
+// Validation is a pure function of the descriptor values, and a training loop
+// passes the same list every step: each thread keeps a copy of the last list
+// that passed, and an identical list (byte for byte, same rule) is not checked
+// again.  The copy costs one memcmp per call instead of sorting 6n ranges.
+struct ValidatedList {
+  std::vector<opt8_tensor> list;
+  bool two_state = false;
+  bool valid = false;
+};
+thread_local ValidatedList t_validated;
+
+int validate_tensors_cached(const opt8_tensor* t, int32_t n, bool two_state) {
+  ValidatedList& c = t_validated;
+  if (c.valid && c.two_state == two_state && c.list.size() == static_cast<size_t>(n) &&
+      std::memcmp(c.list.data(), t, sizeof(opt8_tensor) * static_cast<size_t>(n)) == 0)
+    return OPT8_OK;
+  c.valid = false;
+  const int rc = validate_tensors(t, n, two_state);
+  if (rc != OPT8_OK) return rc;
+  c.list.assign(t, t + n);
+  c.two_state = two_state;
+  c.valid = true;
+  return OPT8_OK;
+}
+
 // ----------------------------------------------------------------------------- device state
 // Descriptor lists live in device memory, one slot per distinct list; a list
 // passed again (the usual training loop) is launched without a new upload.
@@ -482,9 +507,9 @@ int run_step(int algo, const opt8_tensor* tensors, int32_t n, const opt8_hparams
   const bool two_state = algo == kAdamW;
   int rc = validate_hparams(*hp, algo);
   if (rc != OPT8_OK) return rc;
-  rc = validate_tensors(tensors, n, two_state);
-  if (rc != OPT8_OK) return rc;
   if (n == 0) return OPT8_OK;
+  rc = validate_tensors_cached(tensors, n, two_state);
+  if (rc != OPT8_OK) return rc;
 
   std::lock_guard<std::mutex> lock(g_mu);
   int dev = 0;

@@ -1079,6 +1079,25 @@ __device__ __forceinline__ void block_1s_wide(const DevTensor& d, int64_t blk, i
 }
 
 // ----------------------------------------------------------------------------- driver
+// Index of the tensor holding block b: the last i in [lo, hi] whose first
+// block is <= b, given that list[lo] starts at or before b (blocks are
+// numbered by a prefix sum, so the predicate holds on a prefix of the list).
+// Each round the 64 lanes test 64 evenly spaced candidates at once and a
+// ballot keeps the last that passes, so the range shrinks 64-fold per round
+// trip: one round for up to 64 tensors, two for 4,096, three for 262,144.
+__device__ __forceinline__ int find_tensor(const DevTensor* __restrict__ list, int lo, int hi, int64_t b,
+                                           int lane) {
+  while (true) {
+    const int step = (hi - lo + 64) >> 6;          // ceil((hi - lo + 1) / 64)
+    const int cand = lo + lane * step;
+    const bool ok = cand <= hi && list[cand].block_begin <= b;
+    const uint64_t m = __builtin_amdgcn_ballot_w64(ok);   // lane 0 always passes
+    lo = __builtin_amdgcn_readfirstlane(lo + (63 - __builtin_clzll(m)) * step);
+    if (step == 1) return lo;
+    hi = min(hi, lo + step - 1);
+  }
+}
+
 template <int kBytes>
 __device__ __forceinline__ void stage_tables(uint8_t* lds) {
   uint4* dst = reinterpret_cast<uint4*>(lds);
@@ -1115,16 +1134,16 @@ step_kernel(const DevTensor* __restrict__ list, int ntensors, int64_t total_bloc
   int64_t b = gw;
   if (b >= total_blocks) return;
 
-  // the tensor holding block b: the last one whose first block is <= b
-  int lo = 0, hi = ntensors - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (list[mid].block_begin <= b) lo = mid; else hi = mid - 1;
-  }
-  int t = lo;
+  int t = find_tensor(list, 0, ntensors - 1, b, lane);
   DevTensor d = list[t];
   for (; b < total_blocks; b += nw) {
-    while (b >= d.block_begin + static_cast<int64_t>(d.nblocks)) d = list[++t];
+    // past the current tensor: the next one starts at or before b, and a later
+    // one holds it (b < total_blocks); a wave strides over many blocks, which
+    // for lists of small tensors crosses many descriptors at once
+    if (b >= d.block_begin + static_cast<int64_t>(d.nblocks)) {
+      t = find_tensor(list, t + 1, ntensors - 1, b, lane);
+      d = list[t];
+    }
     const int64_t blk = b - d.block_begin;
     if constexpr (A != kAdamW) {
       if constexpr (K == Kind::k8bit) {

@@ -186,6 +186,20 @@ int main() {
     expect_scalars(a.sc, h1, true);
   }
 
+  // a list that passed is not checked again while it stays byte-identical; edited in
+  // place it is checked afresh
+  {
+    const opt8_tensor keep = mixed[3];
+    mixed[3].grad = mixed[2].grad;                     // now overlaps tensor 2's gradient
+    CHECK(step(mixed, h1) == OPT8_E_ALIAS);
+    mixed[3] = keep;
+    CHECK(step(mixed, h1) == OPT8_OK);
+    mixed[6].tensor_id = 10;                           // duplicates tensor 0's id
+    CHECK(step(mixed, h1) == OPT8_E_DUPID);
+    mixed[6].tensor_id = 16;
+    CHECK(step(mixed, h1) == OPT8_OK);
+  }
+
   // ---------------------------------------------------------------- scalar prologue
   {
     const int64_t steps[] = {1, 2, 3, 10, 1000, 5, 200000, 1, (int64_t(1) << 32) + 7};
