@@ -328,27 +328,43 @@ int validate_tensors(const opt8_tensor* t, int32_t n, bool two_state) {
 }
 
 // Validation is a pure function of the descriptor values, and a training loop
-// passes the same list every step: each thread keeps a copy of the last list
-// that passed, and an identical list (byte for byte, same rule) is not checked
-// again.  The copy costs one memcmp per call instead of sorting 6n ranges.
+// passes the same lists every step (often two: parameters with and without
+// weight decay): each thread keeps copies of the last four lists that passed,
+// and a list identical to one of them (byte for byte, same rule) is not
+// checked again.  A hit costs one memcmp instead of sorting 6n ranges.
+constexpr int kValidated = 4;
 struct ValidatedList {
   std::vector<opt8_tensor> list;
   bool two_state = false;
   bool valid = false;
+  uint64_t stamp = 0;
 };
-thread_local ValidatedList t_validated;
+struct ValidatedCache {
+  ValidatedList entry[kValidated];
+  uint64_t clock = 0;
+};
+thread_local ValidatedCache t_validated;
 
 int validate_tensors_cached(const opt8_tensor* t, int32_t n, bool two_state) {
-  ValidatedList& c = t_validated;
-  if (c.valid && c.two_state == two_state && c.list.size() == static_cast<size_t>(n) &&
-      std::memcmp(c.list.data(), t, sizeof(opt8_tensor) * static_cast<size_t>(n)) == 0)
-    return OPT8_OK;
-  c.valid = false;
+  ValidatedCache& c = t_validated;
+  ++c.clock;
+  const size_t bytes = sizeof(opt8_tensor) * static_cast<size_t>(n);
+  ValidatedList* victim = &c.entry[0];
+  for (ValidatedList& e : c.entry) {
+    if (e.valid && e.two_state == two_state && e.list.size() == static_cast<size_t>(n) &&
+        std::memcmp(e.list.data(), t, bytes) == 0) {
+      e.stamp = c.clock;
+      return OPT8_OK;
+    }
+    if (!e.valid) victim = &e;
+    else if (victim->valid && e.stamp < victim->stamp) victim = &e;
+  }
   const int rc = validate_tensors(t, n, two_state);
   if (rc != OPT8_OK) return rc;
-  c.list.assign(t, t + n);
-  c.two_state = two_state;
-  c.valid = true;
+  victim->list.assign(t, t + n);
+  victim->two_state = two_state;
+  victim->valid = true;
+  victim->stamp = c.clock;
   return OPT8_OK;
 }
 

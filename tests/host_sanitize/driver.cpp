@@ -198,6 +198,19 @@ int main() {
     CHECK(step(mixed, h1) == OPT8_E_DUPID);
     mixed[6].tensor_id = 16;
     CHECK(step(mixed, h1) == OPT8_OK);
+    // two lists alternating (two parameter groups) both stay cached
+    for (int k = 0; k < 3; ++k) {
+      CHECK(step(mixed, h1) == OPT8_OK);
+      CHECK(step(one, h1) == OPT8_OK);
+    }
+    // a list that passed under a one-state rule (v unused, may be NULL) is still checked
+    // under AdamW's
+    std::vector<opt8_tensor> nov = one;
+    nov[0].v = nullptr;
+    nov[0].absmax_v = nullptr;
+    CHECK(step(nov, h1) == OPT8_E_NULL);
+    CHECK(opt8_lion_step(nov.data(), 1, &h1, nullptr) == OPT8_OK);
+    CHECK(step(nov, h1) == OPT8_E_NULL);
   }
 
   // ---------------------------------------------------------------- scalar prologue
