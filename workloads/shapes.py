@@ -115,6 +115,15 @@ def gptneo_6p7b() -> Workload:
         steps=5, lr=1.2e-4, weight_decay=0.1, seed=1234, grad_recipe="outliers100")
 
 
+def many_small(numel: int, count: int = 30000) -> Workload:
+    """`count` equal tensors of `numel` elements (a stress case for the multi-tensor schedule:
+    each wave's stride over the blocks crosses many tensors)."""
+    return Workload(
+        name=f"many-{numel}",
+        tensors=tuple(TensorSpec(f"t{i}", (numel,), "weight", numel) for i in range(count)),
+        steps=3, lr=1e-3, weight_decay=0.01, seed=0, grad_recipe="plain")
+
+
 WORKLOADS = {
     "single-1M": single_tensor,
     "gpt2-350m": gpt2_350m,
@@ -122,6 +131,8 @@ WORKLOADS = {
     "gptneo-2.7b": gptneo_2p7b,
     "gptneo-2.7b-bf16": lambda: gptneo_2p7b("bf16"),
     "gptneo-6.7b": gptneo_6p7b,
+    "many-4096": lambda: many_small(4096),
+    "many-6151": lambda: many_small(6151),
 }
 
 
