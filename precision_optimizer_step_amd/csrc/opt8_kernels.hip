@@ -437,13 +437,19 @@ __device__ __forceinline__ uint32_t code_sr(float n, const uint8_t* lds, uint32_
   return k + ((f > static_cast<float>(r16)) ? 1u : 0u);
 }
 
-// A full block; returns false (having written nothing) when the block must
-// take the plain path instead.  Everything that could make a result NaN or
-// leave the range of the fast sequences is checked after pass 1, so pass 2
-// stores each group's parameters and codes as soon as they are formed.
-template <bool kNearest, bool kSS>
+// A full block, or with kPartial the last block of a tensor holding `valid`
+// elements; returns false (having written nothing) when the block must take
+// the plain path instead.  Everything that could make a result NaN or leave
+// the range of the fast sequences is checked after pass 1, so pass 2 stores
+// each group's parameters and codes as soon as they are formed.  In a partial
+// block a lane reads only valid elements (element by element in the one group
+// that straddles the end) and fills the rest with a zero gradient, a zero
+// parameter and the zero codes, whose moments are +0: they leave every block
+// maximum and range check to the valid elements, and are never stored.
+template <bool kNearest, bool kSS, bool kPartial = false>
 __device__ __forceinline__ bool block_8bit_fast(const DevTensor& d, int64_t blk, int lane,
-                                                const StepScalars& sc, const uint8_t* lds, bool range_ok) {
+                                                const StepScalars& sc, const uint8_t* lds, bool range_ok,
+                                                int valid = kBlock) {
   const int64_t e0 = blk * kBlock;
   const uint16_t* gp = d.grad + e0;
   uint16_t* pp = d.param + e0;
@@ -454,16 +460,43 @@ __device__ __forceinline__ bool block_8bit_fast(const DevTensor& d, int64_t blk,
 
   uint4 G[kGroups], P[kGroups];
   uint2 QM[kGroups], QV[kGroups];
+  if constexpr (kPartial) {
 #pragma unroll
-  for (int r = 0; r < kGroups; ++r) {
-    const int off = r * 512 + lane * 8;
-    G[r] = ld_stream16(gp + off);
-    QM[r] = ld_stream8(mp + off);
-    QV[r] = ld_stream8(vp + off);
+    for (int r = 0; r < kGroups; ++r) {
+      const int off = r * 512 + lane * 8;
+      if (off + 8 <= valid) {
+        G[r] = ld_stream16(gp + off);
+        P[r] = ld_stream16(pp + off);
+        QM[r] = ld_stream8(mp + off);
+        QV[r] = ld_stream8(vp + off);
+      } else {
+        uint32_t gw[4] = {0, 0, 0, 0}, pw[4] = {0, 0, 0, 0};
+        uint32_t mw[2] = {0x7F7F7F7Fu, 0x7F7F7F7Fu}, vw[2] = {0, 0};
+        for (int j = 0; j < 8 && off + j < valid; ++j) {
+          const int sh16 = 16 * (j & 1), sh8 = 8 * (j & 3);
+          gw[j >> 1] |= static_cast<uint32_t>(gp[off + j]) << sh16;
+          pw[j >> 1] |= static_cast<uint32_t>(pp[off + j]) << sh16;
+          mw[j >> 2] = (mw[j >> 2] & ~(0xFFu << sh8)) | (static_cast<uint32_t>(mp[off + j]) << sh8);
+          vw[j >> 2] |= static_cast<uint32_t>(vp[off + j]) << sh8;
+        }
+        G[r] = make_uint4(gw[0], gw[1], gw[2], gw[3]);
+        P[r] = make_uint4(pw[0], pw[1], pw[2], pw[3]);
+        QM[r] = make_uint2(mw[0], mw[1]);
+        QV[r] = make_uint2(vw[0], vw[1]);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int r = 0; r < kGroups; ++r) {
+      const int off = r * 512 + lane * 8;
+      G[r] = ld_stream16(gp + off);
+      QM[r] = ld_stream8(mp + off);
+      QV[r] = ld_stream8(vp + off);
+    }
+#pragma unroll
+    for (int r = 0; r < kGroups; ++r)
+      P[r] = ld_stream16(pp + r * 512 + lane * 8);
   }
-#pragma unroll
-  for (int r = 0; r < kGroups; ++r)
-    P[r] = ld_stream16(pp + r * 512 + lane * 8);
 
   // pass 1: moments, block maxima (NaN-propagating), smallest exponents, and
   // the largest parameter magnitude
@@ -539,10 +572,14 @@ __device__ __forceinline__ bool block_8bit_fast(const DevTensor& d, int64_t blk,
       sums[j] = b + (kNearest ? (0x7FFFu + ((b >> 16) & 1u)) : r16_of(rnd, j));
     }
     // keep the upper halves: bf16 pairs (element 2k in the low half)
-    st_stream16(pp + off, make_uint4(__builtin_amdgcn_perm(sums[1], sums[0], 0x07060302u),
-                                     __builtin_amdgcn_perm(sums[3], sums[2], 0x07060302u),
-                                     __builtin_amdgcn_perm(sums[5], sums[4], 0x07060302u),
-                                     __builtin_amdgcn_perm(sums[7], sums[6], 0x07060302u)));
+    if (!kPartial || off + 8 <= valid) {
+      st_stream16(pp + off, make_uint4(__builtin_amdgcn_perm(sums[1], sums[0], 0x07060302u),
+                                       __builtin_amdgcn_perm(sums[3], sums[2], 0x07060302u),
+                                       __builtin_amdgcn_perm(sums[5], sums[4], 0x07060302u),
+                                       __builtin_amdgcn_perm(sums[7], sums[6], 0x07060302u)));
+    } else {
+      for (int j = 0; j < 8 && off + j < valid; ++j) pp[off + j] = static_cast<uint16_t>(sums[j] >> 16);
+    }
     uint32_t cm[2] = {0, 0}, cv[2] = {0, 0};
     if constexpr (kSS && kNearest) state_bits(grp, d.tensor_id, sc, rm, rv);
 #pragma unroll
@@ -560,8 +597,15 @@ __device__ __forceinline__ bool block_8bit_fast(const DevTensor& d, int64_t blk,
     }
     if (!live_m) cm[0] = cm[1] = 0x7F7F7F7Fu;
     if (!live_v) cv[0] = cv[1] = 0u;
-    st_stream8(mp + off, make_uint2(cm[0], cm[1]));
-    st_stream8(vp + off, make_uint2(cv[0], cv[1]));
+    if (!kPartial || off + 8 <= valid) {
+      st_stream8(mp + off, make_uint2(cm[0], cm[1]));
+      st_stream8(vp + off, make_uint2(cv[0], cv[1]));
+    } else {
+      for (int j = 0; j < 8 && off + j < valid; ++j) {
+        mp[off + j] = static_cast<uint8_t>(cm[j >> 2] >> (8 * (j & 3)));
+        vp[off + j] = static_cast<uint8_t>(cv[j >> 2] >> (8 * (j & 3)));
+      }
+    }
   }
   if (lane == 0) {
     d.amax_m[blk] = mxm;
@@ -1166,7 +1210,11 @@ step_kernel(const DevTensor* __restrict__ list, int ntensors, int64_t total_bloc
     } else if constexpr (K == Kind::k8bitTail) {
       // this list holds the last, partial block of 8-bit tensors (one per entry)
       const int64_t tail = (d.numel - 1) / kBlock;
-      block_8bit_plain<false, SS>(d, tail, lane, static_cast<int>(d.numel - tail * kBlock), sc, lds);
+      const int valid = static_cast<int>(d.numel - tail * kBlock);
+      const bool done = sc.param_round
+                            ? block_8bit_fast<true, SS, true>(d, tail, lane, sc, lds, range_ok != 0, valid)
+                            : block_8bit_fast<false, SS, true>(d, tail, lane, sc, lds, range_ok != 0, valid);
+      if (!done) block_8bit_plain<false, SS>(d, tail, lane, valid, sc, lds);
     } else {
       const int64_t left = d.numel - blk * kBlock;
       const bool full = left >= kBlock;
