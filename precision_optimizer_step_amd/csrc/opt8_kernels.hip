@@ -938,9 +938,13 @@ __device__ __forceinline__ void block_1s_8bit_plain(const DevTensor& d, int64_t 
 // 8-bit state, full block: LUT requantisation and the plain add-and-truncate
 // rounding; returns false (nothing written) on a NaN parameter or moment, or
 // an infinite block maximum.
-template <int A, bool kNearest, bool kSS>
+// With kPartial, the last block of a tensor holding `valid` elements, filled as
+// in block_8bit_fast (a zero gradient, parameter and moment leave a zero
+// moment and parameter under either rule, never stored).
+template <int A, bool kNearest, bool kSS, bool kPartial = false>
 __device__ __forceinline__ bool block_1s_8bit_fast(const DevTensor& d, int64_t blk, int lane,
-                                                   const StepScalars& sc, const uint8_t* lds) {
+                                                   const StepScalars& sc, const uint8_t* lds,
+                                                   int valid = kBlock) {
   const float* cb_s = reinterpret_cast<const float*>(lds + kOffCbS);
   const float* mid_s = reinterpret_cast<const float*>(lds + kOffMidS);
   const int64_t e0 = blk * kBlock;
@@ -953,9 +957,23 @@ __device__ __forceinline__ bool block_1s_8bit_fast(const DevTensor& d, int64_t b
 #pragma unroll
   for (int r = 0; r < kGroups; ++r) {
     const int off = r * 512 + lane * 8;
-    G[r] = ld_stream16(gp + off);
-    P[r] = ld_stream16(pp + off);
-    QM[r] = ld_stream8(mp + off);
+    if (!kPartial || off + 8 <= valid) {
+      G[r] = ld_stream16(gp + off);
+      P[r] = ld_stream16(pp + off);
+      QM[r] = ld_stream8(mp + off);
+    } else {
+      uint32_t gw[4] = {0, 0, 0, 0}, pw[4] = {0, 0, 0, 0};
+      uint32_t mw[2] = {0x7F7F7F7Fu, 0x7F7F7F7Fu};
+      for (int j = 0; j < 8 && off + j < valid; ++j) {
+        const int sh16 = 16 * (j & 1), sh8 = 8 * (j & 3);
+        gw[j >> 1] |= static_cast<uint32_t>(gp[off + j]) << sh16;
+        pw[j >> 1] |= static_cast<uint32_t>(pp[off + j]) << sh16;
+        mw[j >> 2] = (mw[j >> 2] & ~(0xFFu << sh8)) | (static_cast<uint32_t>(mp[off + j]) << sh8);
+      }
+      G[r] = make_uint4(gw[0], gw[1], gw[2], gw[3]);
+      P[r] = make_uint4(pw[0], pw[1], pw[2], pw[3]);
+      QM[r] = make_uint2(mw[0], mw[1]);
+    }
   }
   uint32_t c0[4] = {0, 0, 0, 0}, c1[4] = {0, 0, 0, 0}, c2[4] = {0, 0, 0, 0}, c3[4] = {0, 0, 0, 0};
   if (!kNearest) {
@@ -997,7 +1015,15 @@ __device__ __forceinline__ bool block_1s_8bit_fast(const DevTensor& d, int64_t b
   mxm = wave_max_nonneg(mxm);
   if (nan_lanes != 0 || !(mxm <= 3.0e38f)) return false;
 #pragma unroll
-  for (int r = 0; r < kGroups; ++r) st_stream16(pp + r * 512 + lane * 8, P[r]);
+  for (int r = 0; r < kGroups; ++r) {
+    const int off = r * 512 + lane * 8;
+    if (!kPartial || off + 8 <= valid) {
+      st_stream16(pp + off, P[r]);
+    } else {
+      for (int j = 0; j < 8 && off + j < valid; ++j)
+        pp[off + j] = static_cast<uint16_t>(word_of(P[r], j >> 1) >> (16 * (j & 1)));
+    }
+  }
   const bool live = mxm >= kMinNormal;
   const float inv = live ? 1.0f / mxm : 0.0f;
 #pragma unroll
@@ -1013,7 +1039,12 @@ __device__ __forceinline__ bool block_1s_8bit_fast(const DevTensor& d, int64_t b
       for (int j = 0; j < 8; ++j) cm[j >> 2] |= code_s(M2[r * 8 + j] * inv, lds, mid_s) << (8 * (j & 3));
     }
     if (!live) cm[0] = cm[1] = 0x7F7F7F7Fu;
-    st_stream8(mp + r * 512 + lane * 8, make_uint2(cm[0], cm[1]));
+    const int off = r * 512 + lane * 8;
+    if (!kPartial || off + 8 <= valid) {
+      st_stream8(mp + off, make_uint2(cm[0], cm[1]));
+    } else {
+      for (int j = 0; j < 8 && off + j < valid; ++j) mp[off + j] = static_cast<uint8_t>(cm[j >> 2] >> (8 * (j & 3)));
+    }
   }
   if (lane == 0) d.amax_m[blk] = mxm;
   return true;
@@ -1196,7 +1227,10 @@ step_kernel(const DevTensor* __restrict__ list, int ntensors, int64_t total_bloc
         if (!done) block_1s_8bit_plain<A, true, SS>(d, blk, lane, kBlock, sc, lds);
       } else if constexpr (K == Kind::k8bitTail) {
         const int64_t tail = (d.numel - 1) / kBlock;
-        block_1s_8bit_plain<A, false, SS>(d, tail, lane, static_cast<int>(d.numel - tail * kBlock), sc, lds);
+        const int valid = static_cast<int>(d.numel - tail * kBlock);
+        const bool done = sc.param_round ? block_1s_8bit_fast<A, true, SS, true>(d, tail, lane, sc, lds, valid)
+                                         : block_1s_8bit_fast<A, false, SS, true>(d, tail, lane, sc, lds, valid);
+        if (!done) block_1s_8bit_plain<A, false, SS>(d, tail, lane, valid, sc, lds);
       } else {
         const int64_t left = d.numel - blk * kBlock;
         if (left >= kBlock) block_1s_wide<A, K == Kind::kBf16, true>(d, blk, lane, kBlock, sc);
