@@ -644,9 +644,14 @@ __device__ __forceinline__ uint32_t hi_pair(uint32_t even, uint32_t odd) {
 // plain add-and-truncate rounding) when every element of the wave's group is
 // in their range -- no NaN result, and non-zero m2, v2 and m2/den all at or
 // above 2^-88 -- and otherwise recomputes the group on the plain path.
-template <bool kNearest>
+// With kPartial, the last block of a tensor holding `valid` elements: groups
+// wholly past the end are skipped, the group that straddles it is read and
+// written element by element with zeros in the rest (a zero gradient,
+// parameter and moments give den = eps and u = 0, so they decide nothing),
+// and every other group takes the same path as in a full block.
+template <bool kNearest, bool kPartial = false>
 __device__ __forceinline__ void block_bf16_full(const DevTensor& d, int64_t blk, int lane,
-                                                const StepScalars& sc, bool range_ok) {
+                                                const StepScalars& sc, bool range_ok, int valid = kBlock) {
   const int64_t e0 = blk * kBlock;
   const uint16_t* gp = d.grad + e0;
   uint16_t* pp = d.param + e0;
@@ -655,11 +660,29 @@ __device__ __forceinline__ void block_bf16_full(const DevTensor& d, int64_t blk,
   const uint64_t grp0 = (static_cast<uint64_t>(d.index_base + e0) >> 3) + static_cast<uint64_t>(lane);
 #pragma unroll 1
   for (int r = 0; r < kGroups; ++r) {
+    if (kPartial && r * 512 >= valid) break;       // no lane has an element left
     const int off = r * 512 + lane * 8;
-    const uint4 G = ld_stream16(gp + off);
-    const uint4 P = ld_stream16(pp + off);
-    const uint4 M = ld_stream16(mp + off);
-    const uint4 V = ld_stream16(vp + off);
+    const bool whole = !kPartial || off + 8 <= valid;
+    uint4 G, P, M, V;
+    if (whole) {
+      G = ld_stream16(gp + off);
+      P = ld_stream16(pp + off);
+      M = ld_stream16(mp + off);
+      V = ld_stream16(vp + off);
+    } else {
+      uint32_t a[4] = {0, 0, 0, 0}, b[4] = {0, 0, 0, 0}, c[4] = {0, 0, 0, 0}, e[4] = {0, 0, 0, 0};
+      for (int j = 0; j < 8 && off + j < valid; ++j) {
+        const int sh = 16 * (j & 1);
+        a[j >> 1] |= static_cast<uint32_t>(gp[off + j]) << sh;
+        b[j >> 1] |= static_cast<uint32_t>(pp[off + j]) << sh;
+        c[j >> 1] |= static_cast<uint32_t>(mp[off + j]) << sh;
+        e[j >> 1] |= static_cast<uint32_t>(vp[off + j]) << sh;
+      }
+      G = make_uint4(a[0], a[1], a[2], a[3]);
+      P = make_uint4(b[0], b[1], b[2], b[3]);
+      M = make_uint4(c[0], c[1], c[2], c[3]);
+      V = make_uint4(e[0], e[1], e[2], e[3]);
+    }
     const uint64_t grp = grp0 + static_cast<uint64_t>(r * 64);
     uint32_t c0[3], c1[3], c2[3], c3[3];
 #pragma unroll
@@ -705,52 +728,16 @@ __device__ __forceinline__ void block_bf16_full(const DevTensor& d, int64_t blk,
     } else {
       group_bf16_plain(G, P, M, V, rp, rm, rv, kNearest, sc, po, mo, vo);
     }
-    st_stream16(pp + off, make_uint4(po[0], po[1], po[2], po[3]));
-    st_stream16(mp + off, make_uint4(mo[0], mo[1], mo[2], mo[3]));
-    st_stream16(vp + off, make_uint4(vo[0], vo[1], vo[2], vo[3]));
-  }
-}
-
-// The partial last block of a tensor.
-__device__ __forceinline__ void block_bf16_tail(const DevTensor& d, int64_t blk, int lane, int valid,
-                                                const StepScalars& sc) {
-  const int64_t e0 = blk * kBlock;
-  const uint16_t* gp = d.grad + e0;
-  uint16_t* pp = d.param + e0;
-  uint16_t* mp = static_cast<uint16_t*>(d.m) + e0;
-  uint16_t* vp = static_cast<uint16_t*>(d.v) + e0;
-  const bool nearest = sc.param_round != 0;
-  const uint64_t grp0 = static_cast<uint64_t>(d.index_base + e0) >> 3;
-#pragma unroll 1
-  for (int r = 0; r < kGroups; ++r) {
-    const int off = r * 512 + lane * 8;
-    uint32_t a[4] = {0, 0, 0, 0}, b[4] = {0, 0, 0, 0}, c[4] = {0, 0, 0, 0}, e[4] = {0, 0, 0, 0};
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      if (off + j < valid) {
-        const int s = 16 * (j & 1);
-        a[j >> 1] |= static_cast<uint32_t>(gp[off + j]) << s;
-        b[j >> 1] |= static_cast<uint32_t>(pp[off + j]) << s;
-        c[j >> 1] |= static_cast<uint32_t>(mp[off + j]) << s;
-        e[j >> 1] |= static_cast<uint32_t>(vp[off + j]) << s;
-      }
-    }
-    const uint64_t grp = grp0 + (off >> 3);
-    Rand4 rp{{0, 0, 0, 0}};
-    if (!nearest) rp = group_bits(grp, 0u, d.tensor_id, sc);
-    const Rand4 rm = group_bits(grp, 1u, d.tensor_id, sc);
-    const Rand4 rv = group_bits(grp, 2u, d.tensor_id, sc);
-    uint32_t po[4], mo[4], vo[4];
-    group_bf16_plain(make_uint4(a[0], a[1], a[2], a[3]), make_uint4(b[0], b[1], b[2], b[3]),
-                     make_uint4(c[0], c[1], c[2], c[3]), make_uint4(e[0], e[1], e[2], e[3]),
-                     rp, rm, rv, nearest, sc, po, mo, vo);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      if (off + j < valid) {
-        const int s = 16 * (j & 1);
-        pp[off + j] = static_cast<uint16_t>(po[j >> 1] >> s);
-        mp[off + j] = static_cast<uint16_t>(mo[j >> 1] >> s);
-        vp[off + j] = static_cast<uint16_t>(vo[j >> 1] >> s);
+    if (whole) {
+      st_stream16(pp + off, make_uint4(po[0], po[1], po[2], po[3]));
+      st_stream16(mp + off, make_uint4(mo[0], mo[1], mo[2], mo[3]));
+      st_stream16(vp + off, make_uint4(vo[0], vo[1], vo[2], vo[3]));
+    } else {
+      for (int j = 0; j < 8 && off + j < valid; ++j) {
+        const int sh = 16 * (j & 1);
+        pp[off + j] = static_cast<uint16_t>(po[j >> 1] >> sh);
+        mp[off + j] = static_cast<uint16_t>(mo[j >> 1] >> sh);
+        vp[off + j] = static_cast<uint16_t>(vo[j >> 1] >> sh);
       }
     }
   }
@@ -1254,8 +1241,10 @@ step_kernel(const DevTensor* __restrict__ list, int ntensors, int64_t total_bloc
       const bool full = left >= kBlock;
       const int valid = full ? kBlock : static_cast<int>(left);
       if constexpr (K == Kind::kBf16) {
-        if (!full) block_bf16_tail(d, blk, lane, valid, sc);
-        else if (sc.param_round) block_bf16_full<true>(d, blk, lane, sc, range_ok != 0);
+        if (!full) {
+          if (sc.param_round) block_bf16_full<true, true>(d, blk, lane, sc, range_ok != 0, valid);
+          else block_bf16_full<false, true>(d, blk, lane, sc, range_ok != 0, valid);
+        } else if (sc.param_round) block_bf16_full<true>(d, blk, lane, sc, range_ok != 0);
         else block_bf16_full<false>(d, blk, lane, sc, range_ok != 0);
       } else {
         if (full) block_fp32<true>(d, blk, lane, valid, sc);
