@@ -307,6 +307,45 @@ def test_non_finite_inputs():
     assert np.array_equal(got[0][4096:], want[0][4096:])
 
 
+@pytest.mark.parametrize("algo,mode", [(0, M8), (0, MB), (oracle.ALGO_LION, M8), (oracle.ALGO_MOMENTUM, M8)])
+def test_non_finite_in_a_partial_block(algo, mode):
+    """A NaN and an infinite gradient inside the partial last block of a tensor: the partial
+    block leaves its fast path for the plain one, and the results follow the oracle (NaN
+    compared as NaN); the full block before it matches bit for bit."""
+    rng = np.random.default_rng(22 + algo + 10 * mode)
+    n = 2048 + 100
+    p = _rand_bf16(rng, n, 0.02)
+    g = _rand_bf16(rng, n, 1e-3)
+    g[2048 + 50] = 0x7FC0
+    g[2048 + 60] = 0x7F80
+    m, v, am, av = _rand_state(mode, n, 7, 3)
+    if algo != 0:
+        v = av = None
+    hp = oracle.Hparams(lr=1e-3, beta2=0.99 if algo else 0.999, weight_decay=0.01, step=2, seed=5)
+    want = oracle_step(DevTensorSet(mode, p, g, m, v, am, av, tensor_id=2), [p, m, v, am, av], hp, algo)
+    s = DevTensorSet(mode, p, g, m, v, am, av, tensor_id=2)
+    gpu_step([s], hp, algo)
+    got = s.read()
+    wp = oracle.rounding.bf16_to_f32(want[0])
+    gp_ = oracle.rounding.bf16_to_f32(got[0])
+    assert np.array_equal(np.isnan(wp), np.isnan(gp_))
+    assert np.isnan(gp_).any(), "the NaN gradient must reach the parameter"
+    fin = ~np.isnan(wp)
+    assert np.array_equal(got[0][fin], want[0][fin])
+    for k in range(1, 5):
+        if want[k] is None:
+            continue
+        if want[k].dtype == np.uint8:
+            assert np.array_equal(got[k], want[k])
+        else:
+            w = want[k].view(np.float32) if want[k].dtype == np.float32 else oracle.rounding.bf16_to_f32(want[k])
+            h = got[k].view(np.float32) if got[k].dtype == np.float32 else oracle.rounding.bf16_to_f32(got[k])
+            assert np.array_equal(np.isnan(h), np.isnan(w))
+            ok = ~np.isnan(w)
+            assert np.array_equal(h[ok], w[ok])
+    assert np.array_equal(got[0][:2048], want[0][:2048])
+
+
 @pytest.mark.parametrize("label,hp_kw", [
     ("eps below 2^-60", dict(eps=1e-20)),
     ("eps above 2^60", dict(eps=1e20)),
