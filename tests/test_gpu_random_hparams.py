@@ -2,8 +2,9 @@
 
 Each case draws an update rule (AdamW, Lion, momentum), beta1, beta2, eps, lr, weight decay,
 a step number, a seed and both rounding choices, and runs three steps over a list holding an
-8-bit tensor with full blocks and a ragged tail, a bf16-state tensor and an fp32-state tensor,
-each started from a random state.  Every result is compared with the oracle, which carries its
+8-bit tensor (0-3 full blocks and a last block of 1-2047 elements, drawn per case), a
+bf16-state tensor and an fp32-state tensor (lengths drawn per case), each started from a
+random state.  Every result is compared with the oracle, which carries its
 state from step to step independently of the GPU.
 """
 
@@ -42,14 +43,15 @@ def _draw(rng):
     return algo, hp
 
 
-@pytest.mark.parametrize("case", range(12))
+@pytest.mark.parametrize("case", range(24))
 def test_random_hyperparameters(case):
     rng = np.random.default_rng(1000 + case)
     algo, kw = _draw(rng)
     one = algo != ALGO_ADAMW
     gsig = float(10.0 ** rng.uniform(-5, -1))
     sets, states = [], []
-    for tid, (n, mode) in enumerate([(2048 * 5 + 333, M8), (3000, MB), (700, MF)]):
+    n8 = 2048 * int(rng.integers(0, 4)) + int(rng.integers(1, 2048))
+    for tid, (n, mode) in enumerate([(n8, M8), (int(rng.integers(1, 5000)), MB), (int(rng.integers(1, 4096)), MF)]):
         p = gen.to_bf16_bits((rng.standard_normal(n) * 0.05).astype(np.float32))
         g = gen.to_bf16_bits((rng.standard_normal(n) * gsig).astype(np.float32))
         if mode == M8:
