@@ -507,6 +507,7 @@ __device__ __forceinline__ bool block_8bit_fast(const DevTensor& d, int64_t blk,
   int emin = 0;
 #pragma unroll
   for (int r = 0; r < kGroups; ++r) {
+    if (kPartial && r * 512 >= valid) continue;   // no lane has an element left
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const float g = bf16_at(G[r], j);
@@ -555,6 +556,7 @@ __device__ __forceinline__ bool block_8bit_fast(const DevTensor& d, int64_t blk,
   const uint64_t grp0 = (static_cast<uint64_t>(d.index_base + e0) >> 3) + static_cast<uint64_t>(lane);
 #pragma unroll
   for (int r = 0; r < kGroups; ++r) {
+    if (kPartial && r * 512 >= valid) continue;   // no lane has an element left
     const int off = r * 512 + lane * 8;
     const uint64_t grp = grp0 + static_cast<uint64_t>(r * 64);
     Rand4 rnd{{0, 0, 0, 0}};
@@ -943,6 +945,7 @@ __device__ __forceinline__ bool block_1s_8bit_fast(const DevTensor& d, int64_t b
   uint2 QM[kGroups];
 #pragma unroll
   for (int r = 0; r < kGroups; ++r) {
+    if (kPartial && r * 512 >= valid) continue;   // no lane has an element left
     const int off = r * 512 + lane * 8;
     if (!kPartial || off + 8 <= valid) {
       G[r] = ld_stream16(gp + off);
@@ -980,6 +983,7 @@ __device__ __forceinline__ bool block_1s_8bit_fast(const DevTensor& d, int64_t b
   uint64_t nan_lanes = 0;
 #pragma unroll
   for (int r = 0; r < kGroups; ++r) {
+    if (kPartial && r * 512 >= valid) continue;   // no lane has an element left
     const Rand4 rnd{{c0[r], c1[r], c2[r], c3[r]}};
     uint32_t sums[8];
 #pragma unroll
@@ -1003,6 +1007,7 @@ __device__ __forceinline__ bool block_1s_8bit_fast(const DevTensor& d, int64_t b
   if (nan_lanes != 0 || !(mxm <= 3.0e38f)) return false;
 #pragma unroll
   for (int r = 0; r < kGroups; ++r) {
+    if (kPartial && r * 512 >= valid) continue;   // no lane has an element left
     const int off = r * 512 + lane * 8;
     if (!kPartial || off + 8 <= valid) {
       st_stream16(pp + off, P[r]);
@@ -1015,6 +1020,7 @@ __device__ __forceinline__ bool block_1s_8bit_fast(const DevTensor& d, int64_t b
   const float inv = live ? 1.0f / mxm : 0.0f;
 #pragma unroll
   for (int r = 0; r < kGroups; ++r) {
+    if (kPartial && r * 512 >= valid) continue;   // no lane has an element left
     uint32_t cm[2] = {0, 0};
     if constexpr (kSS) {
       const Rand4 rm = group_bits((static_cast<uint64_t>(d.index_base + e0) >> 3) +
