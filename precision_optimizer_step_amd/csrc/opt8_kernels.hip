@@ -746,70 +746,108 @@ __device__ __forceinline__ void block_bf16_full(const DevTensor& d, int64_t blk,
 }
 
 // ----------------------------------------------------------------------------- fp32 state
-template <bool kFull>
-__device__ __forceinline__ void block_fp32(const DevTensor& d, int64_t blk, int lane, int valid,
-                                           const StepScalars& sc) {
+// The fallback for small tensors.  Each 8-element group takes the fast exact
+// sequences under the same per-group check as the bf16-state kernel (no NaN
+// result, non-zero m2, v2 and m2/den at or above 2^-89, the host's range for
+// eps and the corrections), else the plain IEEE operations; the moments are
+// stored as computed.  Whole groups move with 16-byte accesses; with kPartial
+// (the last block of a tensor holding `valid` elements) the groups past the
+// end are skipped and the one that straddles it is read and written element
+// by element with zeros in the rest.
+template <bool kNearest, bool kPartial>
+__device__ __forceinline__ void block_fp32(const DevTensor& d, int64_t blk, int lane, const StepScalars& sc,
+                                           bool range_ok, int valid = kBlock) {
   const int64_t e0 = blk * kBlock;
   const uint16_t* gp = d.grad + e0;
   uint16_t* pp = d.param + e0;
   float* mp = static_cast<float*>(d.m) + e0;
   float* vp = static_cast<float*>(d.v) + e0;
-  const bool nearest = sc.param_round != 0;
   const uint64_t grp0 = static_cast<uint64_t>(d.index_base + e0) >> 3;
-#pragma unroll
+#pragma unroll 1
   for (int r = 0; r < kGroups; ++r) {
+    if (kPartial && r * 512 >= valid) break;       // no lane has an element left
     const int off = r * 512 + lane * 8;
-    uint4 G = make_uint4(0, 0, 0, 0), P = make_uint4(0, 0, 0, 0);
+    const bool whole = !kPartial || off + 8 <= valid;
+    uint4 G, P;
     float M[8], V[8];
-    if (kFull) {
-      G = *reinterpret_cast<const uint4*>(gp + off);
-      P = *reinterpret_cast<const uint4*>(pp + off);
-      const float4 m0 = *reinterpret_cast<const float4*>(mp + off);
-      const float4 m1 = *reinterpret_cast<const float4*>(mp + off + 4);
-      const float4 v0 = *reinterpret_cast<const float4*>(vp + off);
-      const float4 v1 = *reinterpret_cast<const float4*>(vp + off + 4);
-      M[0] = m0.x; M[1] = m0.y; M[2] = m0.z; M[3] = m0.w;
-      M[4] = m1.x; M[5] = m1.y; M[6] = m1.z; M[7] = m1.w;
-      V[0] = v0.x; V[1] = v0.y; V[2] = v0.z; V[3] = v0.w;
-      V[4] = v1.x; V[5] = v1.y; V[6] = v1.z; V[7] = v1.w;
+    if (whole) {
+      G = ld_stream16(gp + off);
+      P = ld_stream16(pp + off);
+      const uint4 m0 = ld_stream16(mp + off), m1 = ld_stream16(mp + off + 4);
+      const uint4 v0 = ld_stream16(vp + off), v1 = ld_stream16(vp + off + 4);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        M[k] = __uint_as_float(word_of(m0, k));
+        M[k + 4] = __uint_as_float(word_of(m1, k));
+        V[k] = __uint_as_float(word_of(v0, k));
+        V[k + 4] = __uint_as_float(word_of(v1, k));
+      }
     } else {
       uint32_t a[4] = {0, 0, 0, 0}, b[4] = {0, 0, 0, 0};
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const bool ok = off + j < valid;
-        if (ok) {
-          a[j >> 1] |= static_cast<uint32_t>(gp[off + j]) << (16 * (j & 1));
-          b[j >> 1] |= static_cast<uint32_t>(pp[off + j]) << (16 * (j & 1));
-        }
-        M[j] = ok ? mp[off + j] : 0.0f;
-        V[j] = ok ? vp[off + j] : 0.0f;
+        M[j] = 0.0f;
+        V[j] = 0.0f;
+      }
+      for (int j = 0; j < 8 && off + j < valid; ++j) {
+        a[j >> 1] |= static_cast<uint32_t>(gp[off + j]) << (16 * (j & 1));
+        b[j >> 1] |= static_cast<uint32_t>(pp[off + j]) << (16 * (j & 1));
+        M[j] = mp[off + j];
+        V[j] = vp[off + j];
       }
       G = make_uint4(a[0], a[1], a[2], a[3]);
       P = make_uint4(b[0], b[1], b[2], b[3]);
     }
     Rand4 rp{{0, 0, 0, 0}};
-    if (!nearest) rp = group_bits(grp0 + (off >> 3), 0u, d.tensor_id, sc);
-    uint32_t po[4] = {0, 0, 0, 0};
+    if (!kNearest) rp = group_bits(grp0 + (off >> 3), 0u, d.tensor_id, sc);
+    uint32_t ps[8];
     float M2[8], V2[8];
+    int emin = 0;
+    bool nan = false;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const float pn = adamw(bf16_at(P, j), bf16_at(G, j), M[j], V[j], sc, M2[j], V2[j]);
-      po[j >> 1] |= to_bf16(pn, r16_of(rp, j), nearest) << (16 * (j & 1));
+      const float g = bf16_at(G, j);
+      const float p = bf16_at(P, j);
+      const float m2 = sc.beta1 * M[j] + sc.w1 * g;
+      const float v2 = sc.beta2 * V[j] + sc.w2 * (g * g);
+      const float den = sqrt_rn(v2) * sc.rbc2 + sc.eps;
+      const float u = div_rn(m2, den);
+      const float pn = (p - sc.lrwd * p) - sc.step_size * u;
+      nan |= (pn != pn);
+      emin = min(min(emin, __builtin_amdgcn_frexp_expf(u)),
+                 min(__builtin_amdgcn_frexp_expf(m2), __builtin_amdgcn_frexp_expf(v2)));
+      const uint32_t bits = __float_as_uint(pn);
+      ps[j] = bits + (kNearest ? (0x7FFFu + ((bits >> 16) & 1u)) : r16_of(rp, j));
+      M2[j] = m2;
+      V2[j] = v2;
     }
-    if (kFull) {
-      *reinterpret_cast<uint4*>(pp + off) = make_uint4(po[0], po[1], po[2], po[3]);
-      *reinterpret_cast<float4*>(mp + off) = make_float4(M2[0], M2[1], M2[2], M2[3]);
-      *reinterpret_cast<float4*>(mp + off + 4) = make_float4(M2[4], M2[5], M2[6], M2[7]);
-      *reinterpret_cast<float4*>(vp + off) = make_float4(V2[0], V2[1], V2[2], V2[3]);
-      *reinterpret_cast<float4*>(vp + off + 4) = make_float4(V2[4], V2[5], V2[6], V2[7]);
+    uint32_t po[4];
+    if (range_ok && __builtin_amdgcn_ballot_w64(nan || emin < -88) == 0) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) po[k] = hi_pair(ps[2 * k], ps[2 * k + 1]);
     } else {
+      po[0] = po[1] = po[2] = po[3] = 0u;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        if (off + j < valid) {
-          pp[off + j] = static_cast<uint16_t>(po[j >> 1] >> (16 * (j & 1)));
-          mp[off + j] = M2[j];
-          vp[off + j] = V2[j];
-        }
+        const float pn = adamw(bf16_at(P, j), bf16_at(G, j), M[j], V[j], sc, M2[j], V2[j]);
+        po[j >> 1] |= to_bf16(pn, r16_of(rp, j), kNearest) << (16 * (j & 1));
+      }
+    }
+    if (whole) {
+      st_stream16(pp + off, make_uint4(po[0], po[1], po[2], po[3]));
+      st_stream16(mp + off, make_uint4(__float_as_uint(M2[0]), __float_as_uint(M2[1]), __float_as_uint(M2[2]),
+                                       __float_as_uint(M2[3])));
+      st_stream16(mp + off + 4, make_uint4(__float_as_uint(M2[4]), __float_as_uint(M2[5]), __float_as_uint(M2[6]),
+                                           __float_as_uint(M2[7])));
+      st_stream16(vp + off, make_uint4(__float_as_uint(V2[0]), __float_as_uint(V2[1]), __float_as_uint(V2[2]),
+                                       __float_as_uint(V2[3])));
+      st_stream16(vp + off + 4, make_uint4(__float_as_uint(V2[4]), __float_as_uint(V2[5]), __float_as_uint(V2[6]),
+                                           __float_as_uint(V2[7])));
+    } else {
+      for (int j = 0; j < 8 && off + j < valid; ++j) {
+        pp[off + j] = static_cast<uint16_t>(po[j >> 1] >> (16 * (j & 1)));
+        mp[off + j] = M2[j];
+        vp[off + j] = V2[j];
       }
     }
   }
@@ -1253,8 +1291,15 @@ step_kernel(const DevTensor* __restrict__ list, int ntensors, int64_t total_bloc
         } else if (sc.param_round) block_bf16_full<true>(d, blk, lane, sc, range_ok != 0);
         else block_bf16_full<false>(d, blk, lane, sc, range_ok != 0);
       } else {
-        if (full) block_fp32<true>(d, blk, lane, valid, sc);
-        else block_fp32<false>(d, blk, lane, valid, sc);
+        const bool ro = range_ok != 0;
+        if (full) {
+          if (sc.param_round) block_fp32<true, false>(d, blk, lane, sc, ro);
+          else block_fp32<false, false>(d, blk, lane, sc, ro);
+        } else if (sc.param_round) {
+          block_fp32<true, true>(d, blk, lane, sc, ro, valid);
+        } else {
+          block_fp32<false, true>(d, blk, lane, sc, ro, valid);
+        }
       }
     }
   }

@@ -133,6 +133,7 @@ WORKLOADS = {
     "gptneo-6.7b": gptneo_6p7b,
     "many-4096": lambda: many_small(4096),
     "many-6151": lambda: many_small(6151),
+    "many-2000": lambda: many_small(2000),    # every tensor under 4096 elements: fp32 state
 }
 
 
