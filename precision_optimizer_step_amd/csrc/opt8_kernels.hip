@@ -1095,9 +1095,13 @@ __device__ __forceinline__ void block_1s_wide(const DevTensor& d, int64_t blk, i
   const uint64_t grp0 = static_cast<uint64_t>(d.index_base + e0) >> 3;
 #pragma unroll 1
   for (int r = 0; r < kGroups; ++r) {
+    if (!kFull && r * 512 >= valid) break;         // no lane has an element left
     const int off = r * 512 + lane * 8;
+    // a whole group moves with 16-byte accesses; only the one that straddles the
+    // end of a partial block goes element by element
+    const bool whole = kFull || off + 8 <= valid;
     float g[8], p[8], m1[8];
-    if constexpr (kFull) {
+    if (whole) {
       const uint4 G = ld_stream16(gp + off);
       const uint4 P = ld_stream16(pp + off);
 #pragma unroll
@@ -1158,7 +1162,7 @@ __device__ __forceinline__ void block_1s_wide(const DevTensor& d, int64_t blk, i
       po[j >> 1] |= to_bf16(pn, r16_of(rp, j), nearest) << (16 * (j & 1));
       if constexpr (kBf16State) mo[j >> 1] |= to_bf16(M2[j], r16_of(rm, j), false) << (16 * (j & 1));
     }
-    if constexpr (kFull) {
+    if (whole) {
       st_stream16(pp + off, make_uint4(po[0], po[1], po[2], po[3]));
       if constexpr (kBf16State) {
         st_stream16(static_cast<uint16_t*>(d.m) + e0 + off, make_uint4(mo[0], mo[1], mo[2], mo[3]));
