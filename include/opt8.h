@@ -142,17 +142,39 @@ typedef struct opt8_hparams {
  * upload them to the CURRENT device; idempotent, once per device.  If
  * signed_out / unsigned_out are non-NULL the fp32 tables are also copied to
  * those host arrays, before the upload, so a host without a GPU still gets
- * them (the call then returns OPT8_E_HIP).  Returns OPT8_OK or OPT8_E_HIP.   */
+ * them (the call then returns OPT8_E_HIP).  Returns OPT8_OK or OPT8_E_HIP.
+ * Defined by: "8-bit Optimizers via Block-wise Quantization", method bullets
+ * (non-linear 8-bit codes searched by binary search, decoded by lookup table)
+ * and innovations list (dynamic tree quantisation, extended to unipolar data
+ * for the unsigned table).  Outputs: signed_out[k], unsigned_out[k] = entry
+ * of code k, ascending; host arrays owned by the caller, written in full.   */
 int opt8_init_codebooks(float* signed_out, float* unsigned_out);
 
 /* Default state mode for a tensor of numel elements: OPT8_STATE_FP32 below
- * 4096 elements, OPT8_STATE_8BIT otherwise (the small-tensor fallback).      */
+ * 4096 elements, OPT8_STATE_8BIT otherwise (the small-tensor fallback).
+ * Defined by: "Stochastic rounding support for 8-bit optimizers", scoping
+ * comment (small tensors keep 32-bit state); the 4096 threshold is this
+ * library's choice.  Pure function; never fails.                            */
 int32_t opt8_default_mode(int64_t numel);
 
-/* One AdamW step over a list of n tensors, queued on hip_stream (a
+/* Defined by: "8-bit Optimizers via Block-wise Quantization", method bullets
+ * (block-wise absmax, dequantise -> 32-bit update -> requantise in registers);
+ * "Stochastic rounding support for 8-bit optimizers", feature request
+ * (stochastic rounding of the bf16 parameter) and scoping comment (opt-in,
+ * non-paged, no fp32 master copy, fp32 state for small tensors, the caller's
+ * stream); "[Feat]: Stochastic rounding of AdamW momentums", comment thread
+ * (fp32 Adam arithmetic, the p + value*exp_avg/denom update, bf16 momenta
+ * written with stochastic rounding).
+ *
+ * One AdamW step over a list of n tensors, queued on hip_stream (a
  * hipStream_t; NULL = the null stream) and asynchronous to the host.
- * Every descriptor and hyperparameter is validated first; on any error
- * nothing is queued and nothing is modified.  n == 0 is a no-op.  Tensors of
+ * Every descriptor and hyperparameter is validated first; on a validation
+ * error (every status but OPT8_E_HIP) nothing is queued and nothing is
+ * modified.  A step is up to four kernel launches, one per kind of tensor in
+ * the list (8-bit full blocks, bf16 state, fp32 state, 8-bit last partial
+ * blocks); if a launch fails (OPT8_E_HIP) the kinds launched before it have
+ * been queued and will step their tensors, and the message names them.
+ * n == 0 is a no-op.  Tensors of
  * different modes may be mixed.  Concurrent calls on different streams must
  * use disjoint buffers.  Device faults surface at the caller's next
  * synchronisation.  A stream that is being captured into a HIP graph is
@@ -189,7 +211,8 @@ int opt8_momentum_step(const opt8_tensor* tensors, int32_t n, const opt8_hparams
                        void* hip_stream);
 
 /* Message of the last failure on the calling thread ("" if none).  The
- * string is owned by the library and valid until the thread's next call.    */
+ * string is owned by the library and valid until the thread's next call.
+ * (Not from the pages: the error channel of this C ABI.)                    */
 const char* opt8_last_error(void);
 
 #ifdef __cplusplus

@@ -545,7 +545,9 @@ int run_step(int algo, const opt8_tensor* tensors, int32_t n, const opt8_hparams
   // one sub-list per kernel, each with its own block numbering: full blocks of
   // 8-bit tensors, bf16-state tensors, fp32-state tensors, and the partial last
   // block of 8-bit tensors
-  std::vector<DevTensor> list;
+  // host-side list, reused by the thread's later calls
+  thread_local std::vector<DevTensor> list;
+  list.clear();
   list.reserve(static_cast<size_t>(n) * 2);
   int count[kKinds] = {0, 0, 0, 0};
   int64_t blocks[kKinds] = {0, 0, 0, 0};
@@ -580,13 +582,28 @@ int run_step(int algo, const opt8_tensor* tensors, int32_t n, const opt8_hparams
   Slot* slot = nullptr;
   rc = acquire_slot(ds, list, stream, slot);
   if (rc != OPT8_OK) return rc;
+  DevTensor* dev_list = slot->dev;
   const StepScalars sc = make_scalars(*hp, algo, ds.pow);
+  static const char* const kKindName[kKinds] = {"8-bit full blocks", "bf16 state", "fp32 state",
+                                                "8-bit last partial blocks"};
+  std::string queued;
   for (int kind = 0; kind < kKinds; ++kind) {
     if (!count[kind]) continue;
     const int cap = ds.num_cu * ds.occ[sc.state_round != 0][algo][kind];
-    const hipError_t e = launch_step(static_cast<Kind>(kind), algo, slot->dev + first[kind], count[kind],
+    const hipError_t e = launch_step(static_cast<Kind>(kind), algo, dev_list + first[kind], count[kind],
                                      blocks[kind], sc, stream, cap);
-    if (e != hipSuccess) return hip_fail(e, "kernel launch");
+    if (e != hipSuccess) {
+      // launches queued before this one still read the slot: keep its event
+      // and stream current so a later call that reuses or rewrites it waits
+      if (!queued.empty()) {
+        (void)hipEventRecord(slot->done, stream);
+        slot->last_stream = stream;
+      }
+      return fail(OPT8_E_HIP, "kernel launch (%s) failed: %s; already queued: %s", kKindName[kind],
+                  hipGetErrorString(e), queued.empty() ? "nothing" : queued.c_str());
+    }
+    if (!queued.empty()) queued += ", ";
+    queued += kKindName[kind];
   }
   const hipError_t e = hipEventRecord(slot->done, stream);
   if (e != hipSuccess) return hip_fail(e, "hipEventRecord");

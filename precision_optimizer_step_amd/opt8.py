@@ -145,13 +145,67 @@ def _addr(x):
     return x.data_ptr()
 
 
+def _dtypes(*names):
+    import torch
+    return tuple(getattr(torch, n) for n in names if hasattr(torch, n))
+
+
+def _check_buffer(what, t, dtypes, need, device):
+    """A torch buffer the kernels will read or write `need` elements of."""
+    if t.dtype not in dtypes:
+        raise ValueError(f"{what}: dtype {t.dtype} not allowed here (expected one of "
+                         f"{', '.join(str(d) for d in dtypes)})")
+    if t.device != device:
+        raise ValueError(f"{what}: on {t.device}, but param is on {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{what}: must be contiguous")
+    if t.numel() < need:
+        raise ValueError(f"{what}: holds {t.numel()} elements, the step needs {need}")
+
+
 def make_tensor(param, grad, m, v, absmax_m=None, absmax_v=None, tensor_id=0,
                 mode=OPT8_STATE_8BIT, index_base=0, numel=None) -> opt8_tensor:
-    """Descriptor from torch tensors (or raw device addresses given as ints)."""
+    """Descriptor from torch tensors (or raw device addresses given as ints).
+
+    When torch tensors are given, each one is checked before the descriptor is
+    built (the library can check alignment and overlap only, and its kernels
+    trust the sizes): same device as param and on a GPU, contiguous, a dtype
+    that fits the state mode (param and grad bf16 or an int16 view of it;
+    8-bit state uint8 with float32 absmax; bf16 state bf16 or int16; fp32
+    state float32), and at least numel elements (ceil(numel / 2048) for the
+    absmax arrays).  v and absmax_v may be None (the one-state rules); absmax
+    arrays are required in 8-bit mode.  Raw int addresses are passed through
+    unchecked.  Raises ValueError on a mismatch.
+    """
+    tensors = [x for x in (param, grad, m, v, absmax_m, absmax_v) if x is not None]
     if numel is None:
         numel = param.numel()
+    numel = int(numel)
+    if tensors and not any(isinstance(x, int) for x in tensors):
+        if mode not in (OPT8_STATE_8BIT, OPT8_STATE_BF16_SR, OPT8_STATE_FP32):
+            raise ValueError(f"unknown state mode {mode}")
+        dev = param.device
+        half = _dtypes("bfloat16", "int16", "uint16")
+        state = {OPT8_STATE_8BIT: _dtypes("uint8"), OPT8_STATE_BF16_SR: half,
+                 OPT8_STATE_FP32: _dtypes("float32")}[mode]
+        _check_buffer("param", param, half, numel, dev)
+        _check_buffer("grad", grad, half, numel, dev)
+        _check_buffer("m", m, state, numel, dev)
+        if v is not None:
+            _check_buffer("v", v, state, numel, dev)
+        if mode == OPT8_STATE_8BIT:
+            nb = (numel + OPT8_BLOCK - 1) // OPT8_BLOCK
+            if absmax_m is None:
+                raise ValueError("absmax_m: required in 8-bit state mode")
+            _check_buffer("absmax_m", absmax_m, _dtypes("float32"), nb, dev)
+            if v is not None:
+                if absmax_v is None:
+                    raise ValueError("absmax_v: required in 8-bit state mode with a second moment")
+                _check_buffer("absmax_v", absmax_v, _dtypes("float32"), nb, dev)
+        if dev.type != "cuda":
+            raise ValueError(f"param: on {dev}; the step runs on a GPU")
     return opt8_tensor(_addr(param), _addr(grad), _addr(m), _addr(v), _addr(absmax_m),
-                       _addr(absmax_v), int(numel), int(index_base), int(tensor_id), int(mode))
+                       _addr(absmax_v), numel, int(index_base), int(tensor_id), int(mode))
 
 
 def tensor_array(descs) -> ctypes.Array:

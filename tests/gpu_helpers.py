@@ -115,7 +115,13 @@ def compare(name, got, want, kind, stats=None):
     if kind == "absmax":
         g = got.astype(np.float64)
         w = want.astype(np.float64)
+        # NaN on exactly the same blocks first (a comparison with NaN is always False)
+        nan_g, nan_w = np.isnan(g), np.isnan(w)
+        assert np.array_equal(nan_g, nan_w), f"{name}: NaN absmax at blocks " \
+            f"{np.flatnonzero(nan_g != nan_w)[:5]} on one side only"
+        g, w = g[~nan_w], w[~nan_w]
         bad = np.abs(g - w) > ABSMAX_RTOL * np.abs(w)
+        bad |= np.isinf(g) != np.isinf(w)
         assert not bad.any(), f"{name}: {int(bad.sum())} absmax beyond 1e-6 relative, e.g. " \
             f"{g[bad][:3]} vs {w[bad][:3]}"
         diff = int(np.sum(got.view(np.uint32) != want.view(np.uint32)))

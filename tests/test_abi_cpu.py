@@ -242,3 +242,68 @@ def test_one_state_rules_ignore_v_and_eps(L, name, fn):
     expect(run([fake_tensor(0)], hp=opt8.make_hparams(1e-4, step=0)), opt8.OPT8_E_HPARAM)
     expect(run([fake_tensor(0, mode=7)]), opt8.OPT8_E_MODE)
     assert run([], n=0) == opt8.OPT8_OK
+
+
+# ----------------------------------------------------------------------------- binding checks
+def _bufs(n=5000, mode=opt8.OPT8_STATE_8BIT, one_state=False):
+    import torch
+    nb = (n + 2047) // 2048
+    sd = {opt8.OPT8_STATE_8BIT: torch.uint8, opt8.OPT8_STATE_BF16_SR: torch.bfloat16,
+          opt8.OPT8_STATE_FP32: torch.float32}[mode]
+    b = dict(param=torch.zeros(n, dtype=torch.bfloat16), grad=torch.zeros(n, dtype=torch.bfloat16),
+             m=torch.zeros(n, dtype=sd), v=None if one_state else torch.zeros(n, dtype=sd),
+             absmax_m=None, absmax_v=None)
+    if mode == opt8.OPT8_STATE_8BIT:
+        b["absmax_m"] = torch.zeros(nb, dtype=torch.float32)
+        if not one_state:
+            b["absmax_v"] = torch.zeros(nb, dtype=torch.float32)
+    return b
+
+
+def _refused(match, mode=opt8.OPT8_STATE_8BIT, **over):
+    b = _bufs(mode=mode, one_state=over.pop("one_state", False))
+    b.update(over)
+    numel = b.pop("numel", None)
+    with pytest.raises(ValueError, match=match):
+        opt8.make_tensor(mode=mode, numel=numel, **b)
+
+
+def test_make_tensor_refuses_mismatched_buffers():
+    """Every check make_tensor runs on torch buffers before building a descriptor: the
+    kernels trust the sizes, so a wrong dtype, length, layout or device must stop here."""
+    import torch
+    n = 5000
+    M8, BF, F32 = opt8.OPT8_STATE_8BIT, opt8.OPT8_STATE_BF16_SR, opt8.OPT8_STATE_FP32
+    # dtype per mode
+    _refused("param: dtype", param=torch.zeros(n, dtype=torch.float32))
+    _refused("grad: dtype", grad=torch.zeros(n, dtype=torch.float16))
+    _refused("m: dtype", m=torch.zeros(n, dtype=torch.float32))               # fp32 state in 8-bit mode
+    _refused("v: dtype", mode=BF, v=torch.zeros(n, dtype=torch.uint8))        # codes in bf16 mode
+    _refused("m: dtype", mode=F32, m=torch.zeros(n, dtype=torch.uint8))       # the 4x overrun case
+    _refused("absmax_m: dtype", absmax_m=torch.zeros(3, dtype=torch.float64))
+    # sizes
+    _refused("grad: holds 4999", grad=torch.zeros(n - 1, dtype=torch.bfloat16))
+    _refused("v: holds 100", v=torch.zeros(100, dtype=torch.uint8))
+    _refused("absmax_v: holds 2", absmax_v=torch.zeros(2, dtype=torch.float32))
+    _refused("param: holds 5000", numel=n + 1)
+    # layout
+    _refused("m: must be contiguous", m=torch.zeros(2 * n, dtype=torch.uint8)[::2])
+    # missing absmax in 8-bit mode
+    _refused("absmax_m: required", absmax_m=None)
+    _refused("absmax_v: required", absmax_v=None)
+    # device: CPU buffers are refused last, so every check above ran on them
+    _refused("runs on a GPU")
+    _refused("runs on a GPU", mode=BF)
+    _refused("runs on a GPU", mode=F32)
+    _refused("runs on a GPU", one_state=True)
+    with pytest.raises(ValueError, match="unknown state mode"):
+        opt8.make_tensor(**_bufs(), mode=7)
+    # int16 views of bf16 data and uint16 patterns pass the dtype checks
+    b = _bufs(mode=BF)
+    b["param"] = b["param"].view(torch.int16)
+    b["m"] = b["m"].view(torch.int16)
+    with pytest.raises(ValueError, match="runs on a GPU"):
+        opt8.make_tensor(mode=BF, **b)
+    # raw addresses are passed through unchecked
+    d = opt8.make_tensor(1 << 40, 2 << 40, 3 << 40, 4 << 40, 5 << 40, 6 << 40, numel=n)
+    assert d.numel == n and d.param == 1 << 40

@@ -1,23 +1,44 @@
-"""Full-size parameter lists on the GPU, checked on sampled blocks.
+"""Every full-size parameter list, run as its configuration states, checked
+against the oracle after every step.
 
-The whole list (up to the 6.7B-shaped one, ~40 GB resident) is stepped in one
-call, the launch the benchmark times.  The inputs of sampled blocks are copied
-to the host before the step; the oracle then steps each sampled block alone
-(blocks are independent: the block absmax never crosses a block and the random
-bits depend on the global element index), and its outputs are compared with
-the GPU's for those blocks.
+  gptneo-6.7b       8-bit state, 5 steps, lr 1.2e-4, wd 0.1, seed 1234,
+                    gradients N(0, 1e-3) with 0.01% of them x100 (~40 GB on the device)
+  lm-1.5b           3 steps, lr 1.5e-4, wd 0.01: embedding rows 95% zero and 5%
+                    N(0, 1e-2), LayerNorm gradients N(0, 1e-4), the rest N(0, 1e-3)
+                    with 0.01% x1000 (whole zero blocks: the zero-absmax path)
+  gptneo-2.7b       3 steps, lr 3.2e-4, wd 0.1, 8-bit state (fp32 under 4096 elements)
+  gptneo-2.7b-bf16  the same list with bf16 state written by stochastic rounding
+  gpt2-350m         3 steps, lr 6e-4, wd 0.1, gradients N(0, 1e-3/sqrt(fan_in)):
+                    EVERY element of every tensor, the embedding included
+
+Each list starts from the zero state (absmax 0 and zero codes, or zero bf16 /
+fp32 moments) with its parameter recipe, and gets fresh gradients at every
+step, generated on the device from (seed, step, tensor id).  The whole list is
+stepped in one call, the launch the benchmark times.  The sampled blocks --
+every tensor's first and last block and 64 others drawn at random (every
+block of gpt2-350m) -- are copied to the host before the first step, and the
+oracle carries its own state for them from there: after every step, the
+zero-state first step included, the GPU's parameters, codes and absmax
+values for those blocks must match the oracle's within the comparison bar.
+The oracle steps each run of consecutive sampled blocks alone, which is exact
+because blocks are independent; it runs in worker processes.
 """
+
+import time
 
 import numpy as np
 import pytest
 import torch
 
 import oracle
-from gpu_helpers import BLOCK, build_list, compare_state, descriptors, log, sample_blocks, snapshot
+from gpu_helpers import BLOCK, _np, compare_state, log
+from oracle_pool import OraclePool, hp_fields, runs, split_runs
 from precision_optimizer_step_amd import opt8
-from workloads import shapes
+from workloads import gen, shapes
 
 pytestmark = pytest.mark.gpu
+
+SAMPLES_PER_TENSOR = 64
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -28,30 +49,149 @@ def device():
     opt8.opt8_init_codebooks()
 
 
-@pytest.mark.parametrize("name", ["gptneo-6.7b", "gptneo-2.7b", "gptneo-2.7b-bf16", "lm-1.5b", "gpt2-350m"])
-def test_full_size_list_on_sampled_blocks(name):
+@pytest.fixture(scope="module")
+def pool():
+    p = OraclePool()
+    yield p
+    p.close()
+
+
+def _mode_of(w, spec):
+    if w.state_mode == "bf16":
+        return oracle.MODE_BF16_SR
+    return opt8.opt8_default_mode(spec.numel)
+
+
+def _state_dtype(mode):
+    return {oracle.MODE_8BIT: np.uint8, oracle.MODE_BF16_SR: np.uint16, oracle.MODE_FP32: np.float32}[mode]
+
+
+class Sampled:
+    """One tensor on the device, and the blocks of it the oracle follows."""
+
+    def __init__(self, w, tid, blocks_per_tensor, rng, dev):
+        spec = w.tensors[tid]
+        self.tid, self.spec, self.n = tid, spec, spec.numel
+        self.mode = _mode_of(w, spec)
+        n = self.n
+        nb = (n + BLOCK - 1) // BLOCK
+        self.P = torch.empty(n, dtype=torch.bfloat16, device=dev)
+        gen.param_init_device(spec, w, tid, self.P)
+        self.G = torch.empty(n, dtype=torch.bfloat16, device=dev)
+        self.AM = self.AV = None
+        if self.mode == oracle.MODE_8BIT:
+            self.M = torch.full((n,), 127, dtype=torch.uint8, device=dev)
+            self.V = torch.zeros(n, dtype=torch.uint8, device=dev)
+            self.AM = torch.zeros(nb, dtype=torch.float32, device=dev)
+            self.AV = torch.zeros(nb, dtype=torch.float32, device=dev)
+        else:
+            dt = torch.bfloat16 if self.mode == oracle.MODE_BF16_SR else torch.float32
+            self.M = torch.zeros(n, dtype=dt, device=dev)
+            self.V = torch.zeros(n, dtype=dt, device=dev)
+        if blocks_per_tensor is None or nb <= blocks_per_tensor + 2:
+            blocks = list(range(nb))
+        else:
+            inner = rng.choice(np.arange(1, nb - 1), size=blocks_per_tensor, replace=False)
+            blocks = sorted({0, nb - 1} | set(int(b) for b in inner))
+        self.whole = len(blocks) == nb
+        self.blocks = blocks
+        if self.whole:
+            self.eidx = self.bidx = None
+        else:
+            self.eidx = torch.cat([torch.arange(b * BLOCK, min(n, (b + 1) * BLOCK), device=dev) for b in blocks])
+            self.bidx = torch.tensor(blocks, dtype=torch.int64, device=dev)
+        # pieces: (first block, block count, element range and block range in the gathered arrays)
+        self.pieces = []
+        pos_b = {b: i for i, b in enumerate(blocks)}
+        for a, c in split_runs(runs(blocks), 2048):
+            e0 = pos_b[a] * BLOCK
+            e1 = e0 + min(n, (a + c) * BLOCK) - a * BLOCK
+            self.pieces.append((a, c, e0, e1, pos_b[a], pos_b[a] + c))
+
+    def desc(self):
+        return opt8.make_tensor(self.P, self.G, self.M, self.V, self.AM, self.AV, tensor_id=self.tid,
+                                mode=self.mode)
+
+    def gather(self, t, per_block, dtype):
+        if t is None:
+            return None
+        if not self.whole:
+            t = t[self.bidx if per_block else self.eidx]
+        return _np(t, dtype)
+
+    def read(self):
+        sd = _state_dtype(self.mode)
+        return [self.gather(self.P, False, np.uint16), self.gather(self.M, False, sd),
+                self.gather(self.V, False, sd), self.gather(self.AM, True, np.float32),
+                self.gather(self.AV, True, np.float32)]
+
+
+def _oracle_items(samples, carried, grads, hp):
+    items, where = [], []
+    fields = hp_fields(hp)
+    for s, (p, m, v, am, av), g in zip(samples, carried, grads):
+        for a, c, e0, e1, b0, b1 in s.pieces:
+            items.append((0, s.mode, fields, p[e0:e1], g[e0:e1], m[e0:e1], v[e0:e1],
+                          None if am is None else am[b0:b1], None if av is None else av[b0:b1],
+                          s.tid, a * BLOCK))
+            where.append(s)
+    return items, where
+
+
+def _assemble(samples, where, results):
+    out = {}
+    for s, r in zip(where, results):
+        out.setdefault(s.tid, []).append(r)
+    assembled = []
+    for s in samples:
+        parts = out[s.tid]
+        cat = [None if parts[0][k] is None else np.concatenate([x[k] for x in parts]) for k in range(5)]
+        assembled.append(cat)
+    return assembled
+
+
+CONFIGS = [("gptneo-6.7b", SAMPLES_PER_TENSOR), ("lm-1.5b", SAMPLES_PER_TENSOR),
+           ("gptneo-2.7b", SAMPLES_PER_TENSOR), ("gptneo-2.7b-bf16", SAMPLES_PER_TENSOR), ("gpt2-350m", None)]
+
+
+@pytest.mark.timeout(1200)
+@pytest.mark.parametrize("name,per_tensor", CONFIGS)
+def test_full_size_list_as_configured(name, per_tensor, pool):
     w = shapes.get(name)
-    log(f"{name}: building {len(w.tensors)} tensors, {w.numel} elements on the device")
-    lst = build_list(w)
+    dev = torch.device("cuda:0")
+    t0 = time.time()
+    rng = np.random.default_rng(2024)
+    samples = [Sampled(w, tid, per_tensor, rng, dev) for tid in range(len(w.tensors))]
+    arr = opt8.tensor_array(s.desc() for s in samples)
     torch.cuda.synchronize()
-    rng = np.random.default_rng(1)
-    blocks = sample_blocks(lst, 2, rng)
-    before = snapshot(lst, blocks)
-    hp = oracle.Hparams(lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps,
-                        weight_decay=w.weight_decay, step=2, seed=w.seed)
-    arr = descriptors(lst)
-    opt8.opt8_adamw_step(arr, opt8.make_hparams(hp.lr, hp.beta1, hp.beta2, hp.eps, hp.weight_decay,
-                                                hp.step, hp.seed))
-    torch.cuda.synchronize()
-    after = snapshot(lst, blocks)
-    log(f"{name}: stepped; checking {len(blocks)} sampled blocks against the oracle")
-    stats = {}
-    for (i, b), x, y in zip(blocks, before, after):
-        t = lst[i]
-        want = oracle.step_tensor(t["mode"], x["p"], x["g"], x["m"], x["v"], x["am"], x["av"], hp,
-                                  tensor_id=t["tid"], index_base=b * BLOCK)
-        got = [y["p"], y["m"], y["v"], y["am"], y["av"]]
-        compare_state(f"{name}/t{t['tid']}/b{b}", got, want, t["mode"], stats)
-    log(f"{name}: mismatching elements over sampled blocks: {sum(stats.values())}")
-    del lst, arr
+    checked_elems = sum(p[3] - p[2] for s in samples for p in s.pieces)
+    log(f"{name}: {len(samples)} tensors, {w.numel} elements from the zero state, {w.steps} steps; "
+        f"the oracle follows {sum(len(s.blocks) for s in samples)} blocks ({checked_elems} elements); "
+        f"built in {time.time() - t0:.1f}s")
+    carried = [s.read() for s in samples]        # the parameters and the zero state, as the oracle starts
+    per_step = []
+    for step in range(1, w.steps + 1):
+        t1 = time.time()
+        for s in samples:
+            gen.grad_init_device(s.spec, w, step, s.tid, s.G)
+        grads = [s.gather(s.G, False, np.uint16) for s in samples]
+        hp = oracle.Hparams(lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps, weight_decay=w.weight_decay,
+                            step=step, seed=w.seed)
+        opt8.opt8_adamw_step(arr, opt8.make_hparams(hp.lr, hp.beta1, hp.beta2, hp.eps, hp.weight_decay,
+                                                    hp.step, hp.seed))
+        torch.cuda.synchronize()
+        got = [s.read() for s in samples]
+        items, where = _oracle_items(samples, carried, grads, hp)
+        want = _assemble(samples, where, pool.step(items))
+        stats = {}
+        for s, x, y in zip(samples, got, want):
+            compare_state(f"{name}/step{step}/t{s.tid}", x, y, s.mode, stats)
+        zero_blocks = sum(int(np.count_nonzero(y[3] == 0)) for y in want if y[3] is not None)
+        mism = sum(stats.values())
+        per_step.append(mism)
+        log(f"{name}: step {step}: {checked_elems} elements checked, {mism} differ from the oracle "
+            f"({zero_blocks} sampled blocks with a zero first-moment absmax); {time.time() - t1:.1f}s")
+        carried = want
+    log(f"{name}: mismatching elements per step {per_step}")
+    del samples, arr
     torch.cuda.empty_cache()
