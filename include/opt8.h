@@ -78,7 +78,8 @@ typedef enum {
   OPT8_OK = 0,
   OPT8_E_NULL = -1,      /* a required pointer is NULL                               */
   OPT8_E_ALIGN = -2,     /* param/grad/m/v not 16-byte aligned, absmax not 4-byte    */
-  OPT8_E_SIZE = -3,      /* n < 0, numel <= 0 or > 2^42, bad index_base              */
+  OPT8_E_SIZE = -3,      /* n < 0 (> 4096 without allocation), numel <= 0 or > 2^42, */
+                         /*   bad index_base                                         */
   OPT8_E_MODE = -4,      /* unknown state mode, rounding mode or state rounding      */
   OPT8_E_HPARAM = -5,    /* lr/betas/eps/weight_decay/step outside their ranges      */
   OPT8_E_ALIAS = -6,     /* two buffers of the list overlap                          */
@@ -183,6 +184,26 @@ int32_t opt8_default_mode(int64_t numel);
  * graph replay would not follow.  Returns OPT8_OK or a negative opt8_status. */
 int opt8_adamw_step(const opt8_tensor* tensors, int32_t n, const opt8_hparams* hp,
                     void* hip_stream);
+
+/* The step of opt8_adamw_step for callers that cannot allocate memory
+ * (code paths that must not call hipMalloc, tight serving or training loops,
+ * harnesses that forbid allocation).  Same arguments, validation, kernels,
+ * results and status codes as opt8_adamw_step.  The difference is where the
+ * per-kernel descriptor lists live: opt8_adamw_step keeps them in device
+ * buffers it allocates (and grows) on first use; this entry point writes
+ * them into a fixed array in the library's device image ("scratch", 8192
+ * descriptors of 80 bytes = 640 KiB on each device the library runs on,
+ * held until the process ends) with one host-to-device copy on hip_stream,
+ * and calls no hipMalloc, hipFree or other allocating routine.
+ * Limit: n <= 4096 tensors; a longer list returns OPT8_E_SIZE with nothing
+ * queued.  Every call on a device shares that device's array, which keeps
+ * the last call's descriptors: calls on one stream are ordered by it, but
+ * calls that overlap on one device (different streams with no ordering
+ * between them) race on the array and must be ordered by the caller.  A
+ * stream under graph capture is refused with OPT8_E_CAPTURE, as for
+ * opt8_adamw_step.                                                          */
+int opt8_adamw_step_noalloc(const opt8_tensor* tensors, int32_t n, const opt8_hparams* hp,
+                            void* hip_stream);
 
 /* One-state update rules on the same state machinery (codebook, block absmax,
  * state modes, rounding, Random bits; the SIGNED codebook holds the state in

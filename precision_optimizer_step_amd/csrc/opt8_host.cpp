@@ -390,6 +390,7 @@ struct Slot {
 struct DeviceState {
   bool init = false;
   int num_cu = 0;
+  DevTensor* scratch = nullptr;      // device address of the no-allocation descriptor array
   int occ[2][kAlgos][kKinds] = {};   // [state_round][algo][kind]
   Slot slots[kSlots];
   uint64_t clock = 0;
@@ -488,6 +489,9 @@ extern "C" int opt8_init_codebooks(float* signed_out, float* unsigned_out) {
   if (ds.init) return OPT8_OK;
   hipError_t e = upload_tables(t.bytes);
   if (e != hipSuccess) return hip_fail(e, "upload of codebooks");
+  // this device's copy of the descriptor scratch (each device has its own address)
+  e = scratch_address(&ds.scratch);
+  if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
   e = hipDeviceGetAttribute(&ds.num_cu, hipDeviceAttributeMultiprocessorCount, dev);
   if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute(CU count)");
   for (int sr = 0; sr < 2; ++sr)
@@ -515,11 +519,17 @@ namespace opt8 {
 namespace {
 
 // One step of update rule `algo` over a tensor list (every entry point).
-int run_step(int algo, const opt8_tensor* tensors, int32_t n, const opt8_hparams* hp, void* hip_stream) {
+// noalloc: the descriptor lists go to the device's fixed scratch array with
+// one copy per call instead of the cached, allocated slots.
+int run_step(int algo, const opt8_tensor* tensors, int32_t n, const opt8_hparams* hp, void* hip_stream,
+             bool noalloc = false) {
   t_error.clear();
   if (!hp) return fail(OPT8_E_NULL, "hparams is NULL");
   if (n < 0) return fail(OPT8_E_SIZE, "n must be >= 0 (got %d)", n);
   if (n > 0 && !tensors) return fail(OPT8_E_NULL, "tensor list is NULL");
+  if (noalloc && n > kNoAllocMaxTensors)
+    return fail(OPT8_E_SIZE, "the no-allocation entry point takes at most %d tensors (got %d)",
+                kNoAllocMaxTensors, n);
   const bool two_state = algo == kAdamW;
   int rc = validate_hparams(*hp, algo);
   if (rc != OPT8_OK) return rc;
@@ -580,9 +590,19 @@ int run_step(int algo, const opt8_tensor* tensors, int32_t n, const opt8_hparams
     }
   }
   Slot* slot = nullptr;
-  rc = acquire_slot(ds, list, stream, slot);
-  if (rc != OPT8_OK) return rc;
-  DevTensor* dev_list = slot->dev;
+  DevTensor* dev_list = nullptr;
+  if (noalloc) {
+    // ordered on the stream after the work queued before it; calls on other
+    // streams that are not ordered with this one race on the array
+    const hipError_t e = hipMemcpyAsync(ds.scratch, list.data(), list.size() * sizeof(DevTensor),
+                                        hipMemcpyHostToDevice, stream);
+    if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync(descriptors to scratch)");
+    dev_list = ds.scratch;
+  } else {
+    rc = acquire_slot(ds, list, stream, slot);
+    if (rc != OPT8_OK) return rc;
+    dev_list = slot->dev;
+  }
   const StepScalars sc = make_scalars(*hp, algo, ds.pow);
   static const char* const kKindName[kKinds] = {"8-bit full blocks", "bf16 state", "fp32 state",
                                                 "8-bit last partial blocks"};
@@ -595,7 +615,7 @@ int run_step(int algo, const opt8_tensor* tensors, int32_t n, const opt8_hparams
     if (e != hipSuccess) {
       // launches queued before this one still read the slot: keep its event
       // and stream current so a later call that reuses or rewrites it waits
-      if (!queued.empty()) {
+      if (!queued.empty() && slot) {
         (void)hipEventRecord(slot->done, stream);
         slot->last_stream = stream;
       }
@@ -605,6 +625,7 @@ int run_step(int algo, const opt8_tensor* tensors, int32_t n, const opt8_hparams
     if (!queued.empty()) queued += ", ";
     queued += kKindName[kind];
   }
+  if (!slot) return OPT8_OK;
   const hipError_t e = hipEventRecord(slot->done, stream);
   if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
   slot->last_stream = stream;
@@ -617,6 +638,11 @@ int run_step(int algo, const opt8_tensor* tensors, int32_t n, const opt8_hparams
 extern "C" int opt8_adamw_step(const opt8_tensor* tensors, int32_t n, const opt8_hparams* hp,
                                void* hip_stream) {
   return run_step(kAdamW, tensors, n, hp, hip_stream);
+}
+
+extern "C" int opt8_adamw_step_noalloc(const opt8_tensor* tensors, int32_t n, const opt8_hparams* hp,
+                                       void* hip_stream) {
+  return run_step(kAdamW, tensors, n, hp, hip_stream, true);
 }
 
 extern "C" int opt8_lion_step(const opt8_tensor* tensors, int32_t n, const opt8_hparams* hp,

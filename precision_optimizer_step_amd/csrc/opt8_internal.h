@@ -87,8 +87,17 @@ static_assert(kOffPairU + 2048 <= kOffFloor + static_cast<int>(kKeyLo) &&
 
 enum class Kind : int { k8bit = 0, kBf16 = 1, kFp32 = 2, k8bitTail = 3 };
 
+// Descriptor scratch of the entry point that allocates nothing: a fixed
+// device array in opt8_kernels.hip, one copy per device, holding the
+// per-kernel descriptor lists of one call (a tensor is at most two entries:
+// its full 8-bit blocks and its partial last block).
+constexpr int kNoAllocMaxTensors = 4096;
+constexpr int kScratchDescs = 2 * kNoAllocMaxTensors;
+
 // Kernel side (opt8_kernels.hip).
 hipError_t upload_tables(const uint8_t* host_tables);   // kTableBytesSR, to the current device
+// Device address of the descriptor scratch on the current device (taken once per device).
+hipError_t scratch_address(DevTensor** out);
 // The 8-bit kinds take the stochastic-state kernels when sc.state_round is set.
 hipError_t launch_step(Kind kind, int algo, const DevTensor* dev_list, int ntensors,
                        int64_t total_blocks, const StepScalars& sc, hipStream_t stream, int grid_cap);

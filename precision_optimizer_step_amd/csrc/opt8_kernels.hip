@@ -1353,8 +1353,21 @@ int occupancy_algo(int algo) {
 
 }  // namespace
 
+// Descriptor lists of the entry point that allocates nothing: 8192
+// descriptors of 80 bytes (640 KiB) per device, held until the process ends.
+// In host code the array's name is only a host-side stand-in; kernels get
+// its device address, taken below with hipGetSymbolAddress.
+static __device__ __align__(256) DevTensor scratch[kScratchDescs];
+
 hipError_t upload_tables(const uint8_t* host_tables) {
   return hipMemcpyToSymbol(HIP_SYMBOL(g_tables), host_tables, kTableBytesSR, 0, hipMemcpyHostToDevice);
+}
+
+hipError_t scratch_address(DevTensor** out) {
+  void* ptr = nullptr;
+  const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+  *out = e == hipSuccess ? static_cast<DevTensor*>(ptr) : nullptr;
+  return e;
 }
 
 hipError_t launch_step(Kind kind, int algo, const DevTensor* list, int n, int64_t total_blocks,

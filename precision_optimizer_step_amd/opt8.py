@@ -92,7 +92,7 @@ def lib() -> ctypes.CDLL:
         L.opt8_init_codebooks.restype = ctypes.c_int
         L.opt8_default_mode.argtypes = [ctypes.c_int64]
         L.opt8_default_mode.restype = ctypes.c_int32
-        for name in ("opt8_adamw_step", "opt8_lion_step", "opt8_momentum_step"):
+        for name in ("opt8_adamw_step", "opt8_adamw_step_noalloc", "opt8_lion_step", "opt8_momentum_step"):
             fn = getattr(L, name)
             fn.argtypes = [ctypes.POINTER(opt8_tensor), ctypes.c_int32,
                            ctypes.POINTER(opt8_hparams), ctypes.c_void_p]
@@ -246,6 +246,12 @@ def opt8_adamw_step(tensors, hp: opt8_hparams, stream=None, n=None, check: bool 
     torch stream (the null stream if torch is not in use).
     """
     return _run(lib().opt8_adamw_step, tensors, hp, stream, n, check)
+
+
+def opt8_adamw_step_noalloc(tensors, hp: opt8_hparams, stream=None, n=None, check: bool = True) -> int:
+    """opt8_adamw_step without any allocation (descriptors in the library's fixed device
+    array, at most 4096 tensors; calls that overlap on one device race on it)."""
+    return _run(lib().opt8_adamw_step_noalloc, tensors, hp, stream, n, check)
 
 
 def opt8_lion_step(tensors, hp: opt8_hparams, stream=None, n=None, check: bool = True) -> int:

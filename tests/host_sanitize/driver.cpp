@@ -285,6 +285,49 @@ int main() {
     CHECK(step(huge, h1) == OPT8_OK);
   }
 
+  // ---------------------------------------------------------------- entry point without allocation
+  {
+    CHECK(g.scratch_queries == 1);            // the scratch address was taken once, at init
+    auto noalloc = [](const std::vector<opt8_tensor>& ts, const opt8_hparams& h, void* stream = nullptr) {
+      return opt8_adamw_step_noalloc(ts.data(), static_cast<int32_t>(ts.size()), &h, stream);
+    };
+    std::vector<opt8_tensor> mixed = {tensor(300, 5000, OPT8_STATE_8BIT, 0), tensor(301, 9000, OPT8_STATE_BF16_SR, 1),
+                                      tensor(302, 100, OPT8_STATE_FP32, 2), tensor(303, 4096, OPT8_STATE_8BIT, 3)};
+    std::vector<opt8_tensor> big;
+    for (int i = 0; i < 4096; ++i) big.push_back(tensor(400 + i, 2048 + 7, OPT8_STATE_8BIT, static_cast<uint32_t>(i)));
+    const long mallocs = g.mallocs, host_mallocs = g.host_mallocs, frees = g.frees, syncs = g.event_syncs;
+    for (int round = 0; round < 3; ++round) {
+      for (const auto* L : {&mixed, &big}) {
+        g.launches.clear();
+        const long up = g.uploads;
+        CHECK(noalloc(*L, h1) == OPT8_OK);
+        CHECK(g.uploads == up + 1);           // one copy into the scratch per call, never cached
+        bool in_scratch = !g.launches.empty();
+        for (const auto& x : g.launches)
+          in_scratch = in_scratch && x.ok && x.list >= g.scratch_lo && x.list < g.scratch_hi;
+        CHECK(in_scratch);                    // every launch reads the scratch array
+      }
+    }
+    CHECK(g.launches.size() == 2 && g.launches[0].n == 4096 && g.launches[1].n == 4096);   // 4096 + 4096 tails
+    CHECK(g.mallocs == mallocs && g.host_mallocs == host_mallocs && g.frees == frees);   // nothing allocated
+    CHECK(g.event_syncs == syncs);            // and no waiting on the host
+    big.push_back(tensor(400 + 4096, 4096, OPT8_STATE_8BIT, 4096));
+    g.launches.clear();
+    const long up = g.uploads;
+    CHECK(noalloc(big, h1) == OPT8_E_SIZE);   // over the limit: refused, nothing queued
+    CHECK(g.launches.empty() && g.uploads == up);
+    CHECK(std::strstr(opt8_last_error(), "at most 4096") != nullptr);
+    g.capturing = true;
+    CHECK(noalloc(mixed, h1) == OPT8_E_CAPTURE);
+    g.capturing = false;
+    std::vector<opt8_tensor> dup = mixed;
+    dup[2].tensor_id = 0;
+    CHECK(noalloc(dup, h1) == OPT8_E_DUPID);  // the same validation as opt8_adamw_step
+    CHECK(g.launches.empty() && g.uploads == up);
+    // the cached entry point still works alongside
+    CHECK(step(mixed, h1) == OPT8_OK);
+  }
+
   if (failures) {
     std::printf("%d host checks failed\n", failures);
     return 1;

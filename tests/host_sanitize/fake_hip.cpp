@@ -76,6 +76,7 @@ hipError_t hipFree(void* ptr) {
 
 hipError_t hipHostMalloc(void** ptr, size_t size, unsigned) {
   *ptr = std::malloc(size);
+  ++g.host_mallocs;
   return hipSuccess;
 }
 
@@ -108,6 +109,7 @@ hipError_t upload_tables(const uint8_t* host_tables) {
 hipError_t launch_step(Kind kind, int algo, const DevTensor* list, int n, int64_t total_blocks,
                        const StepScalars& sc, hipStream_t, int grid_cap) {
   fake::Launch L;
+  L.list = list;
   L.kind = static_cast<int>(kind);
   L.algo = algo;
   L.n = n;
@@ -130,5 +132,16 @@ hipError_t launch_step(Kind kind, int algo, const DevTensor* list, int n, int64_
 }
 
 int occupancy_per_cu(Kind, int, bool) { return 3; }
+
+// The stand-in for the device's descriptor scratch: a static host array of
+// the same size, so ASan checks every descriptor written into it.
+hipError_t scratch_address(DevTensor** out) {
+  static DevTensor fake_scratch[kScratchDescs];
+  *out = fake_scratch;
+  g.scratch_lo = fake_scratch;
+  g.scratch_hi = fake_scratch + kScratchDescs;
+  ++g.scratch_queries;
+  return hipSuccess;
+}
 
 }  // namespace opt8

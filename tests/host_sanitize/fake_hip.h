@@ -10,6 +10,7 @@ namespace fake {
 
 struct Launch {
   int kind = 0, algo = 0, n = 0, grid_cap = 0;
+  const void* list = nullptr;
   int64_t total_blocks = 0, numel = 0;
   opt8::StepScalars sc{};
   std::vector<uint32_t> ids;
@@ -22,6 +23,9 @@ struct State {
   bool capturing = false;
   bool fail_malloc = false;
   long mallocs = 0, frees = 0, uploads = 0, events = 0, event_syncs = 0, stream_waits = 0;
+  long host_mallocs = 0, scratch_queries = 0;
+  const void* scratch_lo = nullptr;   // extent of the stand-in descriptor scratch
+  const void* scratch_hi = nullptr;
   long table_uploads = 0;
   uint32_t table_sum = 0;
   std::vector<Launch> launches;

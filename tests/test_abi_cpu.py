@@ -35,8 +35,8 @@ def declared_functions():
 
 def test_library_exports_every_declared_symbol(L):
     names = declared_functions()
-    assert names == ["opt8_adamw_step", "opt8_default_mode", "opt8_init_codebooks", "opt8_last_error",
-                     "opt8_lion_step", "opt8_momentum_step"]
+    assert names == ["opt8_adamw_step", "opt8_adamw_step_noalloc", "opt8_default_mode", "opt8_init_codebooks",
+                     "opt8_last_error", "opt8_lion_step", "opt8_momentum_step"]
     out = subprocess.run(["nm", "-D", "--defined-only", opt8.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = set(re.findall(r"\bT (opt8_\w+)", out))
