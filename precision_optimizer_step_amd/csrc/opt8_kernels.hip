@@ -746,14 +746,23 @@ __device__ __forceinline__ void block_bf16_full(const DevTensor& d, int64_t blk,
 }
 
 // ----------------------------------------------------------------------------- fp32 state
-// The fallback for small tensors.  Each 8-element group takes the fast exact
-// sequences under the same per-group check as the bf16-state kernel (no NaN
-// result, non-zero m2, v2 and m2/den at or above 2^-89, the host's range for
-// eps and the corrections), else the plain IEEE operations; the moments are
-// stored as computed.  Whole groups move with 16-byte accesses; with kPartial
-// (the last block of a tensor holding `valid` elements) the groups past the
-// end are skipped and the one that straddles it is read and written element
-// by element with zeros in the rest.
+// The fallback for small tensors.  Lane l of a group of 512 elements takes two
+// quads, elements 4l..4l+3 and 256+4l..256+4l+3, so every access instruction
+// of the wave covers one contiguous segment: 8-byte accesses of the bf16
+// gradient and parameter (512 B per instruction) and 16-byte accesses of the
+// fp32 moments (1 KiB).  The random words follow the global element index: a
+// quad is half of an 8-element Philox group, so lane pair (2m, 2m+1) needs
+// groups m and m+32 of the 512; the even lane computes the first, the odd lane
+// the second, and each hands its neighbour the two words of the other's quad.
+// Each group of a lane takes the fast exact sequences under the same check as
+// the bf16-state kernel (no NaN result, non-zero m2, v2 and m2/den at or above
+// 2^-89, the host's range for eps and the corrections), else the plain IEEE
+// operations; the moments are stored as computed.  With kPartial (the last
+// block of a tensor holding `valid` elements) the groups past the end are
+// skipped and the one that straddles it is read and written element by element
+// with zeros in the rest.
+__device__ __forceinline__ uint32_t word2_of(const uint2& q, int k) { return k == 0 ? q.x : q.y; }
+
 template <bool kNearest, bool kPartial>
 __device__ __forceinline__ void block_fp32(const DevTensor& d, int64_t blk, int lane, const StepScalars& sc,
                                            bool range_ok, int valid = kBlock) {
@@ -763,51 +772,64 @@ __device__ __forceinline__ void block_fp32(const DevTensor& d, int64_t blk, int 
   float* mp = static_cast<float*>(d.m) + e0;
   float* vp = static_cast<float*>(d.v) + e0;
   const uint64_t grp0 = static_cast<uint64_t>(d.index_base + e0) >> 3;
+  const bool odd = (lane & 1) != 0;
 #pragma unroll 1
   for (int r = 0; r < kGroups; ++r) {
     if (kPartial && r * 512 >= valid) break;       // no lane has an element left
-    const int off = r * 512 + lane * 8;
-    const bool whole = !kPartial || off + 8 <= valid;
-    uint4 G, P;
+    const int o[2] = {r * 512 + 4 * lane, r * 512 + 256 + 4 * lane};   // the lane's two quads
+    const bool whole = !kPartial || r * 512 + 512 <= valid;
+    // random words of the two quads (element i of quad q: word wq[q][i >> 1], half i & 1)
+    uint32_t wq[2][2] = {{0, 0}, {0, 0}};
+    if (!kNearest) {
+      const Rand4 x = group_bits(grp0 + static_cast<uint64_t>(r * 64 + (odd ? 32 : 0) + (lane >> 1)), 0u,
+                                 d.tensor_id, sc);
+      const uint32_t t0 = __shfl_xor(odd ? x.w[0] : x.w[2], 1, 64);
+      const uint32_t t1 = __shfl_xor(odd ? x.w[1] : x.w[3], 1, 64);
+      wq[0][0] = odd ? t0 : x.w[0];
+      wq[0][1] = odd ? t1 : x.w[1];
+      wq[1][0] = odd ? x.w[2] : t0;
+      wq[1][1] = odd ? x.w[3] : t1;
+    }
+    uint2 G[2], P[2];
     float M[8], V[8];
     if (whole) {
-      G = ld_stream16(gp + off);
-      P = ld_stream16(pp + off);
-      const uint4 m0 = ld_stream16(mp + off), m1 = ld_stream16(mp + off + 4);
-      const uint4 v0 = ld_stream16(vp + off), v1 = ld_stream16(vp + off + 4);
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        M[k] = __uint_as_float(word_of(m0, k));
-        M[k + 4] = __uint_as_float(word_of(m1, k));
-        V[k] = __uint_as_float(word_of(v0, k));
-        V[k + 4] = __uint_as_float(word_of(v1, k));
+      for (int q = 0; q < 2; ++q) {
+        G[q] = ld_stream8(gp + o[q]);
+        P[q] = ld_stream8(pp + o[q]);
+        const uint4 m4 = ld_stream16(mp + o[q]), v4 = ld_stream16(vp + o[q]);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          M[4 * q + k] = __uint_as_float(word_of(m4, k));
+          V[4 * q + k] = __uint_as_float(word_of(v4, k));
+        }
       }
     } else {
-      uint32_t a[4] = {0, 0, 0, 0}, b[4] = {0, 0, 0, 0};
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        M[j] = 0.0f;
-        V[j] = 0.0f;
+      for (int q = 0; q < 2; ++q) {
+        uint32_t a[2] = {0, 0}, b[2] = {0, 0};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const bool ok = o[q] + i < valid;
+          a[i >> 1] |= (ok ? static_cast<uint32_t>(gp[o[q] + i]) : 0u) << (16 * (i & 1));
+          b[i >> 1] |= (ok ? static_cast<uint32_t>(pp[o[q] + i]) : 0u) << (16 * (i & 1));
+          M[4 * q + i] = ok ? mp[o[q] + i] : 0.0f;
+          V[4 * q + i] = ok ? vp[o[q] + i] : 0.0f;
+        }
+        G[q] = make_uint2(a[0], a[1]);
+        P[q] = make_uint2(b[0], b[1]);
       }
-      for (int j = 0; j < 8 && off + j < valid; ++j) {
-        a[j >> 1] |= static_cast<uint32_t>(gp[off + j]) << (16 * (j & 1));
-        b[j >> 1] |= static_cast<uint32_t>(pp[off + j]) << (16 * (j & 1));
-        M[j] = mp[off + j];
-        V[j] = vp[off + j];
-      }
-      G = make_uint4(a[0], a[1], a[2], a[3]);
-      P = make_uint4(b[0], b[1], b[2], b[3]);
     }
-    Rand4 rp{{0, 0, 0, 0}};
-    if (!kNearest) rp = group_bits(grp0 + (off >> 3), 0u, d.tensor_id, sc);
     uint32_t ps[8];
     float M2[8], V2[8];
     int emin = 0;
     bool nan = false;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const float g = bf16_at(G, j);
-      const float p = bf16_at(P, j);
+      const int q = j >> 2, i = j & 3;
+      const uint32_t gw = word2_of(G[q], i >> 1), pw = word2_of(P[q], i >> 1);
+      const float g = (i & 1) ? bf16_hi(gw) : bf16_lo(gw);
+      const float p = (i & 1) ? bf16_hi(pw) : bf16_lo(pw);
       const float m2 = sc.beta1 * M[j] + sc.w1 * g;
       const float v2 = sc.beta2 * V[j] + sc.w2 * (g * g);
       const float den = sqrt_rn(v2) * sc.rbc2 + sc.eps;
@@ -817,7 +839,8 @@ __device__ __forceinline__ void block_fp32(const DevTensor& d, int64_t blk, int 
       emin = min(min(emin, __builtin_amdgcn_frexp_expf(u)),
                  min(__builtin_amdgcn_frexp_expf(m2), __builtin_amdgcn_frexp_expf(v2)));
       const uint32_t bits = __float_as_uint(pn);
-      ps[j] = bits + (kNearest ? (0x7FFFu + ((bits >> 16) & 1u)) : r16_of(rp, j));
+      const uint32_t r16 = (wq[q][i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
+      ps[j] = bits + (kNearest ? (0x7FFFu + ((bits >> 16) & 1u)) : r16);
       M2[j] = m2;
       V2[j] = v2;
     }
@@ -829,25 +852,33 @@ __device__ __forceinline__ void block_fp32(const DevTensor& d, int64_t blk, int 
       po[0] = po[1] = po[2] = po[3] = 0u;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const float pn = adamw(bf16_at(P, j), bf16_at(G, j), M[j], V[j], sc, M2[j], V2[j]);
-        po[j >> 1] |= to_bf16(pn, r16_of(rp, j), kNearest) << (16 * (j & 1));
+        const int q = j >> 2, i = j & 3;
+        const uint32_t gw = word2_of(G[q], i >> 1), pw = word2_of(P[q], i >> 1);
+        const float g = (i & 1) ? bf16_hi(gw) : bf16_lo(gw);
+        const float p = (i & 1) ? bf16_hi(pw) : bf16_lo(pw);
+        const uint32_t r16 = (wq[q][i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
+        const float pn = adamw(p, g, M[j], V[j], sc, M2[j], V2[j]);
+        po[j >> 1] |= to_bf16(pn, r16, kNearest) << (16 * (j & 1));
       }
     }
     if (whole) {
-      st_stream16(pp + off, make_uint4(po[0], po[1], po[2], po[3]));
-      st_stream16(mp + off, make_uint4(__float_as_uint(M2[0]), __float_as_uint(M2[1]), __float_as_uint(M2[2]),
-                                       __float_as_uint(M2[3])));
-      st_stream16(mp + off + 4, make_uint4(__float_as_uint(M2[4]), __float_as_uint(M2[5]), __float_as_uint(M2[6]),
-                                           __float_as_uint(M2[7])));
-      st_stream16(vp + off, make_uint4(__float_as_uint(V2[0]), __float_as_uint(V2[1]), __float_as_uint(V2[2]),
-                                       __float_as_uint(V2[3])));
-      st_stream16(vp + off + 4, make_uint4(__float_as_uint(V2[4]), __float_as_uint(V2[5]), __float_as_uint(V2[6]),
-                                           __float_as_uint(V2[7])));
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        st_stream8(pp + o[q], make_uint2(po[2 * q], po[2 * q + 1]));
+        st_stream16(mp + o[q], make_uint4(__float_as_uint(M2[4 * q]), __float_as_uint(M2[4 * q + 1]),
+                                          __float_as_uint(M2[4 * q + 2]), __float_as_uint(M2[4 * q + 3])));
+        st_stream16(vp + o[q], make_uint4(__float_as_uint(V2[4 * q]), __float_as_uint(V2[4 * q + 1]),
+                                          __float_as_uint(V2[4 * q + 2]), __float_as_uint(V2[4 * q + 3])));
+      }
     } else {
-      for (int j = 0; j < 8 && off + j < valid; ++j) {
-        pp[off + j] = static_cast<uint16_t>(po[j >> 1] >> (16 * (j & 1)));
-        mp[off + j] = M2[j];
-        vp[off + j] = V2[j];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int e = o[j >> 2] + (j & 3);
+        if (e < valid) {
+          pp[e] = static_cast<uint16_t>(po[j >> 1] >> (16 * (j & 1)));
+          mp[e] = M2[j];
+          vp[e] = V2[j];
+        }
       }
     }
   }
@@ -1188,6 +1219,91 @@ __device__ __forceinline__ void block_1s_wide(const DevTensor& d, int64_t blk, i
   }
 }
 
+// fp32 state of the one-state rules: the quad layout of block_fp32 (lane l
+// takes elements 4l..4l+3 and 256+4l..256+4l+3 of each group, so every access
+// instruction covers one contiguous segment; lane pairs share the Philox work
+// of their two groups), plain operations with every rounding's NaN rule.
+// Partial blocks skip the groups past the end and go element by element in
+// the one that straddles it.
+template <int A>
+__device__ __forceinline__ void block_1s_fp32(const DevTensor& d, int64_t blk, int lane, int valid,
+                                              const StepScalars& sc) {
+  const int64_t e0 = blk * kBlock;
+  const uint16_t* gp = d.grad + e0;
+  uint16_t* pp = d.param + e0;
+  float* mp = static_cast<float*>(d.m) + e0;
+  const bool nearest = sc.param_round != 0;
+  const uint64_t grp0 = static_cast<uint64_t>(d.index_base + e0) >> 3;
+  const bool odd = (lane & 1) != 0;
+#pragma unroll 1
+  for (int r = 0; r < kGroups; ++r) {
+    if (r * 512 >= valid) break;                   // no lane has an element left
+    const int o[2] = {r * 512 + 4 * lane, r * 512 + 256 + 4 * lane};
+    const bool whole = r * 512 + 512 <= valid;
+    uint32_t wq[2][2] = {{0, 0}, {0, 0}};
+    if (!nearest) {
+      const Rand4 x = group_bits(grp0 + static_cast<uint64_t>(r * 64 + (odd ? 32 : 0) + (lane >> 1)), 0u,
+                                 d.tensor_id, sc);
+      const uint32_t t0 = __shfl_xor(odd ? x.w[0] : x.w[2], 1, 64);
+      const uint32_t t1 = __shfl_xor(odd ? x.w[1] : x.w[3], 1, 64);
+      wq[0][0] = odd ? t0 : x.w[0];
+      wq[0][1] = odd ? t1 : x.w[1];
+      wq[1][0] = odd ? x.w[2] : t0;
+      wq[1][1] = odd ? x.w[3] : t1;
+    }
+    float g[8], p[8], m1[8];
+    if (whole) {
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const uint2 G = ld_stream8(gp + o[q]), P = ld_stream8(pp + o[q]);
+        const uint4 M = ld_stream16(mp + o[q]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t gw = word2_of(G, i >> 1), pw = word2_of(P, i >> 1);
+          g[4 * q + i] = (i & 1) ? bf16_hi(gw) : bf16_lo(gw);
+          p[4 * q + i] = (i & 1) ? bf16_hi(pw) : bf16_lo(pw);
+          m1[4 * q + i] = __uint_as_float(word_of(M, i));
+        }
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int e = o[j >> 2] + (j & 3);
+        const bool ok = e < valid;
+        g[j] = ok ? __uint_as_float(static_cast<uint32_t>(gp[e]) << 16) : 0.0f;
+        p[j] = ok ? __uint_as_float(static_cast<uint32_t>(pp[e]) << 16) : 0.0f;
+        m1[j] = ok ? mp[e] : 0.0f;
+      }
+    }
+    uint32_t po[4] = {0, 0, 0, 0};
+    float M2[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int q = j >> 2, i = j & 3;
+      const uint32_t r16 = (wq[q][i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
+      const float pn = update1<A>(p[j], g[j], m1[j], sc, M2[j]);
+      po[j >> 1] |= to_bf16(pn, r16, nearest) << (16 * (j & 1));
+    }
+    if (whole) {
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        st_stream8(pp + o[q], make_uint2(po[2 * q], po[2 * q + 1]));
+        st_stream16(mp + o[q], make_uint4(__float_as_uint(M2[4 * q]), __float_as_uint(M2[4 * q + 1]),
+                                          __float_as_uint(M2[4 * q + 2]), __float_as_uint(M2[4 * q + 3])));
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int e = o[j >> 2] + (j & 3);
+        if (e < valid) {
+          pp[e] = static_cast<uint16_t>(po[j >> 1] >> (16 * (j & 1)));
+          mp[e] = M2[j];
+        }
+      }
+    }
+  }
+}
+
 // ----------------------------------------------------------------------------- driver
 // Index of the tensor holding block b: the last i in [lo, hi] whose first
 // block is <= b, given that list[lo] starts at or before b (blocks are
@@ -1266,10 +1382,13 @@ step_kernel(const DevTensor* __restrict__ list, int ntensors, int64_t total_bloc
         const bool done = sc.param_round ? block_1s_8bit_fast<A, true, SS, true>(d, tail, lane, sc, lds, valid)
                                          : block_1s_8bit_fast<A, false, SS, true>(d, tail, lane, sc, lds, valid);
         if (!done) block_1s_8bit_plain<A, false, SS>(d, tail, lane, valid, sc, lds);
+      } else if constexpr (K == Kind::kBf16) {
+        const int64_t left = d.numel - blk * kBlock;
+        if (left >= kBlock) block_1s_wide<A, true, true>(d, blk, lane, kBlock, sc);
+        else block_1s_wide<A, true, false>(d, blk, lane, static_cast<int>(left), sc);
       } else {
         const int64_t left = d.numel - blk * kBlock;
-        if (left >= kBlock) block_1s_wide<A, K == Kind::kBf16, true>(d, blk, lane, kBlock, sc);
-        else block_1s_wide<A, K == Kind::kBf16, false>(d, blk, lane, static_cast<int>(left), sc);
+        block_1s_fp32<A>(d, blk, lane, left >= kBlock ? kBlock : static_cast<int>(left), sc);
       }
     } else if constexpr (K == Kind::k8bit) {
       // this list holds the full blocks of 8-bit tensors only

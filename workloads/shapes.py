@@ -134,6 +134,7 @@ WORKLOADS = {
     "many-4096": lambda: many_small(4096),
     "many-6151": lambda: many_small(6151),
     "many-2000": lambda: many_small(2000),    # every tensor under 4096 elements: fp32 state
+    "many-2048": lambda: many_small(2048),    # fp32 state, one whole block per tensor
 }
 
 
