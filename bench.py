@@ -122,6 +122,78 @@ def probe_bandwidth(dev, words=1 << 27, reps=5):
     return res
 
 
+class ClockSampler:
+    """GFX (per XCD) and memory clocks of the GPU torch uses, read from the driver's metrics
+    table (amdsmi) by a host thread; empty if amdsmi is unavailable.  The table refreshes
+    only every few hundred milliseconds, so the clocks are sampled while the step runs back
+    to back for a few seconds, and samples from the first second are dropped."""
+
+    def __init__(self, pci_bus=None, period_s=0.05, settle_s=1.0):
+        import threading
+        self.period, self.settle = period_s, settle_s
+        self.gfx, self.xcd, self.mem = [], [], []
+        self.err = None
+        self._stop = threading.Event()
+        self._thread = None
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init()
+            self.smi = amdsmi
+            handles = amdsmi.amdsmi_get_processor_handles()
+            # the handle of the GPU torch uses: the same PCI bus number
+            match = [h for h in handles
+                     if pci_bus is not None and int(amdsmi.amdsmi_get_gpu_device_bdf(h).split(":")[1], 16) == pci_bus]
+            if len(match) != 1 and len(handles) != 1:
+                raise RuntimeError(f"cannot tell which of {len(handles)} GPUs is in use")
+            self.handle = match[0] if len(match) == 1 else handles[0]
+            self.smi.amdsmi_get_gpu_metrics_info(self.handle)
+        except Exception as e:   # no amdsmi or no permission: the clock is reported as unknown
+            self.smi = None
+            self.err = f"{type(e).__name__}: {e}"
+
+    def _loop(self):
+        t0 = time.perf_counter()
+        while not self._stop.is_set():
+            try:
+                m = self.smi.amdsmi_get_gpu_metrics_info(self.handle)
+                if time.perf_counter() - t0 >= self.settle:
+                    self.gfx.append(float(m["current_gfxclk"]))
+                    self.mem.append(float(m["current_uclk"]))
+                    xs = [float(x) for x in (m.get("current_gfxclks") or []) if isinstance(x, (int, float))]
+                    if xs:
+                        self.xcd.append(xs)
+            except Exception as e:
+                self.err = f"{type(e).__name__}: {e}"
+                return
+            self._stop.wait(self.period)
+
+    def __enter__(self):
+        import threading
+        if self.smi is not None:
+            self._thread = threading.Thread(target=self._loop, daemon=True)
+            self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        if self._thread is not None:
+            self._thread.join()
+        return False
+
+    def summary(self, note):
+        if not self.gfx:
+            return {"gfx_mhz": None, "mem_mhz": None, "samples": 0, "source": "amdsmi gpu metrics",
+                    "note": self.err or "no samples"}
+        g, m = sorted(self.gfx), sorted(self.mem)
+        out = {"gfx_mhz": {"median": g[len(g) // 2], "min": g[0], "max": g[-1]},
+               "mem_mhz": {"median": m[len(m) // 2], "min": m[0], "max": m[-1]},
+               "samples": len(g), "source": "amdsmi gpu metrics (current_gfxclk, current_uclk)", "note": note}
+        if self.xcd:
+            per = list(zip(*self.xcd))
+            out["gfx_mhz_per_xcd_median"] = [sorted(x)[len(x) // 2] for x in per]
+        return out
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -132,7 +204,10 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--round", choices=("stochastic", "nearest"), default="stochastic",
                     help="parameter rounding (nearest: the deterministic baseline, for the SR overhead)")
-    ap.add_argument("--cpu-sample-elems", type=int, default=128 * 1024 * 1024)
+    ap.add_argument("--clock-seconds", type=float, default=3.0,
+                    help="untimed phase after the timed steps in which the GPU clock is sampled (0: skip)")
+    ap.add_argument("--cpu-cap-elems", type=int, default=1 << 24,
+                    help="oracle leg: elements taken from the start of each tensor of the fixed subset")
     ap.add_argument("--algo", choices=("adamw", "lion", "momentum"), default="adamw",
                     help="update rule (lion / momentum: one 8-bit state, the same machinery)")
     ap.add_argument("--state-round", choices=("nearest", "stochastic"), default="nearest",
@@ -250,6 +325,23 @@ def main():
         t_step += 1
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
+    # the GPU clock under this step: the step again back to back for about clock_s seconds
+    # (untimed), the driver's clocks sampled meanwhile
+    clock_s = args.clock_seconds
+    clocks = ClockSampler(getattr(torch.cuda.get_device_properties(dev), "pci_bus_id", None))
+    n_clock = 0
+    if clock_s > 0 and clocks.smi is not None:
+        est_ms = max(wall * 1000.0 / args.steps, 0.05)
+        with clocks:
+            c0 = time.perf_counter()
+            while time.perf_counter() - c0 < clock_s:
+                for _ in range(max(1, int(200.0 / est_ms))):
+                    step(t_step)
+                    t_step += 1
+                    n_clock += 1
+                torch.cuda.synchronize()
+    clock_note = (f"sampled every 50 ms while {n_clock} more steps ran back to back after the timed ones "
+                  f"(about {clock_s:.0f} s, untimed), the first second dropped")
     ev_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
     ms_per_step = wall * 1000.0 / args.steps
     ev_avg = sum(ev_ms) / len(ev_ms)
@@ -287,36 +379,91 @@ def main():
     if roof and dom == 0 and not one_state and attain.get("pattern_8bit"):
         roof["frac_of_step_pattern"] = round(roof["achieved"] / attain["pattern_8bit"], 4)
 
-    # ---------------------------------------------------------------- CPU baseline (oracle)
+    # ---------------------------------------------------------------- CPU baseline (oracle) + parity
+    # The oracle, single-threaded, on a bounded fixed subset of the list: the embeddings, every
+    # tensor of the first and the last layer and the final LayerNorm, each tensor cut to its
+    # first --cpu-cap-elems elements (whole blocks, so the cut changes no result).  Its inputs
+    # are the state left by the timed steps and the next gradient set; the GPU then runs one
+    # more step (untimed) over the whole list, and its outputs for the subset are compared
+    # with the oracle's element by element.  The oracle's rate, times the list's element
+    # count, gives an extrapolated single-core time for a whole step.
     cpu = None
+    parity = None
     if not args.no_cpu_baseline:
         import oracle
-        big = max(tensors, key=lambda t: t["n"] if t["mode"] == dom else -1)
-        n = min(big["n"], args.cpu_sample_elems)
-        sd = {0: np.uint8, 1: np.uint16, 2: np.float32}[big["mode"]]
+        subset = [tid for tid in shapes.subset_for_sampling(w) if tid < len(tensors)]
+        sd = {0: np.uint8, 1: np.uint16, 2: np.float32}
 
-        def host(t, dtype):
-            h = t[:n].detach().cpu()
+        def host(t, lo, hi, dtype):
+            if t is None:
+                return None
+            h = t[lo:hi].detach().cpu()
             if h.dtype == torch.bfloat16:
                 h = h.view(torch.int16)
             return h.numpy().view(dtype).copy()
-        p, g = host(big["P"], np.uint16), host(big["grads"][0], np.uint16)
-        m = host(big["M"], sd)
-        v = host(big["V"], sd) if big["V"] is not None else None
-        am = big["AM"][: (n + BLOCK - 1) // BLOCK].cpu().numpy() if big["AM"] is not None else None
-        av = big["AV"][: (n + BLOCK - 1) // BLOCK].cpu().numpy() if big["AV"] is not None else None
-        hp = oracle.Hparams(lr=lr, beta1=w.beta1, beta2=beta2, eps=w.eps,
-                            weight_decay=w.weight_decay, step=t_step, seed=w.seed, state_round=srnd)
-        c0t = time.perf_counter()
-        if one_state:
-            oracle.step_tensor_1state(algo_id, big["mode"], p, g, m, am, hp, big["tid"])
-        else:
-            oracle.step_tensor(big["mode"], p, g, m, v, am, av, hp, big["tid"])
-        cpu_s = time.perf_counter() - c0t
-        cpu = {"value": round(n / cpu_s / 1e9, 6), "unit": "Gparams/s", "cores": 1, "kind": "oracle",
-               "sample": f"one step of the first {n} elements of tensor {w.tensors[big['tid']].name} "
-                         f"({cpu_s:.1f} s, numpy single thread, of {os.cpu_count()} host cores)"}
-        log(f"oracle: {n} elements in {cpu_s:.2f}s")
+        gi = (t_step - 1) % pool
+        inputs = []
+        for tid in subset:
+            t = tensors[tid]
+            n = min(t["n"], args.cpu_cap_elems)
+            nb = (n + BLOCK - 1) // BLOCK
+            inputs.append(dict(t=t, n=n, p=host(t["P"], 0, n, np.uint16), g=host(t["grads"][gi], 0, n, np.uint16),
+                               m=host(t["M"], 0, n, sd[t["mode"]]), v=host(t["V"], 0, n, sd[t["mode"]]),
+                               am=host(t["AM"], 0, nb, np.float32), av=host(t["AV"], 0, nb, np.float32)))
+        step(t_step)                   # one more GPU step, outside the timed region
+        torch.cuda.synchronize()
+        hp = oracle.Hparams(lr=lr, beta1=w.beta1, beta2=beta2, eps=w.eps, weight_decay=w.weight_decay,
+                            step=t_step, seed=w.seed, param_round=rnd, state_round=srnd)
+        n_el = sum(x["n"] for x in inputs)
+        mism = {"param": 0, "state": 0, "absmax": 0}
+        max_step = 0
+        cpu_s = 0.0
+        for x in inputs:
+            t, n = x["t"], x["n"]
+            nb = (n + BLOCK - 1) // BLOCK
+            c0t = time.perf_counter()
+            if one_state:
+                pw, mw, amw = oracle.step_tensor_1state(algo_id, t["mode"], x["p"], x["g"], x["m"], x["am"], hp,
+                                                        t["tid"])
+                want = [pw, mw, None, amw, None]
+            else:
+                want = list(oracle.step_tensor(t["mode"], x["p"], x["g"], x["m"], x["v"], x["am"], x["av"], hp,
+                                               t["tid"]))
+            cpu_s += time.perf_counter() - c0t
+            got = [host(t["P"], 0, n, np.uint16), host(t["M"], 0, n, sd[t["mode"]]),
+                   host(t["V"], 0, n, sd[t["mode"]]), host(t["AM"], 0, nb, np.float32),
+                   host(t["AV"], 0, nb, np.float32)]
+            mism["param"] += int(np.count_nonzero(got[0] != want[0]))
+            for k in (1, 2):
+                if want[k] is not None:
+                    a_, b_ = got[k].view(np.uint8 if want[k].dtype == np.uint8 else
+                                         np.uint16 if want[k].dtype == np.uint16 else np.uint32), \
+                        want[k].view(np.uint8 if want[k].dtype == np.uint8 else
+                                     np.uint16 if want[k].dtype == np.uint16 else np.uint32)
+                    mism["state"] += int(np.count_nonzero(a_ != b_))
+                    if want[k].dtype == np.uint8:
+                        max_step = max(max_step, int(np.abs(a_.astype(np.int64) - b_.astype(np.int64)).max(initial=0)))
+            for k in (3, 4):
+                if want[k] is not None:
+                    gk, wk = got[k].astype(np.float64), want[k].astype(np.float64)
+                    mism["absmax"] += int(np.count_nonzero(
+                        (np.isnan(gk) != np.isnan(wk)) | (np.abs(gk - wk) > 1e-6 * np.abs(wk))))
+        rate = n_el / cpu_s
+        names = [w.tensors[tid].name for tid in subset]
+        cpu = {"value": round(rate / 1e9, 6), "unit": "Gparams/s", "cores": 1, "kind": "oracle",
+               "sample": f"one step of {n_el} elements: the first min(numel, {args.cpu_cap_elems}) elements of "
+                         f"each of {len(subset)} tensors ({names[0]}, {names[1]}, layers {names[2].split('.')[0]} "
+                         f"and {names[-3].split('.')[0]}, {names[-2]}, {names[-1]}); {cpu_s:.1f} s, numpy, "
+                         f"single thread, of {os.cpu_count()} host cores",
+               "extrapolated_full_step_s": round(total / rate, 1),
+               "extrapolated": "full-list single-core time = the subset's elements/s x the list's elements"}
+        parity = {"elements": n_el, "tensors": len(subset), "step": t_step,
+                  "mismatch_param": mism["param"], "mismatch_state": mism["state"],
+                  "mismatch_absmax": mism["absmax"], "max_code_distance": max_step,
+                  "allowed_per_kind": int(1e-5 * n_el),
+                  "ok": mism["absmax"] == 0 and max_step <= 1 and
+                  max(mism["param"], mism["state"]) <= int(1e-5 * n_el)}
+        log(f"oracle: {n_el} elements in {cpu_s:.2f}s; parity of the extra step: {parity}")
 
     out = {
         "metric": METRIC,
@@ -345,6 +492,8 @@ def main():
                    "max_ms": round(max(ev_ms), 4),
                    "step1_ms": round(step1_ms, 4) if step1_ms is not None else None},
         "cpu_baseline": cpu,
+        "parity": parity,
+        "gpu_clock": clocks.summary(clock_note),
     }
     print(json.dumps(out), flush=True)
 
