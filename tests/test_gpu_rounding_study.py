@@ -15,11 +15,18 @@ Two regimes:
            while stochastic rounding follows the reference on average (the decay
            that bf16 with stochastic rounding must not lose, "[Feat]: Stochastic
            rounding of AdamW momentums", the linked weight-decay issue).
-The printed summary is the study's result; the assertions fix what must hold.
+Variants: 8-bit, bf16 (moments written with stochastic rounding) and fp32 state, each with a
+stochastic or a nearest-even parameter write.  Also measured: the bytes each state layout
+keeps resident per parameter, and the cost of the stochastic parameter write (the step with
+nearest-even against stochastic rounding, HIP events, 2^29 elements, 8-bit state).
+The printed summary is the study's result; the assertions fix what must hold.  With
+OPT8_STUDY_JSON set, the summary (every variant and seed) is also written to that path.
 """
 
 import json
 import math
+import os
+import statistics
 
 import pytest
 import torch
@@ -60,13 +67,53 @@ def _grads(seed, step, cfg, dev):
     return g
 
 
-def _state(mode, dev):
-    nb = (N + 2047) // 2048
+def _state(mode, dev, n=N):
+    nb = (n + 2047) // 2048
     if mode == opt8.OPT8_STATE_8BIT:
-        return (torch.full((N,), 127, dtype=torch.uint8, device=dev), torch.zeros(N, dtype=torch.uint8, device=dev),
+        return (torch.full((n,), 127, dtype=torch.uint8, device=dev), torch.zeros(n, dtype=torch.uint8, device=dev),
                 torch.zeros(nb, dtype=torch.float32, device=dev), torch.zeros(nb, dtype=torch.float32, device=dev))
-    return (torch.zeros(N, dtype=torch.float32, device=dev), torch.zeros(N, dtype=torch.float32, device=dev),
-            None, None)
+    dt = torch.bfloat16 if mode == opt8.OPT8_STATE_BF16_SR else torch.float32
+    return (torch.zeros(n, dtype=dt, device=dev), torch.zeros(n, dtype=dt, device=dev), None, None)
+
+
+STATES = ((opt8.OPT8_STATE_8BIT, "8bit"), (opt8.OPT8_STATE_BF16_SR, "bf16"), (opt8.OPT8_STATE_FP32, "fp32"))
+
+
+def resident_bytes_per_param(mode):
+    """Bytes a parameter keeps on the device with this state layout: bf16 parameter and
+    gradient, both moments, and the per-block absmax values of the 8-bit layout."""
+    n = 1 << 21
+    p = torch.empty(n, dtype=torch.bfloat16, device="cuda:0")
+    bufs = [p, p, *(_state(mode, p.device, n))]
+    return sum(b.numel() * b.element_size() for b in bufs if b is not None) / n
+
+
+def sr_step_overhead(rounds=4, steps=10):
+    """Median step time with the nearest-even and with the stochastic parameter write."""
+    n = 1 << 29
+    dev = torch.device("cuda:0")
+    P = torch.empty(n, dtype=torch.bfloat16, device=dev).normal_(0.0, 0.02)
+    G = torch.empty(n, dtype=torch.bfloat16, device=dev).normal_(0.0, 1e-3)
+    M, V, AM, AV = _state(opt8.OPT8_STATE_8BIT, dev, n)
+    arr = opt8.tensor_array([opt8.make_tensor(P, G, M, V, AM, AV, tensor_id=0)])
+    times = {"stochastic": [], "nearest": []}
+    t = 1
+    for r in range(rounds):
+        for name in (("stochastic", "nearest") if r % 2 == 0 else ("nearest", "stochastic")):
+            rnd = opt8.OPT8_ROUND_STOCHASTIC if name == "stochastic" else opt8.OPT8_ROUND_NEAREST
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+            for e0, e1 in ev:
+                e0.record()
+                opt8.opt8_adamw_step(arr, opt8.make_hparams(1e-4, weight_decay=0.01, step=t, seed=3, param_round=rnd))
+                e1.record()
+                t += 1
+            torch.cuda.synchronize()
+            times[name].append(statistics.median(a.elapsed_time(b) for a, b in ev))
+    del P, G, M, V, AM, AV, arr
+    torch.cuda.empty_cache()
+    sr, ne = statistics.median(times["stochastic"]), statistics.median(times["nearest"])
+    return {"elements": n, "state": "8bit", "ms_stochastic": round(sr, 4), "ms_nearest": round(ne, 4),
+            "overhead_frac": round(sr / ne - 1.0, 4), "rounds": rounds, "steps_per_round": steps}
 
 
 def _run(regime, seed):
@@ -80,7 +127,7 @@ def _run(regime, seed):
         gp.manual_seed(gen.derived_seed(seed, 0, 0, gen.P_PARAM))
         p0.normal_(0.0, 0.02, generator=gp)
     variants = {}
-    for mode, mname in ((opt8.OPT8_STATE_8BIT, "8bit"), (opt8.OPT8_STATE_FP32, "fp32")):
+    for mode, mname in STATES:
         for rnd, rname in ((opt8.OPT8_ROUND_STOCHASTIC, "sr"), (opt8.OPT8_ROUND_NEAREST, "nearest")):
             variants[f"{mname}-{rname}"] = [mode, rnd, p0.clone(), *_state(mode, dev)]
     ref_p = p0.double()
@@ -120,12 +167,22 @@ def test_nearest_vs_stochastic_rounding_against_float64():
                 continue
             agg[key] = {m: [r[key][m] for r in runs] for m in ("bias", "rmse", "stalled_frac")}
         summary[regime] = agg
+    summary["resident_bytes_per_param"] = {name: resident_bytes_per_param(mode) for mode, name in STATES}
+    summary["sr_step_overhead"] = sr_step_overhead()
+    summary["setup"] = {"elements": N, "steps": STEPS, "seeds": list(SEEDS), "regimes": REGIMES,
+                        "reference": "AdamW in float64 on the same bf16 gradients",
+                        "per_seed_lists": "bias, rmse and stalled_frac are lists over the seeds"}
     log("rounding study: " + json.dumps(summary))
+    out = os.environ.get("OPT8_STUDY_JSON")
+    if out:
+        with open(out, "w") as f:
+            json.dump(summary, f, indent=1, sort_keys=True)
+            f.write("\n")
 
     bf16_step_below_1 = 2.0 ** -8
     dec = summary["decay"]
     noise = bf16_step_below_1 * math.sqrt(STEPS) / 2 / math.sqrt(N)   # sd of the mean SR error
-    for state in ("8bit", "fp32"):
+    for state in ("8bit", "bf16", "fp32"):
         # nearest rounding loses the whole decay: every parameter is still exactly 1.0,
         # so its mean error is minus the reference's mean drift
         assert min(dec[f"{state}-nearest"]["stalled_frac"]) == 1.0
@@ -136,8 +193,12 @@ def test_nearest_vs_stochastic_rounding_against_float64():
             assert abs(b) < 0.05 * abs(drift) + 6 * noise, (state, b, drift)
         assert max(dec[f"{state}-sr"]["stalled_frac"]) < 0.9
     w = summary["weights"]
-    for key in ("8bit-sr", "8bit-nearest", "fp32-sr", "fp32-nearest"):
+    for key in ("8bit-sr", "8bit-nearest", "bf16-sr", "bf16-nearest", "fp32-sr", "fp32-nearest"):
         # every variant tracks the reference to a fraction of the distance moved
         assert max(w[key]["rmse"]) < 0.5 * w["moved"], (key, w[key]["rmse"], w["moved"])
-    for key in ("8bit-sr", "fp32-sr"):
+    for key in ("8bit-sr", "bf16-sr", "fp32-sr"):
         assert max(abs(b) for b in w[key]["bias"]) < 0.05 * w["moved"], (key, w[key]["bias"])
+    # resident bytes per parameter: 2 + 2 + 1 + 1 + 8/2048, 2 + 2 + 2 + 2, 2 + 2 + 4 + 4
+    rb = summary["resident_bytes_per_param"]
+    assert rb["8bit"] == 6 + 8 / 2048 and rb["bf16"] == 8 and rb["fp32"] == 12
+    assert summary["sr_step_overhead"]["ms_nearest"] > 0
