@@ -10,6 +10,9 @@ against the oracle after every step.
   gptneo-2.7b-bf16  the same list with bf16 state written by stochastic rounding
   gpt2-350m         3 steps, lr 6e-4, wd 0.1, gradients N(0, 1e-3/sqrt(fan_in)):
                     EVERY element of every tensor, the embedding included
+and the same protocol for the rules built on the same machinery, on the 6.7B
+list: 8-bit Lion (lr 1.2e-5, betas 0.9 / 0.99), 8-bit SGD with momentum (0.9)
+and AdamW with the 8-bit state rounded stochastically.
 
 Each list starts from the zero state (absmax 0 and zero codes, or zero bf16 /
 fp32 moments) with its parameter recipe, and gets fresh gradients at every
@@ -69,7 +72,7 @@ def _state_dtype(mode):
 class Sampled:
     """One tensor on the device, and the blocks of it the oracle follows."""
 
-    def __init__(self, w, tid, blocks_per_tensor, rng, dev):
+    def __init__(self, w, tid, blocks_per_tensor, rng, dev, one_state=False):
         spec = w.tensors[tid]
         self.tid, self.spec, self.n = tid, spec, spec.numel
         self.mode = _mode_of(w, spec)
@@ -88,6 +91,8 @@ class Sampled:
             dt = torch.bfloat16 if self.mode == oracle.MODE_BF16_SR else torch.float32
             self.M = torch.zeros(n, dtype=dt, device=dev)
             self.V = torch.zeros(n, dtype=dt, device=dev)
+        if one_state:
+            self.V = self.AV = None
         if blocks_per_tensor is None or nb <= blocks_per_tensor + 2:
             blocks = list(range(nb))
         else:
@@ -126,12 +131,12 @@ class Sampled:
                 self.gather(self.AV, True, np.float32)]
 
 
-def _oracle_items(samples, carried, grads, hp):
+def _oracle_items(samples, carried, grads, hp, algo=0):
     items, where = [], []
     fields = hp_fields(hp)
     for s, (p, m, v, am, av), g in zip(samples, carried, grads):
         for a, c, e0, e1, b0, b1 in s.pieces:
-            items.append((0, s.mode, fields, p[e0:e1], g[e0:e1], m[e0:e1], v[e0:e1],
+            items.append((algo, s.mode, fields, p[e0:e1], g[e0:e1], m[e0:e1], None if v is None else v[e0:e1],
                           None if am is None else am[b0:b1], None if av is None else av[b0:b1],
                           s.tid, a * BLOCK))
             where.append(s)
@@ -150,22 +155,34 @@ def _assemble(samples, where, results):
     return assembled
 
 
-CONFIGS = [("gptneo-6.7b", SAMPLES_PER_TENSOR), ("lm-1.5b", SAMPLES_PER_TENSOR),
-           ("gptneo-2.7b", SAMPLES_PER_TENSOR), ("gptneo-2.7b-bf16", SAMPLES_PER_TENSOR), ("gpt2-350m", None)]
+ADAMW, LION, MOMENTUM = 0, oracle.ALGO_LION, oracle.ALGO_MOMENTUM
+STEP_FN = {ADAMW: "opt8_adamw_step", LION: "opt8_lion_step", MOMENTUM: "opt8_momentum_step"}
+# (list, sampled blocks per tensor (None: all), update rule, state rounding)
+CONFIGS = [("gptneo-6.7b", SAMPLES_PER_TENSOR, ADAMW, 0), ("lm-1.5b", SAMPLES_PER_TENSOR, ADAMW, 0),
+           ("gptneo-2.7b", SAMPLES_PER_TENSOR, ADAMW, 0), ("gptneo-2.7b-bf16", SAMPLES_PER_TENSOR, ADAMW, 0),
+           ("gpt2-350m", None, ADAMW, 0),
+           ("gptneo-6.7b", SAMPLES_PER_TENSOR, LION, 0), ("gptneo-6.7b", SAMPLES_PER_TENSOR, MOMENTUM, 0),
+           ("gptneo-6.7b", SAMPLES_PER_TENSOR, ADAMW, 1)]
+RULE_NAMES = {ADAMW: "adamw", LION: "lion", MOMENTUM: "momentum"}
 
 
 @pytest.mark.timeout(1200)
-@pytest.mark.parametrize("name,per_tensor", CONFIGS)
-def test_full_size_list_as_configured(name, per_tensor, pool):
+@pytest.mark.parametrize("name,per_tensor,algo,state_round", CONFIGS,
+                         ids=[f"{c[0]}-{RULE_NAMES[c[2]]}" + ("-sr-state" if c[3] else "") for c in CONFIGS])
+def test_full_size_list_as_configured(name, per_tensor, algo, state_round, pool):
     w = shapes.get(name)
+    # Lion at a tenth of the list's learning rate with beta2 0.99 (its usual setting)
+    lr = w.lr / 10 if algo == LION else w.lr
+    beta2 = 0.99 if algo == LION else w.beta2
+    label = f"{name}/{RULE_NAMES[algo]}" + ("/sr-state" if state_round else "")
     dev = torch.device("cuda:0")
     t0 = time.time()
     rng = np.random.default_rng(2024)
-    samples = [Sampled(w, tid, per_tensor, rng, dev) for tid in range(len(w.tensors))]
+    samples = [Sampled(w, tid, per_tensor, rng, dev, one_state=algo != ADAMW) for tid in range(len(w.tensors))]
     arr = opt8.tensor_array(s.desc() for s in samples)
     torch.cuda.synchronize()
     checked_elems = sum(p[3] - p[2] for s in samples for p in s.pieces)
-    log(f"{name}: {len(samples)} tensors, {w.numel} elements from the zero state, {w.steps} steps; "
+    log(f"{label}: {len(samples)} tensors, {w.numel} elements from the zero state, {w.steps} steps; "
         f"the oracle follows {sum(len(s.blocks) for s in samples)} blocks ({checked_elems} elements); "
         f"built in {time.time() - t0:.1f}s")
     carried = [s.read() for s in samples]        # the parameters and the zero state, as the oracle starts
@@ -175,23 +192,23 @@ def test_full_size_list_as_configured(name, per_tensor, pool):
         for s in samples:
             gen.grad_init_device(s.spec, w, step, s.tid, s.G)
         grads = [s.gather(s.G, False, np.uint16) for s in samples]
-        hp = oracle.Hparams(lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps, weight_decay=w.weight_decay,
-                            step=step, seed=w.seed)
-        opt8.opt8_adamw_step(arr, opt8.make_hparams(hp.lr, hp.beta1, hp.beta2, hp.eps, hp.weight_decay,
-                                                    hp.step, hp.seed))
+        hp = oracle.Hparams(lr=lr, beta1=w.beta1, beta2=beta2, eps=w.eps, weight_decay=w.weight_decay,
+                            step=step, seed=w.seed, state_round=state_round)
+        getattr(opt8, STEP_FN[algo])(arr, opt8.make_hparams(hp.lr, hp.beta1, hp.beta2, hp.eps, hp.weight_decay,
+                                                            hp.step, hp.seed, hp.param_round, hp.state_round))
         torch.cuda.synchronize()
         got = [s.read() for s in samples]
-        items, where = _oracle_items(samples, carried, grads, hp)
+        items, where = _oracle_items(samples, carried, grads, hp, algo)
         want = _assemble(samples, where, pool.step(items))
         stats = {}
         for s, x, y in zip(samples, got, want):
-            compare_state(f"{name}/step{step}/t{s.tid}", x, y, s.mode, stats)
+            compare_state(f"{label}/step{step}/t{s.tid}", x, y, s.mode, stats)
         zero_blocks = sum(int(np.count_nonzero(y[3] == 0)) for y in want if y[3] is not None)
         mism = sum(stats.values())
         per_step.append(mism)
-        log(f"{name}: step {step}: {checked_elems} elements checked, {mism} differ from the oracle "
+        log(f"{label}: step {step}: {checked_elems} elements checked, {mism} differ from the oracle "
             f"({zero_blocks} sampled blocks with a zero first-moment absmax); {time.time() - t1:.1f}s")
         carried = want
-    log(f"{name}: mismatching elements per step {per_step}")
+    log(f"{label}: mismatching elements per step {per_step}")
     del samples, arr
     torch.cuda.empty_cache()
