@@ -759,8 +759,9 @@ __device__ __forceinline__ void block_bf16_full(const DevTensor& d, int64_t blk,
 // 2^-89, the host's range for eps and the corrections), else the plain IEEE
 // operations; the moments are stored as computed.  With kPartial (the last
 // block of a tensor holding `valid` elements) the groups past the end are
-// skipped and the one that straddles it is read and written element by element
-// with zeros in the rest.
+// skipped; in the one that straddles it, every quad wholly inside the tensor
+// still moves with vector accesses, and the one quad that crosses the end is
+// read and written element by element with zeros in the rest.
 __device__ __forceinline__ uint32_t word2_of(const uint2& q, int k) { return k == 0 ? q.x : q.y; }
 
 template <bool kNearest, bool kPartial>
@@ -790,11 +791,13 @@ __device__ __forceinline__ void block_fp32(const DevTensor& d, int64_t blk, int 
       wq[1][0] = odd ? x.w[2] : t0;
       wq[1][1] = odd ? x.w[3] : t1;
     }
+    // a quad wholly inside the tensor moves with vector accesses (in the group that
+    // straddles the end too); only the quad that crosses the end goes element by element
     uint2 G[2], P[2];
     float M[8], V[8];
-    if (whole) {
 #pragma unroll
-      for (int q = 0; q < 2; ++q) {
+    for (int q = 0; q < 2; ++q) {
+      if (whole || o[q] + 4 <= valid) {
         G[q] = ld_stream8(gp + o[q]);
         P[q] = ld_stream8(pp + o[q]);
         const uint4 m4 = ld_stream16(mp + o[q]), v4 = ld_stream16(vp + o[q]);
@@ -803,10 +806,7 @@ __device__ __forceinline__ void block_fp32(const DevTensor& d, int64_t blk, int 
           M[4 * q + k] = __uint_as_float(word_of(m4, k));
           V[4 * q + k] = __uint_as_float(word_of(v4, k));
         }
-      }
-    } else {
-#pragma unroll
-      for (int q = 0; q < 2; ++q) {
+      } else {
         uint32_t a[2] = {0, 0}, b[2] = {0, 0};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -861,23 +861,23 @@ __device__ __forceinline__ void block_fp32(const DevTensor& d, int64_t blk, int 
         po[j >> 1] |= to_bf16(pn, r16, kNearest) << (16 * (j & 1));
       }
     }
-    if (whole) {
 #pragma unroll
-      for (int q = 0; q < 2; ++q) {
+    for (int q = 0; q < 2; ++q) {
+      if (whole || o[q] + 4 <= valid) {
         st_stream8(pp + o[q], make_uint2(po[2 * q], po[2 * q + 1]));
         st_stream16(mp + o[q], make_uint4(__float_as_uint(M2[4 * q]), __float_as_uint(M2[4 * q + 1]),
                                           __float_as_uint(M2[4 * q + 2]), __float_as_uint(M2[4 * q + 3])));
         st_stream16(vp + o[q], make_uint4(__float_as_uint(V2[4 * q]), __float_as_uint(V2[4 * q + 1]),
                                           __float_as_uint(V2[4 * q + 2]), __float_as_uint(V2[4 * q + 3])));
-      }
-    } else {
+      } else {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int e = o[j >> 2] + (j & 3);
-        if (e < valid) {
-          pp[e] = static_cast<uint16_t>(po[j >> 1] >> (16 * (j & 1)));
-          mp[e] = M2[j];
-          vp[e] = V2[j];
+        for (int i = 0; i < 4; ++i) {
+          const int e = o[q] + i;
+          if (e < valid) {
+            pp[e] = static_cast<uint16_t>(po[2 * q + (i >> 1)] >> (16 * (i & 1)));
+            mp[e] = M2[4 * q + i];
+            vp[e] = V2[4 * q + i];
+          }
         }
       }
     }
@@ -1223,8 +1223,8 @@ __device__ __forceinline__ void block_1s_wide(const DevTensor& d, int64_t blk, i
 // takes elements 4l..4l+3 and 256+4l..256+4l+3 of each group, so every access
 // instruction covers one contiguous segment; lane pairs share the Philox work
 // of their two groups), plain operations with every rounding's NaN rule.
-// Partial blocks skip the groups past the end and go element by element in
-// the one that straddles it.
+// Partial blocks skip the groups past the end; in the group that straddles it
+// only the quad that crosses the end goes element by element.
 template <int A>
 __device__ __forceinline__ void block_1s_fp32(const DevTensor& d, int64_t blk, int lane, int valid,
                                               const StepScalars& sc) {
@@ -1251,10 +1251,12 @@ __device__ __forceinline__ void block_1s_fp32(const DevTensor& d, int64_t blk, i
       wq[1][0] = odd ? x.w[2] : t0;
       wq[1][1] = odd ? x.w[3] : t1;
     }
+    // a quad wholly inside the tensor moves with vector accesses; only the quad that
+    // crosses the end goes element by element
     float g[8], p[8], m1[8];
-    if (whole) {
 #pragma unroll
-      for (int q = 0; q < 2; ++q) {
+    for (int q = 0; q < 2; ++q) {
+      if (whole || o[q] + 4 <= valid) {
         const uint2 G = ld_stream8(gp + o[q]), P = ld_stream8(pp + o[q]);
         const uint4 M = ld_stream16(mp + o[q]);
 #pragma unroll
@@ -1264,15 +1266,15 @@ __device__ __forceinline__ void block_1s_fp32(const DevTensor& d, int64_t blk, i
           p[4 * q + i] = (i & 1) ? bf16_hi(pw) : bf16_lo(pw);
           m1[4 * q + i] = __uint_as_float(word_of(M, i));
         }
-      }
-    } else {
+      } else {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int e = o[j >> 2] + (j & 3);
-        const bool ok = e < valid;
-        g[j] = ok ? __uint_as_float(static_cast<uint32_t>(gp[e]) << 16) : 0.0f;
-        p[j] = ok ? __uint_as_float(static_cast<uint32_t>(pp[e]) << 16) : 0.0f;
-        m1[j] = ok ? mp[e] : 0.0f;
+        for (int i = 0; i < 4; ++i) {
+          const int e = o[q] + i;
+          const bool ok = e < valid;
+          g[4 * q + i] = ok ? __uint_as_float(static_cast<uint32_t>(gp[e]) << 16) : 0.0f;
+          p[4 * q + i] = ok ? __uint_as_float(static_cast<uint32_t>(pp[e]) << 16) : 0.0f;
+          m1[4 * q + i] = ok ? mp[e] : 0.0f;
+        }
       }
     }
     uint32_t po[4] = {0, 0, 0, 0};
@@ -1284,20 +1286,20 @@ __device__ __forceinline__ void block_1s_fp32(const DevTensor& d, int64_t blk, i
       const float pn = update1<A>(p[j], g[j], m1[j], sc, M2[j]);
       po[j >> 1] |= to_bf16(pn, r16, nearest) << (16 * (j & 1));
     }
-    if (whole) {
 #pragma unroll
-      for (int q = 0; q < 2; ++q) {
+    for (int q = 0; q < 2; ++q) {
+      if (whole || o[q] + 4 <= valid) {
         st_stream8(pp + o[q], make_uint2(po[2 * q], po[2 * q + 1]));
         st_stream16(mp + o[q], make_uint4(__float_as_uint(M2[4 * q]), __float_as_uint(M2[4 * q + 1]),
                                           __float_as_uint(M2[4 * q + 2]), __float_as_uint(M2[4 * q + 3])));
-      }
-    } else {
+      } else {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int e = o[j >> 2] + (j & 3);
-        if (e < valid) {
-          pp[e] = static_cast<uint16_t>(po[j >> 1] >> (16 * (j & 1)));
-          mp[e] = M2[j];
+        for (int i = 0; i < 4; ++i) {
+          const int e = o[q] + i;
+          if (e < valid) {
+            pp[e] = static_cast<uint16_t>(po[2 * q + (i >> 1)] >> (16 * (i & 1)));
+            mp[e] = M2[4 * q + i];
+          }
         }
       }
     }
