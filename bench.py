@@ -392,6 +392,15 @@ def main():
     if not args.no_cpu_baseline:
         import oracle
         subset = [tid for tid in shapes.subset_for_sampling(w) if tid < len(tensors)]
+        if len(subset) < 2:
+            # lists without the model layout (many small tensors, one tensor): their first
+            # tensors, up to one cap's worth of elements
+            subset, acc = [], 0
+            for t in tensors:
+                if acc >= args.cpu_cap_elems:
+                    break
+                subset.append(t["tid"])
+                acc += min(t["n"], args.cpu_cap_elems)
         sd = {0: np.uint8, 1: np.uint16, 2: np.float32}
 
         def host(t, lo, hi, dtype):
@@ -450,10 +459,15 @@ def main():
                         (np.isnan(gk) != np.isnan(wk)) | (np.abs(gk - wk) > 1e-6 * np.abs(wk))))
         rate = n_el / cpu_s
         names = [w.tensors[tid].name for tid in subset]
+        layers = sorted({n.split(".")[0] for n in names if "." in n and not n.startswith("ln_f")},
+                        key=lambda x: (len(x), x))
+        which = ", ".join([n for n in names if "." not in n] + [f"layer {x}" for x in layers]
+                          + [n for n in names if n.startswith("ln_f")]) if len(names) > 3 else ", ".join(names)
+        if len(which) > 160:
+            which = f"{names[0]} ... {names[-1]}"
         cpu = {"value": round(rate / 1e9, 6), "unit": "Gparams/s", "cores": 1, "kind": "oracle",
                "sample": f"one step of {n_el} elements: the first min(numel, {args.cpu_cap_elems}) elements of "
-                         f"each of {len(subset)} tensors ({names[0]}, {names[1]}, layers {names[2].split('.')[0]} "
-                         f"and {names[-3].split('.')[0]}, {names[-2]}, {names[-1]}); {cpu_s:.1f} s, numpy, "
+                         f"each of {len(subset)} tensors ({which}); {cpu_s:.1f} s, numpy, "
                          f"single thread, of {os.cpu_count()} host cores",
                "extrapolated_full_step_s": round(total / rate, 1),
                "extrapolated": "full-list single-core time = the subset's elements/s x the list's elements"}
