@@ -307,3 +307,18 @@ def test_make_tensor_refuses_mismatched_buffers():
     # raw addresses are passed through unchecked
     d = opt8.make_tensor(1 << 40, 2 << 40, 3 << 40, 4 << 40, 5 << 40, 6 << 40, numel=n)
     assert d.numel == n and d.param == 1 << 40
+
+
+def test_c_driver_links_against_the_library_and_checks_its_arguments():
+    """The plain-C boundary driver (tests/c_abi/step_file.c) builds against include/opt8.h and
+    libopt8.so, and refuses bad arguments before any HIP call (no GPU needed)."""
+    exe = os.path.join(ROOT, "tests", "c_abi", "step_file")
+    if not os.path.exists(exe):
+        pytest.fail(f"{exe} is not built (run __graft_entry__.build())")
+    out = subprocess.run([exe], capture_output=True, text=True, timeout=60)
+    assert out.returncode == 2 and "usage" in out.stderr
+    out = subprocess.run([exe, "/nonexistent", "100", "9", "0", "1", "0", "1e-3", "0", "0"],
+                         capture_output=True, text=True, timeout=60)
+    assert out.returncode == 2
+    deps = subprocess.run(["ldd", exe], capture_output=True, text=True).stdout
+    assert "libopt8.so" in deps and "not found" not in deps.split("libopt8.so", 1)[1].splitlines()[0]
