@@ -1112,16 +1112,18 @@ __device__ __forceinline__ bool block_1s_8bit_fast(const DevTensor& d, int64_t b
   return true;
 }
 
-// bf16 or fp32 state: plain operations with every rounding's NaN rule.  Full
-// blocks move whole 8-element groups with 16-byte accesses (the random words of
-// the parameter and the state come from one two-stream Philox call); the
-// partial last block goes element by element.
-template <int A, bool kBf16State, bool kFull>
-__device__ __forceinline__ void block_1s_wide(const DevTensor& d, int64_t blk, int lane, int valid,
+// bf16 state of the one-state rules: plain operations with every rounding's NaN
+// rule.  Full blocks move whole 8-element groups with 16-byte accesses (the
+// random words of the parameter and the state come from one two-stream Philox
+// call); in the group that straddles the end of a partial block, elements go
+// one by one.
+template <int A, bool kFull>
+__device__ __forceinline__ void block_1s_bf16(const DevTensor& d, int64_t blk, int lane, int valid,
                                               const StepScalars& sc) {
   const int64_t e0 = blk * kBlock;
   const uint16_t* gp = d.grad + e0;
   uint16_t* pp = d.param + e0;
+  uint16_t* mp = static_cast<uint16_t*>(d.m) + e0;
   const bool nearest = sc.param_round != 0;
   const uint64_t grp0 = static_cast<uint64_t>(d.index_base + e0) >> 3;
 #pragma unroll 1
@@ -1135,24 +1137,12 @@ __device__ __forceinline__ void block_1s_wide(const DevTensor& d, int64_t blk, i
     if (whole) {
       const uint4 G = ld_stream16(gp + off);
       const uint4 P = ld_stream16(pp + off);
+      const uint4 M = ld_stream16(mp + off);
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         g[j] = bf16_at(G, j);
         p[j] = bf16_at(P, j);
-      }
-      if constexpr (kBf16State) {
-        const uint4 M = ld_stream16(static_cast<const uint16_t*>(d.m) + e0 + off);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) m1[j] = bf16_at(M, j);
-      } else {
-        const float* mf = static_cast<const float*>(d.m) + e0 + off;
-        const uint4 M0 = ld_stream16(mf);
-        const uint4 M1 = ld_stream16(mf + 4);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          m1[j] = __uint_as_float(word_of(M0, j));
-          m1[j + 4] = __uint_as_float(word_of(M1, j));
-        }
+        m1[j] = bf16_at(M, j);
       }
     } else {
 #pragma unroll
@@ -1160,59 +1150,39 @@ __device__ __forceinline__ void block_1s_wide(const DevTensor& d, int64_t blk, i
         const bool ok = off + j < valid;
         g[j] = ok ? __uint_as_float(static_cast<uint32_t>(gp[off + j]) << 16) : 0.0f;
         p[j] = ok ? __uint_as_float(static_cast<uint32_t>(pp[off + j]) << 16) : 0.0f;
-        if constexpr (kBf16State)
-          m1[j] = ok ? __uint_as_float(static_cast<uint32_t>(static_cast<uint16_t*>(d.m)[e0 + off + j]) << 16)
-                     : 0.0f;
-        else
-          m1[j] = ok ? static_cast<float*>(d.m)[e0 + off + j] : 0.0f;
+        m1[j] = ok ? __uint_as_float(static_cast<uint32_t>(mp[off + j]) << 16) : 0.0f;
       }
     }
+    // streams 0 (parameter) and 1 (state) in one call
     const uint64_t grp = grp0 + (off >> 3);
-    Rand4 rp{{0, 0, 0, 0}}, rm{{0, 0, 0, 0}};
-    if constexpr (kBf16State) {
-      // streams 0 (parameter) and 1 (state) in one call
-      uint32_t c0[2], c1[2], c2[2], c3[2];
+    uint32_t c0[2], c1[2], c2[2], c3[2];
 #pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        c0[s] = static_cast<uint32_t>(grp);
-        c1[s] = static_cast<uint32_t>(grp >> 32) | (static_cast<uint32_t>(s) << 30);
-        c2[s] = sc.step_lo;
-        c3[s] = d.tensor_id;
-      }
-      philox10_n<2>(c0, c1, c2, c3, sc.seed_lo, sc.seed_hi);
-      rp = Rand4{{c0[0], c1[0], c2[0], c3[0]}};
-      rm = Rand4{{c0[1], c1[1], c2[1], c3[1]}};
-    } else if (!nearest) {
-      rp = group_bits(grp, 0u, d.tensor_id, sc);
+    for (int s = 0; s < 2; ++s) {
+      c0[s] = static_cast<uint32_t>(grp);
+      c1[s] = static_cast<uint32_t>(grp >> 32) | (static_cast<uint32_t>(s) << 30);
+      c2[s] = sc.step_lo;
+      c3[s] = d.tensor_id;
     }
+    philox10_n<2>(c0, c1, c2, c3, sc.seed_lo, sc.seed_hi);
+    const Rand4 rp{{c0[0], c1[0], c2[0], c3[0]}};
+    const Rand4 rm{{c0[1], c1[1], c2[1], c3[1]}};
     uint32_t po[4] = {0, 0, 0, 0}, mo[4] = {0, 0, 0, 0};
-    float M2[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const float pn = update1<A>(p[j], g[j], m1[j], sc, M2[j]);
+      float m2;
+      const float pn = update1<A>(p[j], g[j], m1[j], sc, m2);
       po[j >> 1] |= to_bf16(pn, r16_of(rp, j), nearest) << (16 * (j & 1));
-      if constexpr (kBf16State) mo[j >> 1] |= to_bf16(M2[j], r16_of(rm, j), false) << (16 * (j & 1));
+      mo[j >> 1] |= to_bf16(m2, r16_of(rm, j), false) << (16 * (j & 1));
     }
     if (whole) {
       st_stream16(pp + off, make_uint4(po[0], po[1], po[2], po[3]));
-      if constexpr (kBf16State) {
-        st_stream16(static_cast<uint16_t*>(d.m) + e0 + off, make_uint4(mo[0], mo[1], mo[2], mo[3]));
-      } else {
-        float* mf = static_cast<float*>(d.m) + e0 + off;
-        st_stream16(mf, make_uint4(__float_as_uint(M2[0]), __float_as_uint(M2[1]), __float_as_uint(M2[2]),
-                                   __float_as_uint(M2[3])));
-        st_stream16(mf + 4, make_uint4(__float_as_uint(M2[4]), __float_as_uint(M2[5]), __float_as_uint(M2[6]),
-                                       __float_as_uint(M2[7])));
-      }
+      st_stream16(mp + off, make_uint4(mo[0], mo[1], mo[2], mo[3]));
     } else {
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         if (off + j < valid) {
           pp[off + j] = static_cast<uint16_t>(po[j >> 1] >> (16 * (j & 1)));
-          if constexpr (kBf16State)
-            static_cast<uint16_t*>(d.m)[e0 + off + j] = static_cast<uint16_t>(mo[j >> 1] >> (16 * (j & 1)));
-          else
-            static_cast<float*>(d.m)[e0 + off + j] = M2[j];
+          mp[off + j] = static_cast<uint16_t>(mo[j >> 1] >> (16 * (j & 1)));
         }
       }
     }
@@ -1386,8 +1356,8 @@ step_kernel(const DevTensor* __restrict__ list, int ntensors, int64_t total_bloc
         if (!done) block_1s_8bit_plain<A, false, SS>(d, tail, lane, valid, sc, lds);
       } else if constexpr (K == Kind::kBf16) {
         const int64_t left = d.numel - blk * kBlock;
-        if (left >= kBlock) block_1s_wide<A, true, true>(d, blk, lane, kBlock, sc);
-        else block_1s_wide<A, true, false>(d, blk, lane, static_cast<int>(left), sc);
+        if (left >= kBlock) block_1s_bf16<A, true>(d, blk, lane, kBlock, sc);
+        else block_1s_bf16<A, false>(d, blk, lane, static_cast<int>(left), sc);
       } else {
         const int64_t left = d.numel - blk * kBlock;
         block_1s_fp32<A>(d, blk, lane, left >= kBlock ? kBlock : static_cast<int>(left), sc);
