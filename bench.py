@@ -8,16 +8,25 @@ tensor: dequantise, AdamW in fp32, stochastic bf16 param write, block absmax,
 requantise); --algo lion / momentum time the one-state rules on the same list.
 Inputs are synthetic and already resident in HBM when the timed region starts;
 a small pool of gradient sets gives each step fresh gradients without
-generating them inside the timed region.  Prints ONE JSON line.
+generating them inside the timed region.  Without --steps/--warmup, both loops
+run at least 20 / 10 steps and at least a quarter of a second each (a list of
+many small tensors steps in about 0.26 ms; the GPU clock needs tens of
+milliseconds to settle).  Prints ONE JSON line.
 """
 
 import argparse
 import json
+import math
 import os
 import sys
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
+# The GPU's clock takes tens of milliseconds to settle after the first launches: a
+# short step (a list of many small tensors takes about 0.26 ms) warms up and is timed
+# over at least this long, so the rate is the one a training loop sees.
+MIN_WARM_S = 0.25
+MIN_TIMED_S = 0.25
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published peak
@@ -197,8 +206,10 @@ class ClockSampler:
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps (default: at least 20, and enough for about %.2f s)" % MIN_TIMED_S)
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed steps first (default: at least 10, and enough for about %.2f s)" % MIN_WARM_S)
     ap.add_argument("--workload", default="gptneo-6.7b")
     ap.add_argument("--grad-pool", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -249,7 +260,10 @@ def main():
 
     # ---------------------------------------------------------------- inputs in HBM
     t0 = time.time()
-    pool = max(1, min(args.grad_pool, args.steps + args.warmup))
+    if args.steps is None or args.warmup is None:
+        pool = max(1, args.grad_pool)
+    else:
+        pool = max(1, min(args.grad_pool, args.steps + args.warmup))
     tensors = []
     modes = {0: 0, 1: 0, 2: 0}
     alg = {0: 0, 1: 0, 2: 0}
@@ -302,23 +316,51 @@ def main():
     # step 1 (zero state) is timed on its own inside the warmup: its blocks start from absmax 0
     t_step = 1
     step1_ms = None
-    for w_i in range(args.warmup):
-        if w_i == 0:
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
-            step(t_step)
-            e1.record()
-            torch.cuda.synchronize()
-            step1_ms = e0.elapsed_time(e1)
-        else:
-            step(t_step)
+    warmup = 0
+    est_s = None
+    if args.warmup is None or args.warmup > 0:
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        step(t_step)
+        e1.record()
+        torch.cuda.synchronize()
+        step1_ms = e0.elapsed_time(e1)
         t_step += 1
+        warmup = 1
+        if args.warmup is None:
+            # chunks of steps until a quarter second has passed; the last chunk's
+            # rate sizes the default timed loop
+            c0 = time.perf_counter()
+            chunk = 9
+            while True:
+                c1 = time.perf_counter()
+                for _ in range(chunk):
+                    step(t_step)
+                    t_step += 1
+                torch.cuda.synchronize()
+                warmup += chunk
+                est_s = (time.perf_counter() - c1) / chunk
+                if warmup >= 10 and time.perf_counter() - c0 >= MIN_WARM_S:
+                    break
+                chunk = max(8, min(4 * chunk, int(0.05 / est_s)))
+        else:
+            c1 = time.perf_counter()
+            for _ in range(args.warmup - 1):
+                step(t_step)
+                t_step += 1
+            torch.cuda.synchronize()
+            warmup = args.warmup
+            if args.warmup > 1:
+                est_s = (time.perf_counter() - c1) / (args.warmup - 1)
+    steps = args.steps
+    if steps is None:
+        steps = max(20, math.ceil(MIN_TIMED_S / est_s)) if est_s else 20
     torch.cuda.synchronize()
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
-    for k in range(args.steps):
+    for k in range(steps):
         starts[k].record()
         step(t_step)
         ends[k].record()
@@ -331,7 +373,7 @@ def main():
     clocks = ClockSampler(getattr(torch.cuda.get_device_properties(dev), "pci_bus_id", None))
     n_clock = 0
     if clock_s > 0 and clocks.smi is not None:
-        est_ms = max(wall * 1000.0 / args.steps, 0.05)
+        est_ms = max(wall * 1000.0 / steps, 0.05)
         with clocks:
             c0 = time.perf_counter()
             while time.perf_counter() - c0 < clock_s:
@@ -343,7 +385,7 @@ def main():
     clock_note = (f"sampled every 50 ms while {n_clock} more steps ran back to back after the timed ones "
                   f"(about {clock_s:.0f} s, untimed), the first second dropped")
     ev_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
-    ms_per_step = wall * 1000.0 / args.steps
+    ms_per_step = wall * 1000.0 / steps
     ev_avg = sum(ev_ms) / len(ev_ms)
     value = total / (ms_per_step / 1000.0) / 1e9
     log(f"wall {ms_per_step:.3f} ms/step; events per step: avg {ev_avg:.3f} min {min(ev_ms):.3f} "
@@ -484,8 +526,8 @@ def main():
         "value": round(value, 3),
         "unit": "Gparams/s",
         "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
+        "steps": steps,
+        "warmup": warmup,
         "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True,
         "scaling": "weak",

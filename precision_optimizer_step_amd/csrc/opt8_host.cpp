@@ -327,17 +327,85 @@ int validate_tensors(const opt8_tensor* t, int32_t n, bool two_state) {
   return OPT8_OK;
 }
 
-// Validation is a pure function of the descriptor values, and a training loop
-// passes the same lists every step (often two: parameters with and without
-// weight decay): each thread keeps copies of the last four lists that passed,
-// and a list identical to one of them (byte for byte, same rule) is not
-// checked again.  A hit costs one memcmp instead of sorting 6n ranges.
+// ----------------------------------------------------------------------------- launch plans
+constexpr int kKinds = 4;
+
+// The device-side form of a tensor list: one sub-list per kernel, each with its
+// own block numbering (full blocks of 8-bit tensors, bf16-state tensors,
+// fp32-state tensors, the partial last block of 8-bit tensors), in that order.
+struct Plan {
+  std::vector<DevTensor> list;
+  int count[kKinds] = {0, 0, 0, 0};
+  int first[kKinds] = {0, 0, 0, 0};
+  int64_t blocks[kKinds] = {0, 0, 0, 0};
+};
+
+// Blocks tensor `x` contributes to the sub-list of `kind` (0: not in it).
+int64_t blocks_in_kind(const opt8_tensor& x, int kind) {
+  const bool tail = kind == static_cast<int>(Kind::k8bitTail);
+  const int mode = tail ? OPT8_STATE_8BIT : kind;
+  if (x.mode != mode) return 0;
+  if (tail) return (x.numel % kBlock) ? 1 : 0;
+  if (kind == static_cast<int>(Kind::k8bit)) return x.numel / kBlock;
+  return nblocks_of(x.numel);
+}
+
+// Two passes over the caller's array: count each sub-list, then place every
+// descriptor at its final position.
+void build_plan(const opt8_tensor* t, int32_t n, bool two_state, Plan& p) {
+  p = Plan{};
+  int64_t total = 0;
+  for (int32_t i = 0; i < n; ++i)
+    for (int kind = 0; kind < kKinds; ++kind)
+      if (blocks_in_kind(t[i], kind)) ++p.count[kind];
+  for (int kind = 0; kind < kKinds; ++kind) {
+    p.first[kind] = static_cast<int>(total);
+    total += p.count[kind];
+  }
+  p.list.resize(static_cast<size_t>(total));
+  int pos[kKinds];
+  for (int kind = 0; kind < kKinds; ++kind) pos[kind] = p.first[kind];
+  for (int32_t i = 0; i < n; ++i) {
+    const opt8_tensor& x = t[i];
+    const bool q8 = x.mode == OPT8_STATE_8BIT;
+    for (int kind = 0; kind < kKinds; ++kind) {
+      const int64_t nb = blocks_in_kind(x, kind);
+      if (!nb) continue;
+      DevTensor& d = p.list[pos[kind]++];
+      d.param = x.param;
+      d.grad = x.grad;
+      d.m = x.m;
+      d.v = two_state ? x.v : nullptr;
+      d.amax_m = q8 ? x.absmax_m : nullptr;
+      d.amax_v = (two_state && q8) ? x.absmax_v : nullptr;
+      d.numel = x.numel;
+      d.index_base = x.index_base;
+      d.block_begin = p.blocks[kind];
+      d.tensor_id = x.tensor_id;
+      d.nblocks = static_cast<uint32_t>(nb);
+      p.blocks[kind] += nb;
+    }
+  }
+}
+
+// Validation and the launch plan are pure functions of the descriptor values,
+// and a training loop passes the same lists every step (often two: parameters
+// with and without weight decay): each thread keeps copies of the last four
+// lists that passed, with their plans, and a list identical to one of them
+// (byte for byte, same rule) is neither checked nor planned again.  A hit costs
+// one memcmp instead of sorting 6n ranges and building 2n descriptors.
 constexpr int kValidated = 4;
 struct ValidatedList {
   std::vector<opt8_tensor> list;
   bool two_state = false;
   bool valid = false;
   uint64_t stamp = 0;
+  Plan plan;
+  // the device descriptor slot that held plan.list when it was last uploaded;
+  // the link holds while that slot's generation is unchanged
+  int slot_dev = -1;
+  int slot_index = -1;
+  uint64_t slot_gen = 0;
 };
 struct ValidatedCache {
   ValidatedList entry[kValidated];
@@ -345,7 +413,7 @@ struct ValidatedCache {
 };
 thread_local ValidatedCache t_validated;
 
-int validate_tensors_cached(const opt8_tensor* t, int32_t n, bool two_state) {
+int validate_tensors_cached(const opt8_tensor* t, int32_t n, bool two_state, ValidatedList*& out) {
   ValidatedCache& c = t_validated;
   ++c.clock;
   const size_t bytes = sizeof(opt8_tensor) * static_cast<size_t>(n);
@@ -354,6 +422,7 @@ int validate_tensors_cached(const opt8_tensor* t, int32_t n, bool two_state) {
     if (e.valid && e.two_state == two_state && e.list.size() == static_cast<size_t>(n) &&
         std::memcmp(e.list.data(), t, bytes) == 0) {
       e.stamp = c.clock;
+      out = &e;
       return OPT8_OK;
     }
     if (!e.valid) victim = &e;
@@ -361,10 +430,16 @@ int validate_tensors_cached(const opt8_tensor* t, int32_t n, bool two_state) {
   }
   const int rc = validate_tensors(t, n, two_state);
   if (rc != OPT8_OK) return rc;
+  victim->valid = false;
   victim->list.assign(t, t + n);
+  build_plan(t, n, two_state, victim->plan);
   victim->two_state = two_state;
+  victim->slot_dev = -1;
+  victim->slot_index = -1;
+  victim->slot_gen = 0;
   victim->valid = true;
   victim->stamp = c.clock;
+  out = victim;
   return OPT8_OK;
 }
 
@@ -373,7 +448,6 @@ int validate_tensors_cached(const opt8_tensor* t, int32_t n, bool two_state) {
 // passed again (the usual training loop) is launched without a new upload.
 constexpr int kSlots = 4;
 constexpr int kMaxDevices = 64;
-constexpr int kKinds = 4;
 constexpr int kAlgos = 3;
 
 struct Slot {
@@ -385,6 +459,7 @@ struct Slot {
   hipStream_t last_stream = nullptr;
   bool used = false;
   uint64_t stamp = 0;
+  uint64_t gen = 0;            // changes whenever the contents are rewritten
 };
 
 struct DeviceState {
@@ -399,6 +474,7 @@ struct DeviceState {
 
 std::mutex g_mu;
 DeviceState g_dev[kMaxDevices];
+uint64_t g_slot_gen = 0;   // source of slot generations, unique across devices
 
 int hip_fail(hipError_t e, const char* what) {
   return fail(OPT8_E_HIP, "%s failed: %s", what, hipGetErrorString(e));
@@ -432,21 +508,27 @@ bool same_list(const std::vector<DevTensor>& a, const std::vector<DevTensor>& b)
   return a.size() == b.size() && std::memcmp(a.data(), b.data(), a.size() * sizeof(DevTensor)) == 0;
 }
 
+// Marks slot `s`, which already holds the list, as used by work queued next on
+// `stream`: that work is ordered after the launches that last read it.
+int reuse_slot(DeviceState& ds, Slot& s, hipStream_t stream) {
+  if (s.last_stream != stream) {
+    const hipError_t e = hipStreamWaitEvent(stream, s.done, 0);
+    if (e != hipSuccess) return hip_fail(e, "hipStreamWaitEvent");
+  }
+  s.stamp = ++ds.clock;
+  return OPT8_OK;
+}
+
 // Returns the slot holding `list` on the device, ordered before work queued
 // next on `stream`.
 int acquire_slot(DeviceState& ds, const std::vector<DevTensor>& list, hipStream_t stream, Slot*& out) {
-  ++ds.clock;
   for (Slot& s : ds.slots) {
     if (s.used && same_list(s.key, list)) {
-      if (s.last_stream != stream) {
-        const hipError_t e = hipStreamWaitEvent(stream, s.done, 0);
-        if (e != hipSuccess) return hip_fail(e, "hipStreamWaitEvent");
-      }
-      s.stamp = ds.clock;
       out = &s;
-      return OPT8_OK;
+      return reuse_slot(ds, s, stream);
     }
   }
+  ++ds.clock;
   Slot* victim = &ds.slots[0];
   for (Slot& s : ds.slots) {
     if (!s.used) { victim = &s; break; }
@@ -467,6 +549,7 @@ int acquire_slot(DeviceState& ds, const std::vector<DevTensor>& list, hipStream_
   s.key = list;
   s.used = true;
   s.stamp = ds.clock;
+  s.gen = ++g_slot_gen;
   out = &s;
   return OPT8_OK;
 }
@@ -534,7 +617,8 @@ int run_step(int algo, const opt8_tensor* tensors, int32_t n, const opt8_hparams
   int rc = validate_hparams(*hp, algo);
   if (rc != OPT8_OK) return rc;
   if (n == 0) return OPT8_OK;
-  rc = validate_tensors_cached(tensors, n, two_state);
+  ValidatedList* vl = nullptr;
+  rc = validate_tensors_cached(tensors, n, two_state, vl);
   if (rc != OPT8_OK) return rc;
 
   std::lock_guard<std::mutex> lock(g_mu);
@@ -552,54 +636,32 @@ int run_step(int algo, const opt8_tensor* tensors, int32_t n, const opt8_hparams
   if (capture != hipStreamCaptureStatusNone)
     return fail(OPT8_E_CAPTURE, "hip_stream is being captured into a graph; the step cannot be captured");
 
-  // one sub-list per kernel, each with its own block numbering: full blocks of
-  // 8-bit tensors, bf16-state tensors, fp32-state tensors, and the partial last
-  // block of 8-bit tensors
-  // host-side list, reused by the thread's later calls
-  thread_local std::vector<DevTensor> list;
-  list.clear();
-  list.reserve(static_cast<size_t>(n) * 2);
-  int count[kKinds] = {0, 0, 0, 0};
-  int64_t blocks[kKinds] = {0, 0, 0, 0};
-  int first[kKinds] = {0, 0, 0, 0};
-  for (int kind = 0; kind < kKinds; ++kind) {
-    first[kind] = static_cast<int>(list.size());
-    const int mode = kind == static_cast<int>(Kind::k8bitTail) ? OPT8_STATE_8BIT : kind;
-    for (int32_t i = 0; i < n; ++i) {
-      const opt8_tensor& x = tensors[i];
-      if (x.mode != mode) continue;
-      int64_t nb = nblocks_of(x.numel);
-      if (kind == static_cast<int>(Kind::k8bit)) nb = x.numel / kBlock;
-      if (kind == static_cast<int>(Kind::k8bitTail)) nb = (x.numel % kBlock) ? 1 : 0;
-      if (nb == 0) continue;
-      DevTensor d;
-      d.param = x.param;
-      d.grad = x.grad;
-      d.m = x.m;
-      d.v = two_state ? x.v : nullptr;
-      d.amax_m = mode == OPT8_STATE_8BIT ? x.absmax_m : nullptr;
-      d.amax_v = (two_state && mode == OPT8_STATE_8BIT) ? x.absmax_v : nullptr;
-      d.numel = x.numel;
-      d.index_base = x.index_base;
-      d.block_begin = blocks[kind];
-      d.tensor_id = x.tensor_id;
-      d.nblocks = static_cast<uint32_t>(nb);
-      blocks[kind] += nb;
-      ++count[kind];
-      list.push_back(d);
-    }
-  }
+  const Plan& plan = vl->plan;
   Slot* slot = nullptr;
   DevTensor* dev_list = nullptr;
   if (noalloc) {
     // ordered on the stream after the work queued before it; calls on other
     // streams that are not ordered with this one race on the array
-    const hipError_t e = hipMemcpyAsync(ds.scratch, list.data(), list.size() * sizeof(DevTensor),
+    const hipError_t e = hipMemcpyAsync(ds.scratch, plan.list.data(), plan.list.size() * sizeof(DevTensor),
                                         hipMemcpyHostToDevice, stream);
     if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync(descriptors to scratch)");
     dev_list = ds.scratch;
   } else {
-    rc = acquire_slot(ds, list, stream, slot);
+    // the slot this list was uploaded to, if nothing has rewritten it since
+    if (vl->slot_dev == dev && vl->slot_index >= 0) {
+      Slot& s = ds.slots[vl->slot_index];
+      if (s.used && s.gen == vl->slot_gen) slot = &s;
+    }
+    if (slot) {
+      rc = reuse_slot(ds, *slot, stream);
+    } else {
+      rc = acquire_slot(ds, plan.list, stream, slot);
+      if (rc == OPT8_OK) {
+        vl->slot_dev = dev;
+        vl->slot_index = static_cast<int>(slot - ds.slots);
+        vl->slot_gen = slot->gen;
+      }
+    }
     if (rc != OPT8_OK) return rc;
     dev_list = slot->dev;
   }
@@ -608,10 +670,10 @@ int run_step(int algo, const opt8_tensor* tensors, int32_t n, const opt8_hparams
                                                 "8-bit last partial blocks"};
   std::string queued;
   for (int kind = 0; kind < kKinds; ++kind) {
-    if (!count[kind]) continue;
+    if (!plan.count[kind]) continue;
     const int cap = ds.num_cu * ds.occ[sc.state_round != 0][algo][kind];
-    const hipError_t e = launch_step(static_cast<Kind>(kind), algo, dev_list + first[kind], count[kind],
-                                     blocks[kind], sc, stream, cap);
+    const hipError_t e = launch_step(static_cast<Kind>(kind), algo, dev_list + plan.first[kind],
+                                     plan.count[kind], plan.blocks[kind], sc, stream, cap);
     if (e != hipSuccess) {
       // launches queued before this one still read the slot: keep its event
       // and stream current so a later call that reuses or rewrites it waits

@@ -7,6 +7,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <thread>
 #include <vector>
 
 #include "fake_hip.h"
@@ -260,6 +261,37 @@ int main() {
     CHECK(g.stream_waits == waits + 1);       // moved to another stream: ordered after the last launch
     CHECK(step(lists[5], h1, other) == OPT8_OK);
     CHECK(g.stream_waits == waits + 1);
+
+    // a list this thread has validated and planned, while another thread
+    // rewrites every slot: uploaded again, and its launch reads its own descriptors
+    {
+      const std::vector<opt8_tensor> A = {tensor(60, 4096, OPT8_STATE_8BIT, 7),
+                                          tensor(61, 4096, OPT8_STATE_8BIT, 8)};
+      CHECK(step(A, h1) == OPT8_OK);
+      long up = g.uploads;
+      CHECK(step(A, h1) == OPT8_OK);
+      CHECK(g.uploads == up);
+      int rcs[4] = {-1, -1, -1, -1};
+      std::thread writer([&] {
+        for (int l = 0; l < 4; ++l)
+          rcs[l] = step({tensor(70 + l, 8192, OPT8_STATE_8BIT, 0)}, h1);
+      });
+      writer.join();
+      for (int rc : rcs) CHECK(rc == OPT8_OK);
+      up = g.uploads;
+      g.launches.clear();
+      CHECK(step(A, h1) == OPT8_OK);
+      CHECK(g.uploads == up + 1);
+      CHECK(g.launches.size() == 1 && g.launches[0].ok);
+      if (g.launches.size() == 1) CHECK((g.launches[0].ids == std::vector<uint32_t>{7, 8}));
+      CHECK(step(A, h1) == OPT8_OK);
+      CHECK(g.uploads == up + 1);            // linked to its new slot
+      // the other thread steps the same list: its own cache misses, the slot is found by content
+      int rc_same = -1;
+      std::thread reader([&] { rc_same = step(A, h1); });
+      reader.join();
+      CHECK(rc_same == OPT8_OK && g.uploads == up + 1);
+    }
 
     // a list longer than any slot holds: the slot grows
     std::vector<opt8_tensor> big;
