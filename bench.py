@@ -412,6 +412,13 @@ def main():
                 "frac_of_attainable": None,
                 "kernel": kname,
                 "algorithmic_bytes_per_launch": alg[dom], "avg_launch_ms": round(kernel_ms, 4)}
+        ragged = sum(1 for t in tensors if t["mode"] == 0 and t["n"] % BLOCK)
+        if dom == 0 and ragged:
+            # the library launches the last partial blocks of 8-bit tensors separately: the
+            # HIP events bracket both launches, and the bytes are those of both
+            roof["kernel"] = kname + " + its last-partial-block launch"
+            roof["note"] = (f"one step is two launches (full blocks; the last partial block of each of "
+                            f"{ragged} tensors), timed and counted together")
 
     # attainable streaming bandwidth on this machine: the probe kernels (libopt8_probe.so) with a
     # plain 1:1 copy and with the step's own 3:2 read:write mix, 16-byte accesses

@@ -1332,13 +1332,26 @@ step_kernel(const DevTensor* __restrict__ list, int ntensors, int64_t total_bloc
   int64_t b = gw;
   if (b >= total_blocks) return;
 
-  int t = find_tensor(list, 0, ntensors - 1, b, lane);
-  DevTensor d = list[t];
+  // the list of last partial blocks has one block per entry, so block b is
+  // entry b: no search, and the next entry's descriptor is read while the
+  // current block is processed
+  int t = 0;
+  DevTensor d;
+  DevTensor d_next;
+  if constexpr (K == Kind::k8bitTail) {
+    d_next = list[b];
+  } else {
+    t = find_tensor(list, 0, ntensors - 1, b, lane);
+    d = list[t];
+  }
   for (; b < total_blocks; b += nw) {
-    // past the current tensor: the next one starts at or before b, and a later
-    // one holds it (b < total_blocks); a wave strides over many blocks, which
-    // for lists of small tensors crosses many descriptors at once
-    if (b >= d.block_begin + static_cast<int64_t>(d.nblocks)) {
+    if constexpr (K == Kind::k8bitTail) {
+      d = d_next;
+      if (b + nw < total_blocks) d_next = list[b + nw];
+    } else if (b >= d.block_begin + static_cast<int64_t>(d.nblocks)) {
+      // past the current tensor: the next one starts at or before b, and a later
+      // one holds it (b < total_blocks); a wave strides over many blocks, which
+      // for lists of small tensors crosses many descriptors at once
       t = find_tensor(list, t + 1, ntensors - 1, b, lane);
       d = list[t];
     }
@@ -1475,6 +1488,8 @@ hipError_t launch_step(Kind kind, int algo, const DevTensor* list, int n, int64_
       return ss ? launch_algo<Kind::k8bit, true>(algo, list, n, total_blocks, sc, stream, grid_cap, range_ok)
                 : launch_algo<Kind::k8bit, false>(algo, list, n, total_blocks, sc, stream, grid_cap, range_ok);
     case Kind::k8bitTail:
+      // its kernel reads entry b for block b: one block per entry
+      if (total_blocks != n) return hipErrorInvalidValue;
       return ss ? launch_algo<Kind::k8bitTail, true>(algo, list, n, total_blocks, sc, stream, grid_cap, range_ok)
                 : launch_algo<Kind::k8bitTail, false>(algo, list, n, total_blocks, sc, stream, grid_cap, range_ok);
     case Kind::kBf16:

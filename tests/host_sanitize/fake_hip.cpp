@@ -122,6 +122,8 @@ hipError_t launch_step(Kind kind, int algo, const DevTensor* list, int n, int64_
   for (int i = 0; i < n; ++i) {
     if (list[i].block_begin != b) L.ok = false;
     if (list[i].nblocks == 0) L.ok = false;
+    // the last-partial-block kernel reads entry b for block b
+    if (kind == Kind::k8bitTail && list[i].nblocks != 1) L.ok = false;
     b += list[i].nblocks;
     L.numel += list[i].numel;
     L.ids.push_back(list[i].tensor_id);
