@@ -86,7 +86,8 @@ typedef enum {
   OPT8_E_DUPID = -7,     /* tensor_id repeated in one list                           */
   OPT8_E_NOT_INIT = -8,  /* opt8_init_codebooks not called on the current device     */
   OPT8_E_HIP = -9,       /* a HIP runtime call or a kernel launch failed             */
-  OPT8_E_CAPTURE = -10   /* hip_stream is being captured into a graph (see below)    */
+  OPT8_E_CAPTURE = -10,  /* hip_stream is being captured into a graph (see below)    */
+  OPT8_E_NOMEM = -11     /* host memory for the library's copies of a list ran out   */
 } opt8_status;
 
 typedef enum {
@@ -170,8 +171,10 @@ int32_t opt8_default_mode(int64_t numel);
  * One AdamW step over a list of n tensors, queued on hip_stream (a
  * hipStream_t; NULL = the null stream) and asynchronous to the host.
  * Every descriptor and hyperparameter is validated first; on a validation
- * error (every status but OPT8_E_HIP) nothing is queued and nothing is
- * modified.  A step is up to four kernel launches, one per kind of tensor in
+ * error (every status but OPT8_E_HIP and OPT8_E_NOMEM) nothing is queued and
+ * nothing is modified; OPT8_E_NOMEM (the host could not allocate the
+ * library's copy of the list) is returned before any launch, with at most a
+ * descriptor upload into an unused cache slot queued.  A step is up to four kernel launches, one per kind of tensor in
  * the list (8-bit full blocks, bf16 state, fp32 state, 8-bit last partial
  * blocks); if a launch fails (OPT8_E_HIP) the kinds launched before it have
  * been queued and will step their tensors, and the message names them.

@@ -6,6 +6,7 @@
 #include <cstdio>
 #include <cstring>
 #include <mutex>
+#include <new>
 #include <string>
 #include <vector>
 
@@ -15,17 +16,29 @@
 namespace opt8 {
 namespace {
 
-thread_local std::string t_error;
+// the calling thread's last error message (a fixed buffer: reporting an
+// allocation failure must not allocate)
+thread_local char t_error[512];
 
 int fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
 int fail(int code, const char* fmt, ...) {
-  char buf[512];
   va_list ap;
   va_start(ap, fmt);
-  std::vsnprintf(buf, sizeof buf, fmt, ap);
+  std::vsnprintf(t_error, sizeof t_error, fmt, ap);
   va_end(ap);
-  t_error = buf;
   return code;
+}
+
+// No exception crosses the C ABI: host allocation failures become OPT8_E_NOMEM.
+template <class F>
+int guarded(F&& body) {
+  try {
+    return body();
+  } catch (const std::bad_alloc&) {
+    return fail(OPT8_E_NOMEM, "out of host memory");
+  } catch (...) {
+    return fail(OPT8_E_HIP, "internal error: unexpected exception");
+  }
 }
 
 // ----------------------------------------------------------------------------- codebooks
@@ -560,43 +573,45 @@ int acquire_slot(DeviceState& ds, const std::vector<DevTensor>& list, hipStream_
 using namespace opt8;
 
 extern "C" int opt8_init_codebooks(float* signed_out, float* unsigned_out) {
-  std::lock_guard<std::mutex> lock(g_mu);
-  const Tables& t = tables();
-  if (signed_out) std::memcpy(signed_out, t.cb_s(), sizeof(float) * kCodes);
-  if (unsigned_out) std::memcpy(unsigned_out, t.cb_u(), sizeof(float) * kCodes);
-  if (!t.ok) return fail(OPT8_E_HIP, "internal error: code lookup tables failed their construction check");
-  int dev = 0;
-  int rc = current_device(dev);
-  if (rc != OPT8_OK) return rc;
-  DeviceState& ds = g_dev[dev];
-  if (ds.init) return OPT8_OK;
-  hipError_t e = upload_tables(t.bytes);
-  if (e != hipSuccess) return hip_fail(e, "upload of codebooks");
-  // this device's copy of the descriptor scratch (each device has its own address)
-  e = scratch_address(&ds.scratch);
-  if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
-  e = hipDeviceGetAttribute(&ds.num_cu, hipDeviceAttributeMultiprocessorCount, dev);
-  if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute(CU count)");
-  for (int sr = 0; sr < 2; ++sr)
-    for (int a = 0; a < kAlgos; ++a)
-      for (int k = 0; k < kKinds; ++k) ds.occ[sr][a][k] = occupancy_per_cu(static_cast<Kind>(k), a, sr != 0);
-  for (Slot& s : ds.slots) {
-    if (!s.done) {
-      e = hipEventCreateWithFlags(&s.done, hipEventDisableTiming);
-      if (e != hipSuccess) return hip_fail(e, "hipEventCreateWithFlags");
+  return guarded([&]() -> int {
+    std::lock_guard<std::mutex> lock(g_mu);
+    const Tables& t = tables();
+    if (signed_out) std::memcpy(signed_out, t.cb_s(), sizeof(float) * kCodes);
+    if (unsigned_out) std::memcpy(unsigned_out, t.cb_u(), sizeof(float) * kCodes);
+    if (!t.ok) return fail(OPT8_E_HIP, "internal error: code lookup tables failed their construction check");
+    int dev = 0;
+    int rc = current_device(dev);
+    if (rc != OPT8_OK) return rc;
+    DeviceState& ds = g_dev[dev];
+    if (ds.init) return OPT8_OK;
+    hipError_t e = upload_tables(t.bytes);
+    if (e != hipSuccess) return hip_fail(e, "upload of codebooks");
+    // this device's copy of the descriptor scratch (each device has its own address)
+    e = scratch_address(&ds.scratch);
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    e = hipDeviceGetAttribute(&ds.num_cu, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute(CU count)");
+    for (int sr = 0; sr < 2; ++sr)
+      for (int a = 0; a < kAlgos; ++a)
+        for (int k = 0; k < kKinds; ++k) ds.occ[sr][a][k] = occupancy_per_cu(static_cast<Kind>(k), a, sr != 0);
+    for (Slot& s : ds.slots) {
+      if (!s.done) {
+        e = hipEventCreateWithFlags(&s.done, hipEventDisableTiming);
+        if (e != hipSuccess) return hip_fail(e, "hipEventCreateWithFlags");
+      }
     }
-  }
-  e = hipDeviceSynchronize();
-  if (e != hipSuccess) return hip_fail(e, "hipDeviceSynchronize");
-  ds.init = true;
-  return OPT8_OK;
+    e = hipDeviceSynchronize();
+    if (e != hipSuccess) return hip_fail(e, "hipDeviceSynchronize");
+    ds.init = true;
+    return OPT8_OK;
+  });
 }
 
 extern "C" int32_t opt8_default_mode(int64_t numel) {
   return numel < OPT8_FP32_STATE_THRESHOLD ? OPT8_STATE_FP32 : OPT8_STATE_8BIT;
 }
 
-extern "C" const char* opt8_last_error(void) { return t_error.c_str(); }
+extern "C" const char* opt8_last_error(void) { return t_error; }
 
 namespace opt8 {
 namespace {
@@ -606,7 +621,7 @@ namespace {
 // one copy per call instead of the cached, allocated slots.
 int run_step(int algo, const opt8_tensor* tensors, int32_t n, const opt8_hparams* hp, void* hip_stream,
              bool noalloc = false) {
-  t_error.clear();
+  t_error[0] = '\0';
   if (!hp) return fail(OPT8_E_NULL, "hparams is NULL");
   if (n < 0) return fail(OPT8_E_SIZE, "n must be >= 0 (got %d)", n);
   if (n > 0 && !tensors) return fail(OPT8_E_NULL, "tensor list is NULL");
@@ -699,20 +714,20 @@ int run_step(int algo, const opt8_tensor* tensors, int32_t n, const opt8_hparams
 
 extern "C" int opt8_adamw_step(const opt8_tensor* tensors, int32_t n, const opt8_hparams* hp,
                                void* hip_stream) {
-  return run_step(kAdamW, tensors, n, hp, hip_stream);
+  return guarded([&]() -> int { return run_step(kAdamW, tensors, n, hp, hip_stream); });
 }
 
 extern "C" int opt8_adamw_step_noalloc(const opt8_tensor* tensors, int32_t n, const opt8_hparams* hp,
                                        void* hip_stream) {
-  return run_step(kAdamW, tensors, n, hp, hip_stream, true);
+  return guarded([&]() -> int { return run_step(kAdamW, tensors, n, hp, hip_stream, true); });
 }
 
 extern "C" int opt8_lion_step(const opt8_tensor* tensors, int32_t n, const opt8_hparams* hp,
                               void* hip_stream) {
-  return run_step(kLion, tensors, n, hp, hip_stream);
+  return guarded([&]() -> int { return run_step(kLion, tensors, n, hp, hip_stream); });
 }
 
 extern "C" int opt8_momentum_step(const opt8_tensor* tensors, int32_t n, const opt8_hparams* hp,
                                   void* hip_stream) {
-  return run_step(kMomentum, tensors, n, hp, hip_stream);
+  return guarded([&]() -> int { return run_step(kMomentum, tensors, n, hp, hip_stream); });
 }

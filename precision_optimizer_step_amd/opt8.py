@@ -26,6 +26,7 @@ OPT8_E_DUPID = -7
 OPT8_E_NOT_INIT = -8
 OPT8_E_HIP = -9
 OPT8_E_CAPTURE = -10
+OPT8_E_NOMEM = -11
 
 OPT8_STATE_8BIT = 0
 OPT8_STATE_BF16_SR = 1
@@ -39,7 +40,7 @@ OPT8_STATE_ROUND_STOCHASTIC = 1
 STATUS_NAMES = {0: "OPT8_OK", -1: "OPT8_E_NULL", -2: "OPT8_E_ALIGN", -3: "OPT8_E_SIZE",
                 -4: "OPT8_E_MODE", -5: "OPT8_E_HPARAM", -6: "OPT8_E_ALIAS", -7: "OPT8_E_DUPID",
                 -8: "OPT8_E_NOT_INIT", -9: "OPT8_E_HIP",
-                -10: "OPT8_E_CAPTURE"}
+                -10: "OPT8_E_CAPTURE", -11: "OPT8_E_NOMEM"}
 
 
 class opt8_tensor(ctypes.Structure):

@@ -7,6 +7,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <new>
 #include <thread>
 #include <vector>
 
@@ -14,6 +15,18 @@
 #include "opt8.h"
 
 using fake::g;
+
+// Global allocation functions that fail on request, to check that an
+// allocation failure inside the library comes back as a status, not an exception.
+static bool g_fail_new = false;
+void* operator new(std::size_t n) {
+  if (g_fail_new) throw std::bad_alloc();
+  void* p = std::malloc(n ? n : 1);
+  if (!p) throw std::bad_alloc();
+  return p;
+}
+void operator delete(void* p) noexcept { std::free(p); }
+void operator delete(void* p, std::size_t) noexcept { std::free(p); }
 
 static int failures = 0;
 #define CHECK(cond)                                                      \
@@ -358,6 +371,22 @@ int main() {
     CHECK(g.launches.empty() && g.uploads == up);
     // the cached entry point still works alongside
     CHECK(step(mixed, h1) == OPT8_OK);
+  }
+
+  // host allocation failure: a status and a message, nothing queued, and the
+  // same list steps normally once memory is back
+  {
+    const std::vector<opt8_tensor> L = {tensor(90, 8192, OPT8_STATE_8BIT, 0)};
+    g.launches.clear();
+    const long up = g.uploads;
+    g_fail_new = true;
+    const int rc = step(L, h1);
+    g_fail_new = false;
+    CHECK(rc == OPT8_E_NOMEM);
+    CHECK(g.launches.empty() && g.uploads == up);
+    CHECK(std::strstr(opt8_last_error(), "host memory") != nullptr);
+    CHECK(step(L, h1) == OPT8_OK);
+    CHECK(g.launches.size() == 1);
   }
 
   if (failures) {
