@@ -135,12 +135,17 @@ class ClockSampler:
     """GFX (per XCD) and memory clocks of the GPU torch uses, read from the driver's metrics
     table (amdsmi) by a host thread; empty if amdsmi is unavailable.  The table refreshes
     only every few hundred milliseconds, so the clocks are sampled while the step runs back
-    to back for a few seconds, and samples from the first second are dropped."""
+    to back for a few seconds, and samples from the first second are dropped.  Also read: the
+    socket power, and the share of the sampled time the firmware spent holding the package
+    power limit (the PPT residency counter against the metrics' millisecond accumulation
+    counter)."""
 
     def __init__(self, pci_bus=None, period_s=0.05, settle_s=1.0):
         import threading
         self.period, self.settle = period_s, settle_s
-        self.gfx, self.xcd, self.mem = [], [], []
+        self.gfx, self.xcd, self.mem, self.power = [], [], [], []
+        self.acc = []   # (accumulation_counter, ppt_residency_acc) per sample
+        self.cap_w = None
         self.err = None
         self._stop = threading.Event()
         self._thread = None
@@ -156,6 +161,10 @@ class ClockSampler:
                 raise RuntimeError(f"cannot tell which of {len(handles)} GPUs is in use")
             self.handle = match[0] if len(match) == 1 else handles[0]
             self.smi.amdsmi_get_gpu_metrics_info(self.handle)
+            try:   # microwatts
+                self.cap_w = amdsmi.amdsmi_get_power_cap_info(self.handle)["power_cap"] / 1e6
+            except Exception:
+                self.cap_w = None
         except Exception as e:   # no amdsmi or no permission: the clock is reported as unknown
             self.smi = None
             self.err = f"{type(e).__name__}: {e}"
@@ -171,6 +180,11 @@ class ClockSampler:
                     xs = [float(x) for x in (m.get("current_gfxclks") or []) if isinstance(x, (int, float))]
                     if xs:
                         self.xcd.append(xs)
+                    if isinstance(m.get("current_socket_power"), (int, float)):
+                        self.power.append(float(m["current_socket_power"]))
+                    a, r = m.get("accumulation_counter"), m.get("ppt_residency_acc")
+                    if isinstance(a, (int, float)) and isinstance(r, (int, float)):
+                        self.acc.append((a, r))
             except Exception as e:
                 self.err = f"{type(e).__name__}: {e}"
                 return
@@ -200,6 +214,11 @@ class ClockSampler:
         if self.xcd:
             per = list(zip(*self.xcd))
             out["gfx_mhz_per_xcd_median"] = [sorted(x)[len(x) // 2] for x in per]
+        if self.power:
+            pw = sorted(self.power)
+            out["socket_power_w"] = {"median": pw[len(pw) // 2], "max": pw[-1], "cap": self.cap_w}
+        if len(self.acc) >= 2 and self.acc[-1][0] > self.acc[0][0]:
+            out["power_limited_frac"] = round((self.acc[-1][1] - self.acc[0][1]) / (self.acc[-1][0] - self.acc[0][0]), 3)
         return out
 
 
