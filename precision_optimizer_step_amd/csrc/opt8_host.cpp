@@ -548,18 +548,22 @@ int acquire_slot(DeviceState& ds, const std::vector<DevTensor>& list, hipStream_
     if (s.stamp < victim->stamp) victim = &s;
   }
   Slot& s = *victim;
-  if (s.used) {   // every launch that read it has finished before it is rewritten
-    const hipError_t e = hipEventSynchronize(s.done);
-    if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize");
-  }
+  // the last upload from the staging buffer and every launch that read the
+  // slot have finished before either is rewritten (an event never recorded
+  // counts as complete)
+  hipError_t e = hipEventSynchronize(s.done);
+  if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize");
   s.used = false;
   int rc = ensure_capacity(s, list.size());
   if (rc != OPT8_OK) return rc;
+  s.key = list;   // may throw: nothing is queued yet
   std::memcpy(s.host, list.data(), list.size() * sizeof(DevTensor));
-  const hipError_t e = hipMemcpyAsync(s.dev, s.host, list.size() * sizeof(DevTensor),
-                                      hipMemcpyHostToDevice, stream);
+  e = hipMemcpyAsync(s.dev, s.host, list.size() * sizeof(DevTensor), hipMemcpyHostToDevice, stream);
   if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync(descriptors)");
-  s.key = list;
+  // until the step's launches record it again, the event follows the upload
+  e = hipEventRecord(s.done, stream);
+  if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
+  s.last_stream = stream;
   s.used = true;
   s.stamp = ds.clock;
   s.gen = ++g_slot_gen;
@@ -692,7 +696,7 @@ int run_step(int algo, const opt8_tensor* tensors, int32_t n, const opt8_hparams
     if (e != hipSuccess) {
       // launches queued before this one still read the slot: keep its event
       // and stream current so a later call that reuses or rewrites it waits
-      if (!queued.empty() && slot) {
+      if (slot) {
         (void)hipEventRecord(slot->done, stream);
         slot->last_stream = stream;
       }

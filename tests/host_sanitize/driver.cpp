@@ -389,6 +389,25 @@ int main() {
     CHECK(g.launches.size() == 1);
   }
 
+  // a launch that fails right after its list was uploaded: the slot's event
+  // follows the upload, so a later rewrite of that slot's staging buffer waits
+  // for the copy; and the list steps normally afterwards
+  {
+    const std::vector<opt8_tensor> F = {tensor(1300, 8192, OPT8_STATE_8BIT, 0)};
+    g.fail_launch_kind = 0;
+    const long up = g.uploads;
+    CHECK(step(F, h1) == OPT8_E_HIP);
+    g.fail_launch_kind = -1;
+    CHECK(g.uploads == up + 1);
+    CHECK(std::strstr(opt8_last_error(), "already queued: nothing") != nullptr);
+    for (int l = 0; l < 5; ++l)   // five new lists: every slot rewritten
+      CHECK(step({tensor(1310 + l, 8192, OPT8_STATE_8BIT, 0)}, h1) == OPT8_OK);
+    g.launches.clear();
+    CHECK(step(F, h1) == OPT8_OK);
+    CHECK(g.launches.size() == 1 && g.launches[0].ok);
+  }
+  CHECK(g.reuse_violations == 0);   // no staging buffer was rewritten or freed under its copy
+
   if (failures) {
     std::printf("%d host checks failed\n", failures);
     return 1;

@@ -4,6 +4,7 @@
 // prologue, launch planning) can run under AddressSanitizer and UBSan on a
 // machine without a GPU.  "Device" memory is host memory; launches are
 // recorded and their descriptor lists checked the way the kernels walk them.
+#include <algorithm>
 #include <cstdint>
 #include <cstdio>
 #include <cstdlib>
@@ -33,25 +34,26 @@ hipError_t hipDeviceGetAttribute(int* value, hipDeviceAttribute_t, int) {
 
 hipError_t hipDeviceSynchronize(void) { return hipSuccess; }
 
+// an event holds the sequence number of its last record (0: never recorded)
 hipError_t hipEventCreateWithFlags(hipEvent_t* event, unsigned) {
-  *event = reinterpret_cast<hipEvent_t>(new int(0));
+  *event = reinterpret_cast<hipEvent_t>(new long(0));
   ++g.events;
   return hipSuccess;
 }
 
 hipError_t hipEventRecord(hipEvent_t event, hipStream_t) {
-  ++*reinterpret_cast<int*>(event);
+  *reinterpret_cast<long*>(event) = ++g.seq;
   return hipSuccess;
 }
 
 hipError_t hipEventSynchronize(hipEvent_t event) {
-  (void)*reinterpret_cast<int*>(event);
+  g.completed = std::max(g.completed, *reinterpret_cast<long*>(event));
   ++g.event_syncs;
   return hipSuccess;
 }
 
 hipError_t hipStreamWaitEvent(hipStream_t, hipEvent_t event, unsigned) {
-  (void)*reinterpret_cast<int*>(event);
+  (void)*reinterpret_cast<long*>(event);
   ++g.stream_waits;
   return hipSuccess;
 }
@@ -77,10 +79,17 @@ hipError_t hipFree(void* ptr) {
 hipError_t hipHostMalloc(void** ptr, size_t size, unsigned) {
   *ptr = std::malloc(size);
   ++g.host_mallocs;
+  g.pinned.emplace_back(*ptr, 0L);
   return hipSuccess;
 }
 
 hipError_t hipHostFree(void* ptr) {
+  for (size_t i = 0; i < g.pinned.size(); ++i)
+    if (g.pinned[i].first == ptr) {
+      if (g.pinned[i].second > g.completed) ++g.reuse_violations;   // freed under a copy
+      g.pinned.erase(g.pinned.begin() + static_cast<long>(i));
+      break;
+    }
   std::free(ptr);
   return hipSuccess;
 }
@@ -88,6 +97,11 @@ hipError_t hipHostFree(void* ptr) {
 hipError_t hipMemcpyAsync(void* dst, const void* src, size_t bytes, hipMemcpyKind, hipStream_t) {
   std::memcpy(dst, src, bytes);
   ++g.uploads;
+  for (auto& p : g.pinned)
+    if (p.first == src) {
+      if (p.second > g.completed) ++g.reuse_violations;
+      p.second = ++g.seq;
+    }
   return hipSuccess;
 }
 
@@ -108,6 +122,7 @@ hipError_t upload_tables(const uint8_t* host_tables) {
 
 hipError_t launch_step(Kind kind, int algo, const DevTensor* list, int n, int64_t total_blocks,
                        const StepScalars& sc, hipStream_t, int grid_cap) {
+  if (static_cast<int>(kind) == g.fail_launch_kind) return hipErrorInvalidValue;
   fake::Launch L;
   L.list = list;
   L.kind = static_cast<int>(kind);

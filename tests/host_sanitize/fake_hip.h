@@ -27,6 +27,14 @@ struct State {
   const void* scratch_lo = nullptr;   // extent of the stand-in descriptor scratch
   const void* scratch_hi = nullptr;
   long table_uploads = 0;
+  // stream-order model: every upload and event record takes the next
+  // sequence number; synchronising on an event completes everything up to
+  // its number.  An upload from a pinned staging buffer whose previous upload
+  // has not completed is a reuse violation (the host would have overwritten
+  // the buffer while the copy could still be reading it).
+  long seq = 0, completed = 0, reuse_violations = 0;
+  int fail_launch_kind = -1;   // launch_step of this kind fails
+  std::vector<std::pair<const void*, long>> pinned;   // staging buffer, seq of its last upload
   uint32_t table_sum = 0;
   std::vector<Launch> launches;
 };
