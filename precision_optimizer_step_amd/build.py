@@ -31,7 +31,7 @@ def kernel_fingerprint() -> str:
     """sha256 over the kernel sources and the device compile flags (names a kernel build)."""
     import hashlib
     h = hashlib.sha256()
-    for name in ("opt8_kernels.hip", "opt8_internal.h"):
+    for name in ("opt8_kernels.hip", "opt8_internal.h", "opt8_exact.h"):
         with open(os.path.join(HERE, "csrc", name), "rb") as f:
             h.update(f.read())
     h.update(" ".join(FLAGS).encode())

@@ -21,6 +21,7 @@
 // denormals kept.  The fast paths reach the same bits with cheaper instruction
 // sequences whose exactness holds inside a range the block is checked
 // against; a block outside it takes the plain path.
+#include "opt8_exact.h"
 #include "opt8_internal.h"
 
 namespace opt8 {
@@ -212,38 +213,6 @@ __device__ __forceinline__ float adamw(float p, float g, float m1, float v1, con
   v2 = sc.beta2 * v1 + sc.w2 * (g * g);
   const float den = sqrtf(v2) * sc.rbc2 + sc.eps;
   return (p - sc.lrwd * p) - sc.step_size * (m2 / den);
-}
-
-// Correctly rounded sqrt for x == +0 or 2^-96 <= x < inf: one Newton step
-// from the hardware reciprocal square root, s = s0 + (x - s0^2) * y/2 with
-// s0 = x*y, the residual exact in an fma.  Checked against the correctly
-// rounded root for every fp32 in [2^-96, inf) on gfx950 (v_sqrt_f32 alone is
-// one ulp off for about 15% of them).  Below 2^-96 the residual can underflow;
-// the input floor 2^-126 (an integer max on the bits, equal to the float max
-// for x >= +0) keeps y finite so that x = 0 gives 0, and a negative x keeps its
-// bits, so its root is NaN as the IEEE one.  Outside that range the plain
-// sqrtf is used.
-__device__ __forceinline__ float sqrt_rn(float x) {
-  const float y = __builtin_amdgcn_rsqf(__uint_as_float(max(__float_as_uint(x), 0x00800000u)));
-  const float s0 = x * y;
-  const float h = 0.5f * y;
-  const float r = __builtin_fmaf(-s0, s0, x);
-  return __builtin_fmaf(r, h, s0);
-}
-
-// Correctly rounded a / d by a refined reciprocal and one residual
-// correction, valid when a == +-0 or 2^-100 < |a/d|, and |a| and d are normal
-// and far from overflow (no operand or residual leaves the normal range).  Checked against IEEE division on gfx950 for every pair of
-// significands (a, d in [1, 2), 2^46 pairs) and for 1.7e10 random pairs
-// across the exponent ranges of the step; the unrefined reciprocal fails
-// both.  The residual is kept negated so a zero quotient keeps the sign of a.
-__device__ __forceinline__ float div_rn(float a, float d) {
-  const float r0 = __builtin_amdgcn_rcpf(d);
-  const float e = __builtin_fmaf(-d, r0, 1.0f);
-  const float r = __builtin_fmaf(e, r0, r0);
-  const float q0 = a * r;
-  const float t0 = __builtin_fmaf(d, q0, -a);
-  return __builtin_fmaf(-t0, r, q0);
 }
 
 // Number of midpoints strictly below n (255 sorted midpoints): the nearest
