@@ -9,7 +9,8 @@ import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB = os.path.join(HERE, "libopt8.so")
-SOURCES = [os.path.join(HERE, "csrc", "opt8_host.cpp"), os.path.join(HERE, "csrc", "opt8_kernels.hip")]
+SOURCES = [os.path.join(HERE, "csrc", "opt8_host.cpp"), os.path.join(HERE, "csrc", "opt8_tables.cpp"),
+           os.path.join(HERE, "csrc", "opt8_kernels.hip")]
 # bandwidth probe used by bench.py for the attainable-bandwidth context figure
 PROBE_LIB = os.path.join(HERE, "libopt8_probe.so")
 PROBE_SOURCES = [os.path.join(HERE, "csrc", "bw_probe.hip")]
@@ -28,10 +29,11 @@ FLAGS = [
 
 
 def kernel_fingerprint() -> str:
-    """sha256 over the kernel sources and the device compile flags (names a kernel build)."""
+    """sha256 over the kernel sources, the table builder and the device compile flags (names a
+    kernel build)."""
     import hashlib
     h = hashlib.sha256()
-    for name in ("opt8_kernels.hip", "opt8_internal.h", "opt8_exact.h"):
+    for name in ("opt8_kernels.hip", "opt8_internal.h", "opt8_exact.h", "opt8_codes.h", "opt8_tables.cpp"):
         with open(os.path.join(HERE, "csrc", name), "rb") as f:
             h.update(f.read())
     h.update(" ".join(FLAGS).encode())

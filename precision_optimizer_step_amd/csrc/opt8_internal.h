@@ -94,6 +94,10 @@ enum class Kind : int { k8bit = 0, kBf16 = 1, kFp32 = 2, k8bitTail = 3 };
 constexpr int kNoAllocMaxTensors = 4096;
 constexpr int kScratchDescs = 2 * kNoAllocMaxTensors;
 
+// Host side (opt8_tables.cpp): fills the kTableBytesSR-byte table image;
+// false if a construction check fails (a bucket holding two midpoints).
+bool build_table_image(uint8_t* bytes);
+
 // Kernel side (opt8_kernels.hip).
 hipError_t upload_tables(const uint8_t* host_tables);   // kTableBytesSR, to the current device
 // Device address of the descriptor scratch on the current device (taken once per device).

@@ -21,6 +21,7 @@
 // denormals kept.  The fast paths reach the same bits with cheaper instruction
 // sequences whose exactness holds inside a range the block is checked
 // against; a block outside it takes the plain path.
+#include "opt8_codes.h"
 #include "opt8_exact.h"
 #include "opt8_internal.h"
 
@@ -215,28 +216,6 @@ __device__ __forceinline__ float adamw(float p, float g, float m1, float v1, con
   return (p - sc.lrwd * p) - sc.step_size * (m2 / den);
 }
 
-// Number of midpoints strictly below n (255 sorted midpoints): the nearest
-// codebook entry, ties to the lower code; NaN sorts above everything.
-__device__ __forceinline__ uint32_t code_search(float n, const float* mid) {
-  uint32_t idx = 0;
-#pragma unroll
-  for (uint32_t s = 128; s >= 1; s >>= 1) idx += (mid[idx + s - 1] < n) ? s : 0u;
-  return (n != n) ? 255u : idx;
-}
-
-// Stochastic state rounding, plain path: k = the entry at or below n (binary
-// search over the (entry, gap weight) pairs, clamped to [0, 254]), then the
-// upper entry iff fp32(fp32(n - C[k]) * W[k]) > r16; NaN stores 255.
-__device__ __forceinline__ uint32_t code_sr_search(float n, const float* pair, uint32_t r16) {
-  uint32_t pos = 0;   // #{k <= 254 : C[k] <= n}
-#pragma unroll
-  for (uint32_t s = 128; s >= 1; s >>= 1) pos += (pair[2 * (pos + s - 1)] <= n) ? s : 0u;
-  const uint32_t k = pos > 0 ? pos - 1 : 0u;
-  const float f = (n - pair[2 * k]) * pair[2 * k + 1];
-  const uint32_t code = k + ((f > static_cast<float>(r16)) ? 1u : 0u);
-  return (n != n) ? 255u : code;
-}
-
 __device__ __forceinline__ float wave_nan_max(float x) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) x = nan_max(x, __shfl_xor(x, o, 64));
@@ -380,32 +359,6 @@ __device__ __forceinline__ void block_8bit_plain(const DevTensor& d, int64_t blk
 }
 
 // ----------------------------------------------------------------------------- 8-bit, fast path
-// Codes through the bucket LUTs: code = lut[key] + (mid[lut[key]] < n).
-__device__ __forceinline__ uint32_t code_u(float n, const uint8_t* lds, const float* mid) {
-  const uint32_t key = max(__float_as_uint(n) >> 16, kKeyLo);    // 0 <= n < 2
-  const uint32_t c = lds[key];
-  return c + ((mid[c] < n) ? 1u : 0u);
-}
-
-__device__ __forceinline__ uint32_t code_s(float n, const uint8_t* lds, const float* mid) {
-  const uint32_t c = lds[__float_as_uint(n) >> 17];              // -2 < n < 2
-  return c + ((mid[c] < n) ? 1u : 0u);
-}
-
-// Stochastic state rounding through the floor LUTs (finite -2 < n < 2): the
-// entry at or below n is floor + (C[floor + 1] <= n); floors stop at 254 and
-// the last pair's entry is +inf, so k stays in [0, 254].
-template <bool kSigned>
-__device__ __forceinline__ uint32_t code_sr(float n, const uint8_t* lds, uint32_t r16) {
-  const uint32_t b = __float_as_uint(n);
-  const uint32_t key = kSigned ? (b >> 17) : max(b >> 16, kKeyLo);
-  const float* pair = reinterpret_cast<const float*>(lds + (kSigned ? kOffPairS : kOffPairU));
-  const uint32_t c = lds[kOffFloor + key];
-  const uint32_t k = c + ((pair[2 * c + 2] <= n) ? 1u : 0u);
-  const float f = (n - pair[2 * k]) * pair[2 * k + 1];
-  return k + ((f > static_cast<float>(r16)) ? 1u : 0u);
-}
-
 // A full block, or with kPartial the last block of a tensor holding `valid`
 // elements; returns false (having written nothing) when the block must take
 // the plain path instead.  Everything that could make a result NaN or leave

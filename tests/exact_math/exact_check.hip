@@ -1,8 +1,11 @@
-// Test-only GPU check of the library's short correctly rounded sequences
-// (opt8_exact.h: sqrt_rn, div_rn) against the IEEE operations the compiler
-// emits for sqrtf and '/' (correctly rounded under hipcc's defaults, which the
-// Python test confirms on a sample of the inputs with numpy).  Built in-tree
-// into libexact_check.so; nothing in the library loads it.
+// Test-only GPU checks of the library's fast paths against their plain forms:
+// the short correctly rounded sequences (opt8_exact.h: sqrt_rn, div_rn)
+// against the IEEE operations the compiler emits for sqrtf and '/' (correctly
+// rounded under hipcc's defaults, which the Python test confirms on a sample
+// of the inputs with numpy), and the bucket-LUT code lookups (opt8_codes.h)
+// against the binary searches, on the library's own table image
+// (opt8_tables.cpp).  Built in-tree into libexact_check.so; nothing in the
+// library loads it.
 //
 // Every kernel is a grid-stride loop over a 64-bit index range, run to a
 // multiple of the grid so that every lane of a wave takes the same iterations
@@ -12,7 +15,9 @@
 
 #include <hip/hip_runtime.h>
 
+#include "../../precision_optimizer_step_amd/csrc/opt8_codes.h"
 #include "../../precision_optimizer_step_amd/csrc/opt8_exact.h"
+#include "../../precision_optimizer_step_amd/csrc/opt8_internal.h"
 
 namespace {
 
@@ -119,6 +124,54 @@ div_random_kernel(uint64_t seed, uint64_t count, int ea_min, unsigned long long*
   }
 }
 
+// Code lookups for every n with bits lo + i (i < count), on the table image
+// staged in LDS as the step kernels stage it.  which: 0 signed nearest (LUT vs
+// binary search), 1 unsigned nearest, 2 signed stochastic, 3 unsigned
+// stochastic (random 16-bit draw per n from a hash of (seed, i)).  Samples are
+// (bits(n), draw, code) triples.
+__global__ void __launch_bounds__(kThreads)
+codes_kernel(const uint4* image, int which, uint32_t lo, uint64_t count, uint64_t seed, unsigned long long* bad,
+             uint32_t* sample, uint64_t every, int nsample) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[opt8::kTableBytesSR];
+  for (int k = threadIdx.x; k < opt8::kTableBytesSR / 16; k += blockDim.x) reinterpret_cast<uint4*>(lds)[k] = image[k];
+  __syncthreads();
+  const float* mid_s = reinterpret_cast<const float*>(lds + opt8::kOffMidS);
+  const float* mid_u = reinterpret_cast<const float*>(lds + opt8::kOffMidU);
+  const float* pair_s = reinterpret_cast<const float*>(lds + opt8::kOffPairS);
+  const float* pair_u = reinterpret_cast<const float*>(lds + opt8::kOffPairU);
+  const uint64_t stride = static_cast<uint64_t>(gridDim.x) * blockDim.x;
+  const uint64_t end = (count + stride - 1) / stride * stride;   // whole waves to the end
+  for (uint64_t i = static_cast<uint64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < end; i += stride) {
+    bool mismatch = false;
+    if (i < count) {
+      const uint32_t bits = lo + static_cast<uint32_t>(i);
+      const float n = __uint_as_float(bits);
+      const uint32_t r16 = static_cast<uint32_t>(splitmix64(seed ^ i) >> 48);
+      uint32_t got = 0, want = 0;
+      if (which == 0) {
+        got = opt8::code_s(n, lds, mid_s);
+        want = opt8::code_search(n, mid_s);
+      } else if (which == 1) {
+        got = opt8::code_u(n, lds, mid_u);
+        want = opt8::code_search(n, mid_u);
+      } else if (which == 2) {
+        got = opt8::code_sr<true>(n, lds, r16);
+        want = opt8::code_sr_search(n, pair_s, r16);
+      } else {
+        got = opt8::code_sr<false>(n, lds, r16);
+        want = opt8::code_sr_search(n, pair_u, r16);
+      }
+      mismatch = got != want;
+      if (i % every == 0 && i / every < static_cast<uint64_t>(nsample)) {
+        sample[3 * (i / every)] = bits;
+        sample[3 * (i / every) + 1] = r16;
+        sample[3 * (i / every) + 2] = got;
+      }
+    }
+    count_bad(mismatch, bad);
+  }
+}
+
 struct Device {
   unsigned long long* counters = nullptr;   // [0] mismatches, [1] pairs checked
   float* sample = nullptr;
@@ -197,4 +250,34 @@ extern "C" int64_t exact_check_div_random(uint64_t seed, uint64_t count, int ea_
   hipLaunchKernelGGL(div_random_kernel, dim3(kGrid), dim3(kThreads), 0, 0, seed, count, ea_min, dev.counters,
                      dev.counters + 1, dev.sample, every_of(count, nsample), nsample);
   return dev.finish(sample_out, checked);
+}
+
+// Mismatches of the LUT code lookup against the binary search over the fp32
+// bit patterns lo..hi (which: 0 signed, 1 unsigned, 2 signed stochastic, 3
+// unsigned stochastic); the table image is built by the library's own builder.
+// sample_out receives nsample (bits(n), draw, code) triples.  -1 on a HIP
+// error, -2 if the table image fails its construction check.
+extern "C" int64_t exact_check_codes(int which, uint32_t lo, uint32_t hi, uint64_t seed, uint32_t* sample_out,
+                                     int nsample) {
+  if (hi < lo || nsample < 0 || which < 0 || which > 3) return -1;
+  static uint8_t image[opt8::kTableBytesSR] __attribute__((aligned(16)));
+  if (!opt8::build_table_image(image)) return -2;
+  uint4* dimage = nullptr;
+  if (hipMalloc(&dimage, sizeof image) != hipSuccess) return -1;
+  if (hipMemcpy(dimage, image, sizeof image, hipMemcpyHostToDevice) != hipSuccess) {
+    (void)hipFree(dimage);
+    return -1;
+  }
+  const uint64_t count = static_cast<uint64_t>(hi) - lo + 1;
+  int64_t rc = -1;
+  {
+    Device dev(nsample, 3);
+    if (dev.ok) {
+      hipLaunchKernelGGL(codes_kernel, dim3(kGrid), dim3(kThreads), 0, 0, dimage, which, lo, count, seed,
+                         dev.counters, reinterpret_cast<uint32_t*>(dev.sample), every_of(count, nsample), nsample);
+      rc = dev.finish(reinterpret_cast<float*>(sample_out), nullptr);
+    }
+  }
+  (void)hipFree(dimage);
+  return rc;
 }

@@ -1,4 +1,5 @@
-"""The fast AdamW path's correctly rounded square root and division, checked on the GPU.
+"""The fast paths' exact pieces, checked on the GPU: correctly rounded square root and
+division, and the code lookups of the requantisation.
 
 The library reaches IEEE results with short sequences (opt8_exact.h): a square root
 from the hardware reciprocal square root and one Newton step, a division from a
@@ -16,6 +17,14 @@ very functions against the compiler's IEEE sqrtf and '/' over:
 
 The device reference itself is confirmed on evenly spaced samples of each sweep against
 numpy's float32 sqrt and division, which are IEEE operations on the host.
+
+The requantisation's fast path finds a code with one bucket-LUT read and one comparison
+(opt8_codes.h); the plain path binary-searches the sorted midpoints, or for stochastic state
+rounding the sorted entries.  Over every fp32 n in (-2, 2) (signed codes) and [0, 2)
+(unsigned codes), on the table image built by the library's own builder, the two agree; for
+stochastic state rounding with a random 16-bit draw per n.  Samples of each sweep are checked
+against the oracle's definitions: the count of midpoints below n (numpy searchsorted on the
+oracle's midpoints) and the oracle's stochastic code rule.
 """
 
 import ctypes
@@ -48,6 +57,9 @@ def L():
     lib.exact_check_div_random.argtypes = [ctypes.c_uint64, ctypes.c_uint64, ctypes.c_int,
                                            ctypes.POINTER(ctypes.c_ulonglong), fp, ctypes.c_int]
     lib.exact_check_div_random.restype = ctypes.c_int64
+    lib.exact_check_codes.argtypes = [ctypes.c_int, ctypes.c_uint32, ctypes.c_uint32, ctypes.c_uint64,
+                                      ctypes.POINTER(ctypes.c_uint32), ctypes.c_int]
+    lib.exact_check_codes.restype = ctypes.c_int64
     return lib
 
 
@@ -111,3 +123,41 @@ def test_div_rn_range_bound_on_the_dividend_is_needed(L):
     bad_ok = L.exact_check_div_random(20240917, 1 << 30, -89, ctypes.byref(checked), _ptr(small), 1)
     log(f"div_rn below 2^-89: {bad_all - bad_ok} mismatches")
     assert bad_ok == 0 and bad_all > 0
+
+
+# fp32 bit ranges of the normalised moments the LUTs cover: +0 <= n < 2 and -0 >= n > -2
+POSITIVE = (0x00000000, 0x3FFFFFFF)
+NEGATIVE = (0x80000000, 0xBFFFFFFF)
+WHICH = {"signed": 0, "unsigned": 1, "signed-sr": 2, "unsigned-sr": 3}
+
+
+def _codes_sweep(L, which, lo, hi, seed=0):
+    sample = np.zeros(3 * NSAMPLE, np.uint32)
+    bad = L.exact_check_codes(WHICH[which], lo, hi, seed, sample.ctypes.data_as(ctypes.POINTER(ctypes.c_uint32)),
+                              NSAMPLE)
+    log(f"code lookup {which} [{lo:#010x}, {hi:#010x}]: {bad} mismatches over {hi - lo + 1} values")
+    n = sample[0::3].view(np.float32)
+    return bad, n, sample[1::3], sample[2::3]
+
+
+@pytest.mark.parametrize("which,ranges", [("signed", (POSITIVE, NEGATIVE)), ("unsigned", (POSITIVE,))])
+def test_lut_codes_equal_the_binary_search_everywhere(L, which, ranges):
+    import oracle
+    s_tab, s_mid, u_tab, u_mid = oracle.codebook.tables()
+    mid = s_mid if which == "signed" else u_mid
+    for lo, hi in ranges:
+        bad, n, _, got = _codes_sweep(L, which, lo, hi)
+        assert bad == 0
+        assert np.array_equal(got, np.searchsorted(mid, n, side="left"))   # the oracle's rule
+
+
+@pytest.mark.parametrize("which,ranges", [("signed-sr", (POSITIVE, NEGATIVE)), ("unsigned-sr", (POSITIVE,))])
+def test_stochastic_lut_codes_equal_the_search_everywhere(L, which, ranges):
+    import oracle
+    table = oracle.state_sr.signed_table() if which == "signed-sr" else oracle.state_sr.unsigned_table()
+    weights = oracle.state_sr.gap_weights(table)
+    for k, (lo, hi) in enumerate(ranges):
+        bad, n, r16, got = _codes_sweep(L, which, lo, hi, seed=77 + k)
+        assert bad == 0
+        want = oracle.state_sr.sr_codes(n, table, weights, r16.astype(np.uint32))
+        assert np.array_equal(got, want.astype(np.uint32))

@@ -27,7 +27,7 @@ def test_host_code_is_clean_under_sanitizers(tmp_path):
            "-fsanitize=address,undefined", "-fno-sanitize-recover=all",
            "-D__HIP_PLATFORM_AMD__", "-I" + ROCM_INCLUDE, "-I" + os.path.join(ROOT, "include"),
            "-I" + CSRC, "-I" + HERE,
-           os.path.join(CSRC, "opt8_host.cpp"), os.path.join(HERE, "fake_hip.cpp"),
+           os.path.join(CSRC, "opt8_host.cpp"), os.path.join(CSRC, "opt8_tables.cpp"), os.path.join(HERE, "fake_hip.cpp"),
            os.path.join(HERE, "driver.cpp"), "-o", str(exe)]
     build = subprocess.run(cmd, capture_output=True, text=True)
     if build.returncode != 0 and "asan" in build.stderr.lower() and "cannot find" in build.stderr.lower():
