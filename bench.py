@@ -264,7 +264,11 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     opt8.opt8_init_codebooks()
-    w = shapes.get(args.workload)
+    try:
+        w = shapes.get(args.workload)
+    except ValueError as e:
+        print(json.dumps({"error": str(e)}))
+        sys.exit(2)
     one_state = args.algo != "adamw"
     algo_id = {"adamw": 0, "lion": 1, "momentum": 2}[args.algo]
     step_fn = {"adamw": opt8.opt8_adamw_step, "lion": opt8.opt8_lion_step,

@@ -139,7 +139,12 @@ WORKLOADS = {
 
 
 def get(name: str) -> Workload:
-    return WORKLOADS[name]()
+    """The workload of that name (case-insensitive); ValueError naming the known ones."""
+    by_lower = {k.lower(): k for k in WORKLOADS}
+    key = by_lower.get(name.lower())
+    if key is None:
+        raise ValueError(f"unknown workload {name!r}; known: {', '.join(WORKLOADS)}")
+    return WORKLOADS[key]()
 
 
 def subset_for_sampling(w: Workload) -> List[int]:
