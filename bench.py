@@ -66,10 +66,12 @@ def profiled_traffic(kernel: str, workload: str, key: str = "traffic_bytes"):
 
 
 def probe_bandwidth(dev, words=1 << 27, reps=5):
-    """Best GB/s of the streaming probe over three grid sizes: 1 read + 1 write stream, and
-    3 read + 2 write streams (the 8-bit step's 6 B read : 4 B written per element); and of the
-    probe with the 8-bit step's own access pattern (four read and three write streams in
-    2048-element blocks, no arithmetic), the best of one and two adjacent blocks per wave."""
+    """Best GB/s of the streaming probe over grid sizes from the resident count to 32 times it
+    (a grid larger than what fits lets finished workgroups be replaced, which the step kernels
+    need too): 1 read + 1 write stream, and 3 read + 2 write streams (the 8-bit step's 6 B
+    read : 4 B written per element); and of the probe with the 8-bit step's own access pattern
+    (four read and three write streams in 2048-element blocks, no arithmetic), the best of one
+    and two adjacent blocks per wave over grids from 2 to 256 workgroups per CU."""
     import ctypes
     import torch
     path = os.path.join(ROOT, "precision_optimizer_step_amd", "libopt8_probe.so")
@@ -85,7 +87,7 @@ def probe_bandwidth(dev, words=1 << 27, reps=5):
     res = {}
     for name, nin, nout in (("copy", 1, 1), ("mix", 3, 2)):
         best = 0.0
-        for grid in (cus * 8, cus * 16, cus * 32):
+        for grid in (cus * 8, cus * 16, cus * 32, cus * 64, cus * 128, cus * 256):
             def run():
                 assert lib.opt8_probe_stream(inp.data_ptr(), out.data_ptr(), words, nin, nout, grid,
                                              stream) == 0
@@ -111,7 +113,7 @@ def probe_bandwidth(dev, words=1 << 27, reps=5):
     v = torch.empty(n, dtype=torch.uint8, device=dev).random_(0, 255)
     for per_wave in (1, 2):
         best = 0.0
-        for grid in (cus * 2, cus * 3, cus * 4, cus * 8):
+        for grid in (cus * 2, cus * 4, cus * 8, cus * 16, cus * 32, cus * 64, cus * 128, cus * 256):
             def run():
                 assert lib.opt8_probe_pattern(g.data_ptr(), p.data_ptr(), m.data_ptr(), v.data_ptr(), nblocks,
                                               grid, per_wave, stream) == 0

@@ -537,9 +537,9 @@ int run_step(int algo, const opt8_tensor* tensors, int32_t n, const opt8_hparams
   std::string queued;
   for (int kind = 0; kind < kKinds; ++kind) {
     if (!plan.count[kind]) continue;
-    const int cap = ds.num_cu * ds.occ[sc.state_round != 0][algo][kind];
+    const int resident = ds.num_cu * ds.occ[sc.state_round != 0][algo][kind];
     const hipError_t e = launch_step(static_cast<Kind>(kind), algo, dev_list + plan.first[kind],
-                                     plan.count[kind], plan.blocks[kind], sc, stream, cap);
+                                     plan.count[kind], plan.blocks[kind], sc, stream, ds.num_cu, resident);
     if (e != hipSuccess) {
       // launches queued before this one still read the slot: keep its event
       // and stream current so a later call that reuses or rewrites it waits

@@ -103,8 +103,10 @@ hipError_t upload_tables(const uint8_t* host_tables);   // kTableBytesSR, to the
 // Device address of the descriptor scratch on the current device (taken once per device).
 hipError_t scratch_address(DevTensor** out);
 // The 8-bit kinds take the stochastic-state kernels when sc.state_round is set.
+// resident: workgroups of that kernel that fit on the device at once (CUs x
+// occupancy); the launch size itself is the kernel side's choice.
 hipError_t launch_step(Kind kind, int algo, const DevTensor* dev_list, int ntensors,
-                       int64_t total_blocks, const StepScalars& sc, hipStream_t stream, int grid_cap);
+                       int64_t total_blocks, const StepScalars& sc, hipStream_t stream, int num_cu, int resident);
 // Workgroups per CU that the kernel of this kind, algorithm and state rounding can keep resident.
 int occupancy_per_cu(Kind kind, int algo, bool state_sr);
 

@@ -11,10 +11,12 @@
 // the wave with cross-lane (DPP or shuffle) steps, so it is exact and
 // independent of order; no workgroup barrier is needed inside the block loop.
 //
-// The waves of a persistent grid stride over the blocks of the whole tensor
-// list (wave w takes blocks w, w + W, w + 2W, ... for W waves in the grid,
-// the waves numbered so that runs of 16 lie on one XCD); each workgroup
-// stages the codebooks, midpoints and code LUTs in LDS once.
+// The waves of the grid stride over the blocks of the whole tensor list (wave
+// w takes blocks w, w + W, w + 2W, ... for W waves in the grid, the waves
+// numbered so that runs of 16 lie on one XCD); the grid is several times what
+// fits on the device at once, so finished workgroups are replaced until the
+// end (launch_groups); each workgroup stages the codebooks, midpoints and
+// code LUTs in LDS once.
 //
 // Arithmetic is the step exactly as the oracle states it: fp32, one rounding
 // per operation (built with -ffp-contract=off), IEEE sqrt and divide,
@@ -1249,8 +1251,8 @@ step_kernel(const DevTensor* __restrict__ list, int ntensors, int64_t total_bloc
   }
   const int64_t nw = static_cast<int64_t>(gridDim.x) * kWaves;
   // wave gw takes blocks gw, gw + nw, gw + 2 nw, ...: the waves in flight
-  // stream through one window of adjacent blocks, which the memory system
-  // serves faster than as many separate runs
+  // (consecutive workgroups) stream through one window of adjacent blocks,
+  // which the memory system serves faster than as many separate runs
   int64_t b = gw;
   if (b >= total_blocks) return;
 
@@ -1335,12 +1337,44 @@ step_kernel(const DevTensor* __restrict__ list, int ntensors, int64_t total_bloc
   }
 }
 
+// Launch size.  A grid of only the workgroups that fit at once would give each
+// wave a fixed share of the blocks; a SIMD issues from its oldest wave first,
+// so its waves finish their shares far apart (on the 6.7B list the first
+// third of the waves is done at 62% of the kernel's time, the second at 80%)
+// and the SIMD runs the rest with one or two waves instead of three.  The
+// grid is therefore several times the resident count: the dispatcher starts a
+// new workgroup on a CU as soon as one finishes, and every SIMD keeps its
+// full set of waves until the last few hundred microseconds.  Each new
+// workgroup pays for staging the tables and finding its first tensor, so the
+// count per CU is the measured best of a sweep from 6 to 768 per CU for each
+// family on the 6.7B, 2.7B and 1.5B lists (two-state 8-bit 96, Lion 12,
+// momentum 384, bf16 and fp32 state 384; the last partial blocks, one short
+// block per tensor, keep the resident grid), and a wave gets at least four
+// blocks (one in the fp32-state kernels, whose tensors are single blocks).
+template <Kind K, int A>
+constexpr int groups_per_cu() {
+  if constexpr (K == Kind::k8bit) return A == kLion ? 12 : (A == kMomentum ? 384 : 96);
+  else if constexpr (K == Kind::kBf16 || K == Kind::kFp32) return 384;
+  else return 0;
+}
+
+template <Kind K, int A>
+int64_t launch_groups(int64_t total_blocks, int num_cu, int resident) {
+  const int64_t one_block_per_wave = (total_blocks + kWaves - 1) / kWaves;
+  int64_t grid = std::min<int64_t>(one_block_per_wave, resident);
+  if (groups_per_cu<K, A>() > 0) {
+    const int64_t min_blocks = K == Kind::kFp32 ? 1 : 4;
+    const int64_t by_work = (total_blocks + kWaves * min_blocks - 1) / (kWaves * min_blocks);
+    grid = std::max(grid, std::min<int64_t>(static_cast<int64_t>(num_cu) * groups_per_cu<K, A>(), by_work));
+  }
+  if (grid >= 64) grid &= ~int64_t{31};   // a multiple of 32 keeps the XCD-aware wave numbering
+  return std::max<int64_t>(grid, 1);
+}
+
 template <Kind K, int A, bool SS>
 hipError_t launch_kind(const DevTensor* list, int n, int64_t total_blocks, const StepScalars& sc,
-                       hipStream_t stream, int grid_cap, int range_ok) {
-  int64_t grid = (total_blocks + kWaves - 1) / kWaves;
-  if (grid_cap > 0 && grid > grid_cap) grid = grid_cap;
-  if (grid < 1) grid = 1;
+                       hipStream_t stream, int num_cu, int resident, int range_ok) {
+  const int64_t grid = launch_groups<K, A>(total_blocks, num_cu, resident);
   hipLaunchKernelGGL((step_kernel<K, A, SS>), dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0, stream,
                      list, n, total_blocks, sc, range_ok);
   return hipGetLastError();
@@ -1358,11 +1392,12 @@ int occupancy_kind() {
 // no 8-bit state and always take SS = false.
 template <Kind K, bool SS>
 hipError_t launch_algo(int algo, const DevTensor* list, int n, int64_t total_blocks, const StepScalars& sc,
-                       hipStream_t stream, int grid_cap, int range_ok) {
+                       hipStream_t stream, int num_cu, int resident, int range_ok) {
   switch (algo) {
-    case kAdamW: return launch_kind<K, kAdamW, SS>(list, n, total_blocks, sc, stream, grid_cap, range_ok);
-    case kLion: return launch_kind<K, kLion, SS>(list, n, total_blocks, sc, stream, grid_cap, range_ok);
-    case kMomentum: return launch_kind<K, kMomentum, SS>(list, n, total_blocks, sc, stream, grid_cap, range_ok);
+    case kAdamW: return launch_kind<K, kAdamW, SS>(list, n, total_blocks, sc, stream, num_cu, resident, range_ok);
+    case kLion: return launch_kind<K, kLion, SS>(list, n, total_blocks, sc, stream, num_cu, resident, range_ok);
+    case kMomentum:
+      return launch_kind<K, kMomentum, SS>(list, n, total_blocks, sc, stream, num_cu, resident, range_ok);
   }
   return hipErrorInvalidValue;
 }
@@ -1397,7 +1432,7 @@ hipError_t scratch_address(DevTensor** out) {
 }
 
 hipError_t launch_step(Kind kind, int algo, const DevTensor* list, int n, int64_t total_blocks,
-                       const StepScalars& sc, hipStream_t stream, int grid_cap) {
+                       const StepScalars& sc, hipStream_t stream, int num_cu, int resident) {
   if (n <= 0 || total_blocks <= 0) return hipSuccess;
   // the fast AdamW paths need eps well inside the normal range, a bounded
   // second-moment correction, decay and step size (they then check each
@@ -1407,17 +1442,17 @@ hipError_t launch_step(Kind kind, int algo, const DevTensor* list, int n, int64_
   const bool ss = sc.state_round != 0;
   switch (kind) {
     case Kind::k8bit:
-      return ss ? launch_algo<Kind::k8bit, true>(algo, list, n, total_blocks, sc, stream, grid_cap, range_ok)
-                : launch_algo<Kind::k8bit, false>(algo, list, n, total_blocks, sc, stream, grid_cap, range_ok);
+      return ss ? launch_algo<Kind::k8bit, true>(algo, list, n, total_blocks, sc, stream, num_cu, resident, range_ok)
+                : launch_algo<Kind::k8bit, false>(algo, list, n, total_blocks, sc, stream, num_cu, resident, range_ok);
     case Kind::k8bitTail:
       // its kernel reads entry b for block b: one block per entry
       if (total_blocks != n) return hipErrorInvalidValue;
-      return ss ? launch_algo<Kind::k8bitTail, true>(algo, list, n, total_blocks, sc, stream, grid_cap, range_ok)
-                : launch_algo<Kind::k8bitTail, false>(algo, list, n, total_blocks, sc, stream, grid_cap, range_ok);
+      return ss ? launch_algo<Kind::k8bitTail, true>(algo, list, n, total_blocks, sc, stream, num_cu, resident, range_ok)
+                : launch_algo<Kind::k8bitTail, false>(algo, list, n, total_blocks, sc, stream, num_cu, resident, range_ok);
     case Kind::kBf16:
-      return launch_algo<Kind::kBf16, false>(algo, list, n, total_blocks, sc, stream, grid_cap, range_ok);
+      return launch_algo<Kind::kBf16, false>(algo, list, n, total_blocks, sc, stream, num_cu, resident, range_ok);
     case Kind::kFp32:
-      return launch_algo<Kind::kFp32, false>(algo, list, n, total_blocks, sc, stream, grid_cap, range_ok);
+      return launch_algo<Kind::kFp32, false>(algo, list, n, total_blocks, sc, stream, num_cu, resident, range_ok);
   }
   return hipErrorInvalidValue;
 }

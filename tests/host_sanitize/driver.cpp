@@ -196,7 +196,7 @@ int main() {
     CHECK(c.kind == 2 && c.n == 1 && c.total_blocks == 1 && c.ok);
     const fake::Launch& d = g.launches[3];   // partial last blocks of 5000 and 2047
     CHECK(d.kind == 3 && d.n == 2 && d.total_blocks == 2 && d.ok);
-    for (const auto& L : g.launches) CHECK(L.grid_cap == 256 * 3 && L.algo == 0);
+    for (const auto& L : g.launches) CHECK(L.num_cu == 256 && L.resident == 256 * 3 && L.algo == 0);
     expect_scalars(a.sc, h1, true);
   }
 

@@ -121,7 +121,7 @@ hipError_t upload_tables(const uint8_t* host_tables) {
 }
 
 hipError_t launch_step(Kind kind, int algo, const DevTensor* list, int n, int64_t total_blocks,
-                       const StepScalars& sc, hipStream_t, int grid_cap) {
+                       const StepScalars& sc, hipStream_t, int num_cu, int resident) {
   if (static_cast<int>(kind) == g.fail_launch_kind) return hipErrorInvalidValue;
   fake::Launch L;
   L.list = list;
@@ -130,7 +130,8 @@ hipError_t launch_step(Kind kind, int algo, const DevTensor* list, int n, int64_
   L.n = n;
   L.total_blocks = total_blocks;
   L.sc = sc;
-  L.grid_cap = grid_cap;
+  L.num_cu = num_cu;
+  L.resident = resident;
   // the kernels find a block's tensor from block_begin and walk nblocks: the
   // numbering must be a gap-free prefix sum ending at total_blocks
   int64_t b = 0;

@@ -9,7 +9,7 @@
 namespace fake {
 
 struct Launch {
-  int kind = 0, algo = 0, n = 0, grid_cap = 0;
+  int kind = 0, algo = 0, n = 0, num_cu = 0, resident = 0;
   const void* list = nullptr;
   int64_t total_blocks = 0, numel = 0;
   opt8::StepScalars sc{};
