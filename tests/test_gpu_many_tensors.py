@@ -1,8 +1,8 @@
 """GPU parity on a list of many small tensors.
 
-Each wave of the persistent grid strides over thousands of blocks at a time,
-so on a list of small tensors every stride crosses many tensor descriptors;
-the kernels find the tensor holding a block with a wave-parallel search.  This
+Each wave of the grid strides over thousands of blocks at a time, so on a
+list of small tensors every stride crosses many tensor descriptors; the
+kernels find the tensor holding a block with a wave-parallel search.  This
 test steps 20,000 small 8-bit tensors (most with a partial last block, so the
 partial-block launch holds thousands of entries too) in one call and checks
 sampled tensors, whole, against the oracle.
