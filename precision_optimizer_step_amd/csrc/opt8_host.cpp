@@ -198,7 +198,15 @@ struct Plan {
   int count[kKinds] = {0, 0, 0, 0};
   int first[kKinds] = {0, 0, 0, 0};
   int64_t blocks[kKinds] = {0, 0, 0, 0};
+  // for every full 8-bit block, the entry of its sub-list that holds it (the
+  // kernels read it instead of searching the descriptors)
+  std::vector<uint32_t> map;
 };
+
+// Descriptor-sized device units that hold the block map after the descriptors.
+size_t map_units(const Plan& p) {
+  return (p.map.size() * sizeof(uint32_t) + sizeof(DevTensor) - 1) / sizeof(DevTensor);
+}
 
 // Blocks tensor `x` contributes to the sub-list of `kind` (0: not in it).
 int64_t blocks_in_kind(const opt8_tensor& x, int kind) {
@@ -245,6 +253,12 @@ void build_plan(const opt8_tensor* t, int32_t n, bool two_state, Plan& p) {
       d.nblocks = static_cast<uint32_t>(nb);
       p.blocks[kind] += nb;
     }
+  }
+  const int k8 = static_cast<int>(Kind::k8bit);
+  p.map.resize(static_cast<size_t>(p.blocks[k8]));
+  for (int e = 0; e < p.count[k8]; ++e) {
+    const DevTensor& d = p.list[p.first[k8] + e];
+    std::fill(p.map.begin() + d.block_begin, p.map.begin() + d.block_begin + d.nblocks, static_cast<uint32_t>(e));
   }
 }
 
@@ -381,7 +395,8 @@ int reuse_slot(DeviceState& ds, Slot& s, hipStream_t stream) {
 
 // Returns the slot holding `list` on the device, ordered before work queued
 // next on `stream`.
-int acquire_slot(DeviceState& ds, const std::vector<DevTensor>& list, hipStream_t stream, Slot*& out) {
+int acquire_slot(DeviceState& ds, const Plan& plan, hipStream_t stream, Slot*& out) {
+  const std::vector<DevTensor>& list = plan.list;
   for (Slot& s : ds.slots) {
     if (s.used && same_list(s.key, list)) {
       out = &s;
@@ -401,11 +416,15 @@ int acquire_slot(DeviceState& ds, const std::vector<DevTensor>& list, hipStream_
   hipError_t e = hipEventSynchronize(s.done);
   if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize");
   s.used = false;
-  int rc = ensure_capacity(s, list.size());
+  // the descriptors, then the block map (a function of them, so the key stays the list)
+  const size_t units = list.size() + map_units(plan);
+  int rc = ensure_capacity(s, units);
   if (rc != OPT8_OK) return rc;
   s.key = list;   // may throw: nothing is queued yet
   std::memcpy(s.host, list.data(), list.size() * sizeof(DevTensor));
-  e = hipMemcpyAsync(s.dev, s.host, list.size() * sizeof(DevTensor), hipMemcpyHostToDevice, stream);
+  if (!plan.map.empty())
+    std::memcpy(s.host + list.size(), plan.map.data(), plan.map.size() * sizeof(uint32_t));
+  e = hipMemcpyAsync(s.dev, s.host, units * sizeof(DevTensor), hipMemcpyHostToDevice, stream);
   if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync(descriptors)");
   // until the step's launches record it again, the event follows the upload
   e = hipEventRecord(s.done, stream);
@@ -521,7 +540,7 @@ int run_step(int algo, const opt8_tensor* tensors, int32_t n, const opt8_hparams
     if (slot) {
       rc = reuse_slot(ds, *slot, stream);
     } else {
-      rc = acquire_slot(ds, plan.list, stream, slot);
+      rc = acquire_slot(ds, plan, stream, slot);
       if (rc == OPT8_OK) {
         vl->slot_dev = dev;
         vl->slot_index = static_cast<int>(slot - ds.slots);
@@ -538,8 +557,13 @@ int run_step(int algo, const opt8_tensor* tensors, int32_t n, const opt8_hparams
   for (int kind = 0; kind < kKinds; ++kind) {
     if (!plan.count[kind]) continue;
     const int resident = ds.num_cu * ds.occ[sc.state_round != 0][algo][kind];
+    // the block map follows the descriptors in a cached slot; the fixed array of the
+    // entry point without allocation holds descriptors only, and its kernels search
+    const uint32_t* map = nullptr;
+    if (slot && kind == static_cast<int>(Kind::k8bit))
+      map = reinterpret_cast<const uint32_t*>(dev_list + plan.list.size());
     const hipError_t e = launch_step(static_cast<Kind>(kind), algo, dev_list + plan.first[kind],
-                                     plan.count[kind], plan.blocks[kind], sc, stream, ds.num_cu, resident);
+                                     plan.count[kind], plan.blocks[kind], sc, stream, ds.num_cu, resident, map);
     if (e != hipSuccess) {
       // launches queued before this one still read the slot: keep its event
       // and stream current so a later call that reuses or rewrites it waits

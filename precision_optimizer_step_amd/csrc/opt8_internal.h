@@ -104,9 +104,12 @@ hipError_t upload_tables(const uint8_t* host_tables);   // kTableBytesSR, to the
 hipError_t scratch_address(DevTensor** out);
 // The 8-bit kinds take the stochastic-state kernels when sc.state_round is set.
 // resident: workgroups of that kernel that fit on the device at once (CUs x
-// occupancy); the launch size itself is the kernel side's choice.
+// occupancy); the launch size itself is the kernel side's choice.  map: for the
+// 8-bit full blocks, block b -> the entry of dev_list holding it (device
+// memory, total_blocks entries), or NULL to have the kernels search.
 hipError_t launch_step(Kind kind, int algo, const DevTensor* dev_list, int ntensors,
-                       int64_t total_blocks, const StepScalars& sc, hipStream_t stream, int num_cu, int resident);
+                       int64_t total_blocks, const StepScalars& sc, hipStream_t stream, int num_cu, int resident,
+                       const uint32_t* map);
 // Workgroups per CU that the kernel of this kind, algorithm and state rounding can keep resident.
 int occupancy_per_cu(Kind kind, int algo, bool state_sr);
 

@@ -1232,8 +1232,13 @@ __device__ __forceinline__ void stage_tables(uint8_t* lds) {
 template <Kind K, int A, bool SS>
 __global__ void __launch_bounds__(kThreads)
 step_kernel(const DevTensor* __restrict__ list, int ntensors, int64_t total_blocks, StepScalars sc,
-            int range_ok) {
+            int range_ok, const uint32_t* __restrict__ map) {
   constexpr bool kQ8 = (K == Kind::k8bit || K == Kind::k8bitTail);
+  // the block map (block -> entry) replaces the descriptor search in the 8-bit
+  // full-block kernels of AdamW and Lion; the others keep the search, which
+  // measured faster for them (see launch_groups for how they are launched)
+  constexpr bool kMap = K == Kind::k8bit && A != kMomentum;
+  if constexpr (!kMap) map = nullptr;
   constexpr int kLds = kQ8 ? (SS ? kTableBytesSR : kTableBytes) : 16;
   __shared__ __attribute__((aligned(16))) uint8_t lds[kLds];
   if constexpr (kQ8) stage_tables<kLds>(lds);
@@ -1262,16 +1267,24 @@ step_kernel(const DevTensor* __restrict__ list, int ntensors, int64_t total_bloc
   int t = 0;
   DevTensor d;
   DevTensor d_next;
+  uint32_t t_next = 0;   // with a block map: the entry of the wave's next block, read one block ahead
   if constexpr (K == Kind::k8bitTail) {
     d_next = list[b];
   } else {
-    t = find_tensor(list, 0, ntensors - 1, b, lane);
+    t = map ? static_cast<int>(map[b]) : find_tensor(list, 0, ntensors - 1, b, lane);
     d = list[t];
+    if (map && b + nw < total_blocks) t_next = map[b + nw];
   }
   for (; b < total_blocks; b += nw) {
     if constexpr (K == Kind::k8bitTail) {
       d = d_next;
       if (b + nw < total_blocks) d_next = list[b + nw];
+    } else if (map) {
+      if (b != gw && static_cast<int>(t_next) != t) {
+        t = static_cast<int>(t_next);
+        d = list[t];
+      }
+      if (b + nw < total_blocks) t_next = map[b + nw];
     } else if (b >= d.block_begin + static_cast<int64_t>(d.nblocks)) {
       // past the current tensor: the next one starts at or before b, and a later
       // one holds it (b < total_blocks); a wave strides over many blocks, which
@@ -1373,10 +1386,10 @@ int64_t launch_groups(int64_t total_blocks, int num_cu, int resident) {
 
 template <Kind K, int A, bool SS>
 hipError_t launch_kind(const DevTensor* list, int n, int64_t total_blocks, const StepScalars& sc,
-                       hipStream_t stream, int num_cu, int resident, int range_ok) {
+                       hipStream_t stream, int num_cu, int resident, int range_ok, const uint32_t* map) {
   const int64_t grid = launch_groups<K, A>(total_blocks, num_cu, resident);
   hipLaunchKernelGGL((step_kernel<K, A, SS>), dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0, stream,
-                     list, n, total_blocks, sc, range_ok);
+                     list, n, total_blocks, sc, range_ok, map);
   return hipGetLastError();
 }
 
@@ -1392,12 +1405,12 @@ int occupancy_kind() {
 // no 8-bit state and always take SS = false.
 template <Kind K, bool SS>
 hipError_t launch_algo(int algo, const DevTensor* list, int n, int64_t total_blocks, const StepScalars& sc,
-                       hipStream_t stream, int num_cu, int resident, int range_ok) {
+                       hipStream_t stream, int num_cu, int resident, int range_ok, const uint32_t* map) {
   switch (algo) {
-    case kAdamW: return launch_kind<K, kAdamW, SS>(list, n, total_blocks, sc, stream, num_cu, resident, range_ok);
-    case kLion: return launch_kind<K, kLion, SS>(list, n, total_blocks, sc, stream, num_cu, resident, range_ok);
+    case kAdamW: return launch_kind<K, kAdamW, SS>(list, n, total_blocks, sc, stream, num_cu, resident, range_ok, map);
+    case kLion: return launch_kind<K, kLion, SS>(list, n, total_blocks, sc, stream, num_cu, resident, range_ok, map);
     case kMomentum:
-      return launch_kind<K, kMomentum, SS>(list, n, total_blocks, sc, stream, num_cu, resident, range_ok);
+      return launch_kind<K, kMomentum, SS>(list, n, total_blocks, sc, stream, num_cu, resident, range_ok, map);
   }
   return hipErrorInvalidValue;
 }
@@ -1432,7 +1445,8 @@ hipError_t scratch_address(DevTensor** out) {
 }
 
 hipError_t launch_step(Kind kind, int algo, const DevTensor* list, int n, int64_t total_blocks,
-                       const StepScalars& sc, hipStream_t stream, int num_cu, int resident) {
+                       const StepScalars& sc, hipStream_t stream, int num_cu, int resident,
+                       const uint32_t* map) {
   if (n <= 0 || total_blocks <= 0) return hipSuccess;
   // the fast AdamW paths need eps well inside the normal range, a bounded
   // second-moment correction, decay and step size (they then check each
@@ -1442,17 +1456,17 @@ hipError_t launch_step(Kind kind, int algo, const DevTensor* list, int n, int64_
   const bool ss = sc.state_round != 0;
   switch (kind) {
     case Kind::k8bit:
-      return ss ? launch_algo<Kind::k8bit, true>(algo, list, n, total_blocks, sc, stream, num_cu, resident, range_ok)
-                : launch_algo<Kind::k8bit, false>(algo, list, n, total_blocks, sc, stream, num_cu, resident, range_ok);
+      return ss ? launch_algo<Kind::k8bit, true>(algo, list, n, total_blocks, sc, stream, num_cu, resident, range_ok, map)
+                : launch_algo<Kind::k8bit, false>(algo, list, n, total_blocks, sc, stream, num_cu, resident, range_ok, map);
     case Kind::k8bitTail:
       // its kernel reads entry b for block b: one block per entry
       if (total_blocks != n) return hipErrorInvalidValue;
-      return ss ? launch_algo<Kind::k8bitTail, true>(algo, list, n, total_blocks, sc, stream, num_cu, resident, range_ok)
-                : launch_algo<Kind::k8bitTail, false>(algo, list, n, total_blocks, sc, stream, num_cu, resident, range_ok);
+      return ss ? launch_algo<Kind::k8bitTail, true>(algo, list, n, total_blocks, sc, stream, num_cu, resident, range_ok, map)
+                : launch_algo<Kind::k8bitTail, false>(algo, list, n, total_blocks, sc, stream, num_cu, resident, range_ok, map);
     case Kind::kBf16:
-      return launch_algo<Kind::kBf16, false>(algo, list, n, total_blocks, sc, stream, num_cu, resident, range_ok);
+      return launch_algo<Kind::kBf16, false>(algo, list, n, total_blocks, sc, stream, num_cu, resident, range_ok, map);
     case Kind::kFp32:
-      return launch_algo<Kind::kFp32, false>(algo, list, n, total_blocks, sc, stream, num_cu, resident, range_ok);
+      return launch_algo<Kind::kFp32, false>(algo, list, n, total_blocks, sc, stream, num_cu, resident, range_ok, map);
   }
   return hipErrorInvalidValue;
 }

@@ -190,12 +190,14 @@ int main() {
   if (g.launches.size() == 4) {
     const fake::Launch& a = g.launches[0];   // full 8-bit blocks: 2 + 2 + 3
     CHECK(a.kind == 0 && a.n == 3 && a.total_blocks == 7 && a.ok);
+    CHECK(a.has_map);                        // the block map comes with the full 8-bit blocks only
     const fake::Launch& b = g.launches[1];   // bf16 state: 1 + 2 blocks
     CHECK(b.kind == 1 && b.n == 2 && b.total_blocks == 3 && b.ok);
     const fake::Launch& c = g.launches[2];   // fp32 state
     CHECK(c.kind == 2 && c.n == 1 && c.total_blocks == 1 && c.ok);
     const fake::Launch& d = g.launches[3];   // partial last blocks of 5000 and 2047
     CHECK(d.kind == 3 && d.n == 2 && d.total_blocks == 2 && d.ok);
+    CHECK(!b.has_map && !c.has_map && !d.has_map);
     for (const auto& L : g.launches) CHECK(L.num_cu == 256 && L.resident == 256 * 3 && L.algo == 0);
     expect_scalars(a.sc, h1, true);
   }
@@ -349,8 +351,8 @@ int main() {
         CHECK(g.uploads == up + 1);           // one copy into the scratch per call, never cached
         bool in_scratch = !g.launches.empty();
         for (const auto& x : g.launches)
-          in_scratch = in_scratch && x.ok && x.list >= g.scratch_lo && x.list < g.scratch_hi;
-        CHECK(in_scratch);                    // every launch reads the scratch array
+          in_scratch = in_scratch && x.ok && x.list >= g.scratch_lo && x.list < g.scratch_hi && !x.has_map;
+        CHECK(in_scratch);                    // every launch reads the scratch array, and searches (no map)
       }
     }
     CHECK(g.launches.size() == 2 && g.launches[0].n == 4096 && g.launches[1].n == 4096);   // 4096 + 4096 tails

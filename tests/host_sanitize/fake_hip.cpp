@@ -121,7 +121,7 @@ hipError_t upload_tables(const uint8_t* host_tables) {
 }
 
 hipError_t launch_step(Kind kind, int algo, const DevTensor* list, int n, int64_t total_blocks,
-                       const StepScalars& sc, hipStream_t, int num_cu, int resident) {
+                       const StepScalars& sc, hipStream_t, int num_cu, int resident, const uint32_t* map) {
   if (static_cast<int>(kind) == g.fail_launch_kind) return hipErrorInvalidValue;
   fake::Launch L;
   L.list = list;
@@ -145,6 +145,15 @@ hipError_t launch_step(Kind kind, int algo, const DevTensor* list, int n, int64_
     L.ids.push_back(list[i].tensor_id);
   }
   if (b != total_blocks) L.ok = false;
+  // the block map, where given (8-bit full blocks only): block -> the entry holding it
+  L.has_map = map != nullptr;
+  if (map) {
+    if (kind != Kind::k8bit) L.ok = false;
+    int64_t blk = 0;
+    for (int i = 0; i < n; ++i)
+      for (uint32_t k = 0; k < list[i].nblocks; ++k, ++blk)
+        if (map[blk] != static_cast<uint32_t>(i)) L.ok = false;
+  }
   g.launches.push_back(L);
   return hipSuccess;
 }

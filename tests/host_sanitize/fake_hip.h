@@ -15,6 +15,7 @@ struct Launch {
   opt8::StepScalars sc{};
   std::vector<uint32_t> ids;
   bool ok = true;
+  bool has_map = false;
 };
 
 struct State {
