@@ -33,7 +33,7 @@ def kernel_fingerprint() -> str:
     kernel build)."""
     import hashlib
     h = hashlib.sha256()
-    for name in ("opt8_kernels.hip", "opt8_internal.h", "opt8_exact.h", "opt8_codes.h", "opt8_tables.cpp"):
+    for name in ("opt8_kernels.hip", "opt8_internal.h", "opt8_exact.h", "opt8_codes.h", "opt8_launch.h", "opt8_tables.cpp"):
         with open(os.path.join(HERE, "csrc", name), "rb") as f:
             h.update(f.read())
     h.update(" ".join(FLAGS).encode())

@@ -26,11 +26,12 @@
 #include "opt8_codes.h"
 #include "opt8_exact.h"
 #include "opt8_internal.h"
+#include "opt8_launch.h"
 
 namespace opt8 {
 namespace {
 
-constexpr int kWaves = 4;                   // waves per workgroup
+constexpr int kWaves = kWavesPerGroup;      // waves per workgroup
 constexpr int kThreads = 64 * kWaves;
 constexpr int kGroups = kBlock / (64 * 8);  // 8-element groups per lane per block (4)
 constexpr float kMinNormal = 1.17549435e-38f;  // 2^-126
@@ -1348,40 +1349,6 @@ step_kernel(const DevTensor* __restrict__ list, int ntensors, int64_t total_bloc
       }
     }
   }
-}
-
-// Launch size.  A grid of only the workgroups that fit at once would give each
-// wave a fixed share of the blocks; a SIMD issues from its oldest wave first,
-// so its waves finish their shares far apart (on the 6.7B list the first
-// third of the waves is done at 62% of the kernel's time, the second at 80%)
-// and the SIMD runs the rest with one or two waves instead of three.  The
-// grid is therefore several times the resident count: the dispatcher starts a
-// new workgroup on a CU as soon as one finishes, and every SIMD keeps its
-// full set of waves until the last few hundred microseconds.  Each new
-// workgroup pays for staging the tables and finding its first tensor, so the
-// count per CU is the measured best of a sweep from 6 to 768 per CU for each
-// family on the 6.7B, 2.7B and 1.5B lists (two-state 8-bit 96, Lion 12,
-// momentum 384, bf16 and fp32 state 384; the last partial blocks, one short
-// block per tensor, keep the resident grid), and a wave gets at least four
-// blocks (one in the fp32-state kernels, whose tensors are single blocks).
-template <Kind K, int A>
-constexpr int groups_per_cu() {
-  if constexpr (K == Kind::k8bit) return A == kLion ? 12 : (A == kMomentum ? 384 : 96);
-  else if constexpr (K == Kind::kBf16 || K == Kind::kFp32) return 384;
-  else return 0;
-}
-
-template <Kind K, int A>
-int64_t launch_groups(int64_t total_blocks, int num_cu, int resident) {
-  const int64_t one_block_per_wave = (total_blocks + kWaves - 1) / kWaves;
-  int64_t grid = std::min<int64_t>(one_block_per_wave, resident);
-  if (groups_per_cu<K, A>() > 0) {
-    const int64_t min_blocks = K == Kind::kFp32 ? 1 : 4;
-    const int64_t by_work = (total_blocks + kWaves * min_blocks - 1) / (kWaves * min_blocks);
-    grid = std::max(grid, std::min<int64_t>(static_cast<int64_t>(num_cu) * groups_per_cu<K, A>(), by_work));
-  }
-  if (grid >= 64) grid &= ~int64_t{31};   // a multiple of 32 keeps the XCD-aware wave numbering
-  return std::max<int64_t>(grid, 1);
 }
 
 template <Kind K, int A, bool SS>

@@ -2,6 +2,7 @@
 // its tables, every validation error, capture refusal, launch planning, the
 // scalar prologue and the descriptor cache.  Built with AddressSanitizer and
 // UBSan by tests/test_host_sanitizers.py; prints "all host checks passed".
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <cstdio>
@@ -12,6 +13,7 @@
 #include <vector>
 
 #include "fake_hip.h"
+#include "opt8_launch.h"
 #include "opt8.h"
 
 using fake::g;
@@ -409,6 +411,34 @@ int main() {
     CHECK(g.launches.size() == 1 && g.launches[0].ok);
   }
   CHECK(g.reuse_violations == 0);   // no staging buffer was rewritten or freed under its copy
+
+  // launch sizes: the measured counts per CU on the big lists, and for every list size a grid of
+  // at least one workgroup, no more workgroups than blocks / 4, a multiple of 32 from 64 on, and
+  // at least the resident count while there are blocks for it
+  {
+    using opt8::Kind;
+    CHECK((opt8::launch_groups<Kind::k8bit, opt8::kAdamW>(3251174, 256, 768) == 96 * 256));
+    CHECK((opt8::launch_groups<Kind::k8bit, opt8::kLion>(3251174, 256, 512) == 12 * 256));
+    CHECK((opt8::launch_groups<Kind::k8bit, opt8::kMomentum>(3251174, 256, 512) == 384 * 256));
+    CHECK((opt8::launch_groups<Kind::kBf16, opt8::kAdamW>(1294710, 256, 1280) == (1294710 + 15) / 16 / 32 * 32));
+    CHECK((opt8::launch_groups<Kind::kFp32, opt8::kAdamW>(30000, 256, 1280) == 7500 / 32 * 32));
+    CHECK((opt8::launch_groups<Kind::k8bitTail, opt8::kAdamW>(30000, 256, 768) == 768));
+    bool ok = true;
+    for (int64_t blocks = 1; blocks < 4000000; blocks = blocks * 3 / 2 + 1) {
+      const int64_t grids[5] = {opt8::launch_groups<Kind::k8bit, opt8::kAdamW>(blocks, 256, 768),
+                                opt8::launch_groups<Kind::k8bit, opt8::kLion>(blocks, 256, 512),
+                                opt8::launch_groups<Kind::kBf16, opt8::kAdamW>(blocks, 256, 1280),
+                                opt8::launch_groups<Kind::kFp32, opt8::kMomentum>(blocks, 256, 1280),
+                                opt8::launch_groups<Kind::k8bitTail, opt8::kAdamW>(blocks, 256, 768)};
+      const int64_t resident[5] = {768, 512, 1280, 1280, 768};
+      for (int k = 0; k < 5; ++k) {
+        const int64_t gsz = grids[k];
+        ok = ok && gsz >= 1 && gsz <= (blocks + 3) / 4 && (gsz < 64 || gsz % 32 == 0);
+        ok = ok && gsz >= std::min<int64_t>(resident[k], (blocks + 3) / 4) / 32 * 32;
+      }
+    }
+    CHECK(ok);
+  }
 
   if (failures) {
     std::printf("%d host checks failed\n", failures);
