@@ -412,15 +412,17 @@ int main() {
   }
   CHECK(g.reuse_violations == 0);   // no staging buffer was rewritten or freed under its copy
 
-  // launch sizes: the measured counts per CU on the big lists, and for every list size a grid of
-  // at least one workgroup, no more workgroups than blocks / 4, a multiple of 32 from 64 on, and
+  // launch sizes: the measured counts per CU on the big lists, two blocks per wave on a list of
+  // small tensors, and for every list size a grid of at least one workgroup, no more workgroups
+  // than blocks / 4, a multiple of 32 from 64 on, and
   // at least the resident count while there are blocks for it
   {
     using opt8::Kind;
-    CHECK((opt8::launch_groups<Kind::k8bit, opt8::kAdamW>(3251174, 256, 768) == 96 * 256));
-    CHECK((opt8::launch_groups<Kind::k8bit, opt8::kLion>(3251174, 256, 512) == 12 * 256));
+    CHECK((opt8::launch_groups<Kind::k8bit, opt8::kAdamW>(3251174, 256, 768) == 192 * 256));
+    CHECK((opt8::launch_groups<Kind::k8bit, opt8::kLion>(3251174, 256, 512) == 96 * 256));
     CHECK((opt8::launch_groups<Kind::k8bit, opt8::kMomentum>(3251174, 256, 512) == 384 * 256));
-    CHECK((opt8::launch_groups<Kind::kBf16, opt8::kAdamW>(1294710, 256, 1280) == (1294710 + 15) / 16 / 32 * 32));
+    CHECK((opt8::launch_groups<Kind::kBf16, opt8::kAdamW>(1294710, 256, 1280) == 384 * 256));
+    CHECK((opt8::launch_groups<Kind::k8bit, opt8::kAdamW>(60000, 256, 768) == 60000 / 8 / 32 * 32));
     CHECK((opt8::launch_groups<Kind::kFp32, opt8::kAdamW>(30000, 256, 1280) == 7500 / 32 * 32));
     CHECK((opt8::launch_groups<Kind::k8bitTail, opt8::kAdamW>(30000, 256, 768) == 768));
     bool ok = true;
