@@ -470,8 +470,9 @@ __device__ __forceinline__ bool block_8bit_fast(const DevTensor& d, int64_t blk,
     return false;
 
   // pass 2, group by group: parameter update, its rounding and store, then the
-  // requantised moments (a block with absmax below 2^-126 stores the zero code;
-  // its codes are computed from n = 0 and then replaced)
+  // requantised moments (a block with absmax below 2^-126 stores the zero code:
+  // its multiplier is 0, so with finite moments every n is +-0, whose code under
+  // either rounding rule is the zero code, 127 signed and 0 unsigned)
   const float* mid_s = reinterpret_cast<const float*>(lds + kOffMidS);
   const float* mid_u = reinterpret_cast<const float*>(lds + kOffMidU);
   const bool live_m = mxm >= kMinNormal;
@@ -513,8 +514,8 @@ __device__ __forceinline__ bool block_8bit_fast(const DevTensor& d, int64_t blk,
     for (int j = 0; j < 8; ++j) {
       uint32_t qm, qv;
       if constexpr (kSS) {
-        qm = code_sr<true>(M2[r * 8 + j] * inv_m, lds, r16_of(rm, j));
-        qv = code_sr<false>(V2[r * 8 + j] * inv_v, lds, r16_of(rv, j));
+        qm = code_sr<true, true>(M2[r * 8 + j] * inv_m, lds, r16_of(rm, j));
+        qv = code_sr<false, true>(V2[r * 8 + j] * inv_v, lds, r16_of(rv, j));
       } else {
         qm = code_s(M2[r * 8 + j] * inv_m, lds, mid_s);
         qv = code_u(V2[r * 8 + j] * inv_v, lds, mid_u);
@@ -522,8 +523,6 @@ __device__ __forceinline__ bool block_8bit_fast(const DevTensor& d, int64_t blk,
       cm[j >> 2] |= qm << (8 * (j & 3));
       cv[j >> 2] |= qv << (8 * (j & 3));
     }
-    if (!live_m) cm[0] = cm[1] = 0x7F7F7F7Fu;
-    if (!live_v) cv[0] = cv[1] = 0u;
     if (!kPartial || off + 8 <= valid) {
       st_stream8(mp + off, make_uint2(cm[0], cm[1]));
       st_stream8(vp + off, make_uint2(cv[0], cv[1]));
@@ -1010,8 +1009,9 @@ __device__ __forceinline__ bool block_1s_8bit_fast(const DevTensor& d, int64_t b
         pp[off + j] = static_cast<uint16_t>(word_of(P[r], j >> 1) >> (16 * (j & 1)));
     }
   }
-  const bool live = mxm >= kMinNormal;
-  const float inv = live ? 1.0f / mxm : 0.0f;
+  // absmax below 2^-126: the multiplier is 0, every n is +-0 (the moments are
+  // finite here) and takes the zero code, 127, under either rounding rule
+  const float inv = mxm >= kMinNormal ? 1.0f / mxm : 0.0f;
 #pragma unroll
   for (int r = 0; r < kGroups; ++r) {
     if (kPartial && r * 512 >= valid) continue;   // no lane has an element left
@@ -1025,7 +1025,6 @@ __device__ __forceinline__ bool block_1s_8bit_fast(const DevTensor& d, int64_t b
 #pragma unroll
       for (int j = 0; j < 8; ++j) cm[j >> 2] |= code_s(M2[r * 8 + j] * inv, lds, mid_s) << (8 * (j & 3));
     }
-    if (!live) cm[0] = cm[1] = 0x7F7F7F7Fu;
     const int off = r * 512 + lane * 8;
     if (!kPartial || off + 8 <= valid) {
       st_stream8(mp + off, make_uint2(cm[0], cm[1]));

@@ -183,6 +183,24 @@ def test_midpoint_ties_take_the_lower_code():
             assert codes[0] == k and codes[1] == 255
 
 
+def test_a_zero_normalised_value_takes_the_zero_code():
+    """n = +0 and n = -0 code to the zero code under the nearest-entry search and under
+    stochastic rounding between neighbours (any random word): a block whose absmax is
+    below 2^-126 (normaliser 0, so every n is +-0) stores the zero code either by that
+    rule or by the explicit zero-code case, with the same bytes."""
+    from oracle import state_sr
+    zeros = np.array([0.0, -0.0], dtype=np.float32)
+    assert np.all(np.searchsorted(MS, zeros, side="left") == codebook.SIGNED_ZERO_CODE)
+    assert np.all(np.searchsorted(MU, zeros[:1], side="left") == codebook.UNSIGNED_ZERO_CODE)
+    r16 = np.arange(0, 65536, 257, dtype=np.uint32)
+    for table, zero, n in ((state_sr.signed_table(), codebook.SIGNED_ZERO_CODE, zeros),
+                           (state_sr.unsigned_table(), codebook.UNSIGNED_ZERO_CODE, zeros[:1])):
+        w = state_sr.gap_weights(table)
+        for x in n:
+            got = state_sr.sr_codes(np.full(r16.size, x, dtype=np.float32), table, w, r16)
+            assert np.all(got == zero)
+
+
 def test_error_within_half_local_gap():
     """|C[q] * A - x| <= half the gap of the bracketing entries * A (+ fp32 slack)."""
     rng = np.random.default_rng(3)
