@@ -184,7 +184,17 @@ int32_t opt8_default_mode(int64_t numel);
  * synchronisation.  A stream that is being captured into a HIP graph is
  * refused with OPT8_E_CAPTURE before anything is queued: a step may upload
  * its descriptor list into a cache slot that later calls reuse, which a
- * graph replay would not follow.  Returns OPT8_OK or a negative opt8_status. */
+ * graph replay would not follow.
+ * Caching: the library keeps, per calling thread, the last 64 lists that
+ * passed validation (with their launch plans), and on each device up to 64
+ * descriptor slots (device copies of a list's descriptors and block map).  A
+ * list passed again byte for byte -- a training loop passes one per parameter
+ * group, every step -- is neither validated nor uploaded again.  Beyond 64
+ * lists, or beyond a byte budget per cache (256 MiB; the environment variable
+ * OPT8_CACHE_MB, read at the first step, replaces it), the least recently used
+ * lists are dropped; a call that rewrites or frees a slot first waits on the
+ * host for the launches that last read it.  Lion and momentum share the same
+ * caches.  Returns OPT8_OK or a negative opt8_status. */
 int opt8_adamw_step(const opt8_tensor* tensors, int32_t n, const opt8_hparams* hp,
                     void* hip_stream);
 

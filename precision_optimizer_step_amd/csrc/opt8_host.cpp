@@ -4,6 +4,7 @@
 #include <cstdarg>
 #include <cmath>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <mutex>
 #include <new>
@@ -11,6 +12,7 @@
 #include <vector>
 
 #include "../../include/opt8.h"
+#include "opt8_host_limits.h"
 #include "opt8_internal.h"
 
 namespace opt8 {
@@ -263,14 +265,15 @@ void build_plan(const opt8_tensor* t, int32_t n, bool two_state, Plan& p) {
 }
 
 // Validation and the launch plan are pure functions of the descriptor values,
-// and a training loop passes the same lists every step (often two: parameters
-// with and without weight decay): each thread keeps copies of the last four
-// lists that passed, with their plans, and a list identical to one of them
-// (byte for byte, same rule) is neither checked nor planned again.  A hit costs
-// one memcmp instead of sorting 6n ranges and building 2n descriptors.
-constexpr int kValidated = 4;
+// and a training loop passes the same lists every step (two for parameters
+// with and without weight decay, one per group where every layer has its own
+// learning rate): each thread keeps copies of the lists that passed, with
+// their plans, and a list identical to one of them (byte for byte, same rule)
+// is neither checked nor planned again.  A hit costs one memcmp instead of
+// sorting 6n ranges and building 2n descriptors and the block map.
 struct ValidatedList {
   std::vector<opt8_tensor> list;
+  uint64_t hash = 0;   // of the list's bytes, compared before them
   bool two_state = false;
   bool valid = false;
   uint64_t stamp = 0;
@@ -282,37 +285,91 @@ struct ValidatedList {
   uint64_t slot_gen = 0;
 };
 struct ValidatedCache {
-  ValidatedList entry[kValidated];
+  std::vector<ValidatedList> entry;   // grows to kListCache entries (capacity reserved: addresses stay)
   uint64_t clock = 0;
 };
 thread_local ValidatedCache t_validated;
 
+// FNV-1a over the list's 8-byte words (an opt8_tensor is a whole number of them).
+uint64_t list_hash(const opt8_tensor* t, int32_t n) {
+  static_assert(sizeof(opt8_tensor) % sizeof(uint64_t) == 0, "descriptor size");
+  const size_t words = sizeof(opt8_tensor) / sizeof(uint64_t) * static_cast<size_t>(n);
+  const unsigned char* p = reinterpret_cast<const unsigned char*>(t);
+  uint64_t h = 0xCBF29CE484222325ull;
+  for (size_t i = 0; i < words; ++i) {
+    uint64_t w;
+    std::memcpy(&w, p + i * sizeof w, sizeof w);
+    h = (h ^ w) * 0x100000001B3ull;
+  }
+  return h;
+}
+
+// The byte budget of each cache (kCacheBytesDefault, or OPT8_CACHE_MB).
+size_t cache_budget() {
+  static const size_t bytes = [] {
+    const char* e = std::getenv("OPT8_CACHE_MB");
+    const long long mb = e ? std::atoll(e) : 0;
+    return mb > 0 ? static_cast<size_t>(mb) << 20 : kCacheBytesDefault;
+  }();
+  return bytes;
+}
+
+size_t entry_bytes(const ValidatedList& e) {
+  return e.list.capacity() * sizeof(opt8_tensor) + e.plan.list.capacity() * sizeof(DevTensor) +
+         e.plan.map.capacity() * sizeof(uint32_t);
+}
+
+void drop_entry(ValidatedList& e) {
+  e.valid = false;
+  std::vector<opt8_tensor>().swap(e.list);
+  e.plan = Plan{};
+  e.slot_dev = -1;
+  e.slot_index = -1;
+}
+
 int validate_tensors_cached(const opt8_tensor* t, int32_t n, bool two_state, ValidatedList*& out) {
   ValidatedCache& c = t_validated;
+  if (c.entry.capacity() < static_cast<size_t>(kListCache)) c.entry.reserve(kListCache);
   ++c.clock;
   const size_t bytes = sizeof(opt8_tensor) * static_cast<size_t>(n);
-  ValidatedList* victim = &c.entry[0];
+  const uint64_t hash = list_hash(t, n);
+  ValidatedList* victim = nullptr;
   for (ValidatedList& e : c.entry) {
-    if (e.valid && e.two_state == two_state && e.list.size() == static_cast<size_t>(n) &&
+    if (e.valid && e.hash == hash && e.two_state == two_state && e.list.size() == static_cast<size_t>(n) &&
         std::memcmp(e.list.data(), t, bytes) == 0) {
       e.stamp = c.clock;
       out = &e;
       return OPT8_OK;
     }
-    if (!e.valid) victim = &e;
-    else if (victim->valid && e.stamp < victim->stamp) victim = &e;
+    if (!victim || (victim->valid && (!e.valid || e.stamp < victim->stamp))) victim = &e;
   }
   const int rc = validate_tensors(t, n, two_state);
   if (rc != OPT8_OK) return rc;
-  victim->valid = false;
+  // a new entry while there is room, else an empty or the least recently used one
+  if (c.entry.size() < static_cast<size_t>(kListCache) && (!victim || victim->valid)) {
+    c.entry.emplace_back();
+    victim = &c.entry.back();
+  }
+  drop_entry(*victim);
+  victim->hash = hash;
   victim->list.assign(t, t + n);
   build_plan(t, n, two_state, victim->plan);
   victim->two_state = two_state;
-  victim->slot_dev = -1;
-  victim->slot_index = -1;
   victim->slot_gen = 0;
   victim->valid = true;
   victim->stamp = c.clock;
+  // over the byte budget: drop the least recently used other lists
+  size_t total = 0;
+  for (const ValidatedList& e : c.entry)
+    if (e.valid) total += entry_bytes(e);
+  while (total > cache_budget()) {
+    ValidatedList* lru = nullptr;
+    for (ValidatedList& e : c.entry)
+      if (e.valid && &e != victim && (!lru || e.stamp < lru->stamp)) lru = &e;
+    if (!lru) break;
+    total -= entry_bytes(*lru);
+    drop_entry(*lru);
+  }
   out = victim;
   return OPT8_OK;
 }
@@ -320,7 +377,6 @@ int validate_tensors_cached(const opt8_tensor* t, int32_t n, bool two_state, Val
 // ----------------------------------------------------------------------------- device state
 // Descriptor lists live in device memory, one slot per distinct list; a list
 // passed again (the usual training loop) is launched without a new upload.
-constexpr int kSlots = 4;
 constexpr int kMaxDevices = 64;
 constexpr int kAlgos = 3;
 
@@ -341,7 +397,11 @@ struct DeviceState {
   int num_cu = 0;
   DevTensor* scratch = nullptr;      // device address of the no-allocation descriptor array
   int occ[2][kAlgos][kKinds] = {};   // [state_round][algo][kind]
-  Slot slots[kSlots];
+  // grows to kSlotCache slots (capacity reserved at init, so addresses stay);
+  // never destroyed, like the device buffers it points to, which live until
+  // the process ends (freeing them from a static destructor could run after
+  // the HIP runtime has shut down)
+  std::vector<Slot>& slots = *new std::vector<Slot>();
   uint64_t clock = 0;
   PowCache pow;
 };
@@ -378,6 +438,21 @@ int ensure_capacity(Slot& s, size_t count) {
   return OPT8_OK;
 }
 
+// Frees a slot's buffers once the launches that read it and its last upload
+// have finished.
+int release_slot(Slot& s) {
+  const hipError_t e = hipEventSynchronize(s.done);
+  if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize");
+  if (s.dev) (void)hipFree(s.dev);
+  if (s.host) (void)hipHostFree(s.host);
+  s.dev = nullptr;
+  s.host = nullptr;
+  s.cap = 0;
+  s.used = false;
+  std::vector<DevTensor>().swap(s.key);
+  return OPT8_OK;
+}
+
 bool same_list(const std::vector<DevTensor>& a, const std::vector<DevTensor>& b) {
   return a.size() == b.size() && std::memcmp(a.data(), b.data(), a.size() * sizeof(DevTensor)) == 0;
 }
@@ -404,10 +479,19 @@ int acquire_slot(DeviceState& ds, const Plan& plan, hipStream_t stream, Slot*& o
     }
   }
   ++ds.clock;
-  Slot* victim = &ds.slots[0];
+  // an unused slot, a new one while there is room, else the least recently used
+  Slot* victim = nullptr;
   for (Slot& s : ds.slots) {
     if (!s.used) { victim = &s; break; }
-    if (s.stamp < victim->stamp) victim = &s;
+    if (!victim || s.stamp < victim->stamp) victim = &s;
+  }
+  if ((!victim || victim->used) && ds.slots.size() < static_cast<size_t>(kSlotCache)) {
+    hipEvent_t ev = nullptr;
+    const hipError_t ce = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
+    if (ce != hipSuccess) return hip_fail(ce, "hipEventCreateWithFlags");
+    ds.slots.emplace_back();
+    victim = &ds.slots.back();
+    victim->done = ev;
   }
   Slot& s = *victim;
   // the last upload from the staging buffer and every launch that read the
@@ -420,6 +504,18 @@ int acquire_slot(DeviceState& ds, const Plan& plan, hipStream_t stream, Slot*& o
   const size_t units = list.size() + map_units(plan);
   int rc = ensure_capacity(s, units);
   if (rc != OPT8_OK) return rc;
+  // over the byte budget: free the least recently used other slots
+  size_t total = 0;
+  for (const Slot& o : ds.slots) total += o.cap * sizeof(DevTensor);
+  while (total > cache_budget()) {
+    Slot* lru = nullptr;
+    for (Slot& o : ds.slots)
+      if (&o != &s && o.cap && (!lru || o.stamp < lru->stamp)) lru = &o;
+    if (!lru) break;
+    total -= lru->cap * sizeof(DevTensor);
+    rc = release_slot(*lru);
+    if (rc != OPT8_OK) return rc;
+  }
   s.key = list;   // may throw: nothing is queued yet
   std::memcpy(s.host, list.data(), list.size() * sizeof(DevTensor));
   if (!plan.map.empty())
@@ -464,12 +560,7 @@ extern "C" int opt8_init_codebooks(float* signed_out, float* unsigned_out) {
     for (int sr = 0; sr < 2; ++sr)
       for (int a = 0; a < kAlgos; ++a)
         for (int k = 0; k < kKinds; ++k) ds.occ[sr][a][k] = occupancy_per_cu(static_cast<Kind>(k), a, sr != 0);
-    for (Slot& s : ds.slots) {
-      if (!s.done) {
-        e = hipEventCreateWithFlags(&s.done, hipEventDisableTiming);
-        if (e != hipSuccess) return hip_fail(e, "hipEventCreateWithFlags");
-      }
-    }
+    ds.slots.reserve(kSlotCache);
     e = hipDeviceSynchronize();
     if (e != hipSuccess) return hip_fail(e, "hipDeviceSynchronize");
     ds.init = true;
@@ -533,7 +624,7 @@ int run_step(int algo, const opt8_tensor* tensors, int32_t n, const opt8_hparams
     dev_list = ds.scratch;
   } else {
     // the slot this list was uploaded to, if nothing has rewritten it since
-    if (vl->slot_dev == dev && vl->slot_index >= 0) {
+    if (vl->slot_dev == dev && vl->slot_index >= 0 && vl->slot_index < static_cast<int>(ds.slots.size())) {
       Slot& s = ds.slots[vl->slot_index];
       if (s.used && s.gen == vl->slot_gen) slot = &s;
     }
@@ -543,7 +634,7 @@ int run_step(int algo, const opt8_tensor* tensors, int32_t n, const opt8_hparams
       rc = acquire_slot(ds, plan, stream, slot);
       if (rc == OPT8_OK) {
         vl->slot_dev = dev;
-        vl->slot_index = static_cast<int>(slot - ds.slots);
+        vl->slot_index = static_cast<int>(slot - ds.slots.data());
         vl->slot_gen = slot->gen;
       }
     }

@@ -13,6 +13,7 @@
 #include <vector>
 
 #include "fake_hip.h"
+#include "opt8_host_limits.h"
 #include "opt8_launch.h"
 #include "opt8.h"
 
@@ -104,6 +105,9 @@ static int step(const std::vector<opt8_tensor>& ts, const opt8_hparams& h, void*
 }
 
 int main() {
+  // the caches' byte budget for this run (read at the first step): 16 MiB, which the
+  // lists below reach only in the budget check (the count checks stay within it)
+  setenv("OPT8_CACHE_MB", "16", 1);
   // ---------------------------------------------------------------- tables
   g.have_device = false;
   float cs[256], cu[256];
@@ -259,14 +263,14 @@ int main() {
   // ---------------------------------------------------------------- descriptor cache
   {
     std::vector<std::vector<opt8_tensor>> lists;
-    for (int l = 0; l < 6; ++l)
+    for (int l = 0; l < opt8::kSlotCache + 2; ++l)
       lists.push_back({tensor(20 + 2 * l, 4096 + 64 * l, OPT8_STATE_8BIT, 0),
                        tensor(21 + 2 * l, 9000, OPT8_STATE_BF16_SR, 1)});
     for (int round = 0; round < 3; ++round)
       for (auto& L : lists) {
         const long up = g.uploads;
         CHECK(step(L, h1) == OPT8_OK);
-        CHECK(g.uploads == up + 1);           // six lists round-robin through four slots: always a miss
+        CHECK(g.uploads == up + 1);           // more lists than slots, round-robin: always a miss
         const long up2 = g.uploads;
         CHECK(step(L, h1) == OPT8_OK);
         CHECK(g.uploads == up2);              // the same list again: reused, no upload
@@ -274,9 +278,9 @@ int main() {
     CHECK(g.event_syncs > 0);                 // evictions waited for the last reader
     const long waits = g.stream_waits;
     void* other = reinterpret_cast<void*>(uintptr_t(0x1000));
-    CHECK(step(lists[5], h1, other) == OPT8_OK);
+    CHECK(step(lists.back(), h1, other) == OPT8_OK);
     CHECK(g.stream_waits == waits + 1);       // moved to another stream: ordered after the last launch
-    CHECK(step(lists[5], h1, other) == OPT8_OK);
+    CHECK(step(lists.back(), h1, other) == OPT8_OK);
     CHECK(g.stream_waits == waits + 1);
 
     // a list this thread has validated and planned, while another thread
@@ -288,10 +292,10 @@ int main() {
       long up = g.uploads;
       CHECK(step(A, h1) == OPT8_OK);
       CHECK(g.uploads == up);
-      int rcs[4] = {-1, -1, -1, -1};
+      std::vector<int> rcs(opt8::kSlotCache, -1);
       std::thread writer([&] {
-        for (int l = 0; l < 4; ++l)
-          rcs[l] = step({tensor(70 + l, 8192, OPT8_STATE_8BIT, 0)}, h1);
+        for (int l = 0; l < opt8::kSlotCache; ++l)
+          rcs[l] = step({tensor(6000 + l, 8192, OPT8_STATE_8BIT, 0)}, h1);
       });
       writer.join();
       for (int rc : rcs) CHECK(rc == OPT8_OK);
@@ -404,11 +408,56 @@ int main() {
     g.fail_launch_kind = -1;
     CHECK(g.uploads == up + 1);
     CHECK(std::strstr(opt8_last_error(), "already queued: nothing") != nullptr);
-    for (int l = 0; l < 5; ++l)   // five new lists: every slot rewritten
-      CHECK(step({tensor(1310 + l, 8192, OPT8_STATE_8BIT, 0)}, h1) == OPT8_OK);
+    for (int l = 0; l <= opt8::kSlotCache; ++l)   // more new lists than slots: every slot rewritten
+      CHECK(step({tensor(6100 + l, 8192, OPT8_STATE_8BIT, 0)}, h1) == OPT8_OK);
     g.launches.clear();
     CHECK(step(F, h1) == OPT8_OK);
     CHECK(g.launches.size() == 1 && g.launches[0].ok);
+  }
+
+  // one list per parameter group, more groups than a cache of four would keep: once each has
+  // been seen, every list stays validated and uploaded and no call waits for an earlier step
+  {
+    std::vector<std::vector<opt8_tensor>> groups;
+    for (int l = 0; l < 40; ++l) groups.push_back({tensor(6200 + l, 4096, OPT8_STATE_8BIT, 0)});
+    for (auto& L : groups) CHECK(step(L, h1) == OPT8_OK);
+    const long up = g.uploads, syncs = g.event_syncs;
+    for (int round = 0; round < 2; ++round)
+      for (auto& L : groups) CHECK(step(L, h1) == OPT8_OK);
+    CHECK(g.uploads == up && g.event_syncs == syncs);
+  }
+
+  // the byte budget (16 MiB in this run) bounds both caches whatever their counts: lists with
+  // 4 MiB block maps stay a few at a time, the oldest is dropped, its slot freed only after
+  // the launches that read it (the check on reuse_violations below), and uploaded again
+  {
+    auto huge_tensor = [](int j) {   // 2^31 elements (2^20 blocks), its buffers 8 GiB apart
+      opt8_tensor t;
+      std::memset(&t, 0, sizeof t);
+      const uintptr_t b = (uintptr_t(1) << 44) + (uintptr_t(j) << 36);
+      t.param = reinterpret_cast<uint16_t*>(b);
+      t.grad = reinterpret_cast<const uint16_t*>(b + (uintptr_t(1) << 33));
+      t.m = reinterpret_cast<void*>(b + (uintptr_t(2) << 33));
+      t.v = reinterpret_cast<void*>(b + (uintptr_t(3) << 33));
+      t.absmax_m = reinterpret_cast<float*>(b + (uintptr_t(4) << 33));
+      t.absmax_v = reinterpret_cast<float*>(b + (uintptr_t(5) << 33));
+      t.numel = int64_t(1) << 31;
+      t.mode = OPT8_STATE_8BIT;
+      return t;
+    };
+    std::vector<std::vector<opt8_tensor>> big;
+    for (int l = 0; l < 6; ++l) big.push_back({huge_tensor(l)});
+    const long frees = g.frees;
+    for (auto& L : big) CHECK(step(L, h1) == OPT8_OK);
+    CHECK(g.frees > frees);                   // slots were freed to stay within the budget
+    const long up = g.uploads;
+    CHECK(step(big[5], h1) == OPT8_OK);       // the newest stays
+    CHECK(g.uploads == up);
+    CHECK(step(big[0], h1) == OPT8_OK);       // the oldest was dropped: uploaded again
+    CHECK(g.uploads == up + 1);
+    g.launches.clear();
+    CHECK(step(big[0], h1) == OPT8_OK);
+    CHECK(g.uploads == up + 1 && g.launches.size() == 1 && g.launches[0].ok);
   }
   CHECK(g.reuse_violations == 0);   // no staging buffer was rewritten or freed under its copy
 
