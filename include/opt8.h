@@ -185,11 +185,11 @@ int32_t opt8_default_mode(int64_t numel);
  * refused with OPT8_E_CAPTURE before anything is queued: a step may upload
  * its descriptor list into a cache slot that later calls reuse, which a
  * graph replay would not follow.
- * Caching: the library keeps, per calling thread, the last 64 lists that
- * passed validation (with their launch plans), and on each device up to 64
+ * Caching: the library keeps, per calling thread, the last 1024 lists that
+ * passed validation (with their launch plans), and on each device up to 1024
  * descriptor slots (device copies of a list's descriptors and block map).  A
  * list passed again byte for byte -- a training loop passes one per parameter
- * group, every step -- is neither validated nor uploaded again.  Beyond 64
+ * group, every step -- is neither validated nor uploaded again.  Beyond 1024
  * lists, or beyond a byte budget per cache (256 MiB; the environment variable
  * OPT8_CACHE_MB, read at the first step, replaces it), the least recently used
  * lists are dropped; a call that rewrites or frees a slot first waits on the
