@@ -1,11 +1,15 @@
 """Streams and the per-device descriptor cache.
 
-The library keeps up to four descriptor lists on each device and reuses one
-when the same list is passed again; a list moved to another stream waits for
-the last launch that read it.  These tests run steps on side streams and
-cycle more lists than the cache holds, and check every result against the
-oracle.
+The library keeps up to kSlotCache descriptor lists on each device (and as
+many validated lists per thread) and reuses one when the same list is passed
+again; a list moved to another stream waits for the last launch that read it.
+These tests run steps on side streams and push lists out of the cache (with
+enough one-block filler lists stepped in between), and check every result
+against the oracle.
 """
+
+import os
+import re
 
 import numpy as np
 import pytest
@@ -43,6 +47,33 @@ def _hp(step):
     return oracle.Hparams(lr=1e-3, weight_decay=0.01, step=step, seed=77)
 
 
+def _slot_cache():
+    """The cache size the library is built with (opt8_host_limits.h)."""
+    path = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                        "precision_optimizer_step_amd", "csrc", "opt8_host_limits.h")
+    return int(re.search(r"kSlotCache = (\d+);", open(path).read()).group(1))
+
+
+def _fillers(count, first_id):
+    """`count` one-tensor lists of one 2,048-element block each, carved from shared buffers:
+    stepped only to push other lists out of the cache, never checked."""
+    dev = torch.device("cuda:0")
+    n = 2048
+    bufs = (torch.zeros(count * n, dtype=torch.bfloat16, device=dev),
+            torch.zeros(count * n, dtype=torch.bfloat16, device=dev),
+            torch.full((count * n,), 127, dtype=torch.uint8, device=dev),
+            torch.zeros(count * n, dtype=torch.uint8, device=dev),
+            torch.zeros(count, dtype=torch.float32, device=dev),
+            torch.zeros(count, dtype=torch.float32, device=dev))
+    P, G, M, V, AM, AV = bufs
+    lists = [opt8.tensor_array([opt8.make_tensor(P.data_ptr() + 2 * n * i, G.data_ptr() + 2 * n * i,
+                                                 M.data_ptr() + n * i, V.data_ptr() + n * i,
+                                                 AM.data_ptr() + 4 * i, AV.data_ptr() + 4 * i,
+                                                 tensor_id=first_id + i, mode=M8, numel=n)])
+             for i in range(count)]
+    return lists, bufs
+
+
 def _launch(sets, hp, stream):
     descs = [s.desc() for s in sets]
     opt8.opt8_adamw_step(descs, opt8.make_hparams(hp.lr, hp.beta1, hp.beta2, hp.eps, hp.weight_decay,
@@ -78,32 +109,40 @@ def test_side_streams_and_a_list_moving_between_streams():
 
 
 def test_more_lists_than_cached_slots():
-    """Six lists (the cache holds four) stepped round-robin for three rounds, so every list is
-    evicted and uploaded again; results equal the oracle's."""
+    """Six lists stepped for three rounds, with more filler lists than the cache holds
+    stepped after each of them (no host synchronisation in between), so every list is evicted
+    and uploaded again each round and slots are rewritten while earlier launches are queued;
+    results equal the oracle's."""
     rng = np.random.default_rng(6)
     lists = []
     for li in range(6):
         items = [_make(rng, 2048 * (1 + li) + 37 * li, 100 + 10 * li + k, 8 + li) for k in range(2)]
         lists.append(([x[0] for x in items], [x[1] for x in items]))
+    fill, keep = _fillers(_slot_cache() + 8, 5000)
+    fhp = opt8.make_hparams(1e-3, 0.9, 0.999, 1e-8, 0.0, 1, 5)
     stats = {}
     for rnd in range(3):
-        for li, (sets, states) in enumerate(lists):
-            hp = _hp(rnd + 1)
+        hp = _hp(rnd + 1)
+        for sets, _ in lists:
             _launch(sets, hp, None)
-            torch.cuda.synchronize()
+            for f in fill:
+                opt8.opt8_adamw_step(f, fhp)
+        torch.cuda.synchronize()
+        for li, (sets, states) in enumerate(lists):
             for k, (s, st) in enumerate(zip(sets, states)):
                 want = oracle_step(s, st, hp)
                 compare_state(f"cache round {rnd} list {li}/t{s.tensor_id}", s.read(), want, M8, stats)
                 states[k] = want
     log(f"descriptor cache: mismatches {sum(stats.values())}")
+    del keep
     assert sum(stats.values()) == 0
 
 
 def test_concurrent_host_threads():
-    """Two host threads, each with its own stream and three lists of its own (six lists, the
-    cache holds four), launch four rounds of steps with no host synchronisation until both
-    have finished: the calls share the device's descriptor cache (evicting each other's lists)
-    and must still give each list the oracle's result."""
+    """Two host threads, each with its own stream, three lists of its own and more filler
+    lists than half the cache holds, launch four rounds of steps with no host synchronisation
+    until both have finished: the calls share the device's descriptor cache (evicting each
+    other's lists) and must still give each list the oracle's result."""
     import threading
 
     rng = np.random.default_rng(9)
@@ -115,6 +154,9 @@ def test_concurrent_host_threads():
                      for k in range(2)]
             lists.append(([x[0] for x in items], [x[1] for x in items]))
         groups.append(lists)
+    half = _slot_cache() // 2 + 4
+    fillers = [_fillers(half, 6000 + th * half) for th in range(2)]
+    fhp = opt8.make_hparams(1e-3, 0.9, 0.999, 1e-8, 0.0, 1, 5)
     streams = [torch.cuda.Stream(), torch.cuda.Stream()]
     torch.cuda.synchronize()
     errors = []
@@ -124,6 +166,8 @@ def test_concurrent_host_threads():
             for rnd in range(4):
                 for sets, _ in groups[th]:
                     _launch(sets, _hp(rnd + 1), streams[th])
+                for f in fillers[th][0]:
+                    opt8.opt8_adamw_step(f, fhp, stream=streams[th])
         except Exception as e:   # re-raised in the main thread
             errors.append(e)
 
