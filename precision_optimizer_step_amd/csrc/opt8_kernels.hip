@@ -241,6 +241,16 @@ __device__ __forceinline__ float wave_max_nonneg(float x) {
   return __uint_as_float(__builtin_amdgcn_readlane(static_cast<int>(u), 63));
 }
 
+// The same maximum over each run of eight lanes (0-7, 8-15, ...), every lane
+// of a run getting its run's value: quad steps, then the half-row mirror.
+__device__ __forceinline__ float group8_max_nonneg(float x) {
+  uint32_t u = __float_as_uint(x);
+  u = max(u, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(u), 0xB1, 0xF, 0xF, false)));
+  u = max(u, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(u), 0x4E, 0xF, 0xF, false)));
+  u = max(u, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(u), 0x141, 0xF, 0xF, false)));
+  return __uint_as_float(u);
+}
+
 // ----------------------------------------------------------------------------- 8-bit, plain path
 // Every block whose values leave the fast path's range, every partial block,
 // and every non-finite case: IEEE operations, binary search over the
@@ -538,6 +548,166 @@ __device__ __forceinline__ bool block_8bit_fast(const DevTensor& d, int64_t blk,
     d.amax_v[blk] = mxv;
   }
   return true;
+}
+
+// ----------------------------------------------------------------------------- 8-bit, short last blocks
+// Last partial blocks of at most kShortTail (64) elements (AdamW): such a block fits
+// one 8-element group per lane in eight lanes, so a wave takes eight of them at
+// once, lane run t (lanes 8t .. 8t+7) the entry first + t, its lane i holding
+// elements 8i .. 8i+7 as lane i of the one-block layout.  The arithmetic is the
+// fast path's; the block maxima are reduced within the run, the range check
+// decides per run, and the blocks of runs that fail it are then stepped one at
+// a time by the whole wave on the plain path.  (A wave per short block would
+// issue a whole wave's instructions for a few elements.)
+template <bool kNearest, bool kSS>
+__device__ __forceinline__ void blocks_8bit_short(const DevTensor* __restrict__ list, int64_t first, int64_t count,
+                                                  int lane, const StepScalars& sc, const uint8_t* lds,
+                                                  bool range_ok) {
+  const int t = lane >> 3, i = lane & 7;
+  const int64_t entry = first + t;
+  const bool has = entry < count;
+  DevTensor d{};
+  if (has) d = list[entry];
+  const int64_t blk = has ? (d.numel - 1) / kBlock : 0;
+  const int valid = has ? static_cast<int>(d.numel - blk * kBlock) : 0;
+  const int off = 8 * i;
+  const int64_t e0 = blk * kBlock;
+  const uint16_t* gp = d.grad + e0;
+  uint16_t* pp = d.param + e0;
+  uint8_t* mp = static_cast<uint8_t*>(d.m) + e0;
+  uint8_t* vp = static_cast<uint8_t*>(d.v) + e0;
+
+  // a run's lanes past its block's end (and runs with no block) hold a zero
+  // gradient and parameter and the zero codes, whose moments are +0
+  uint4 G = make_uint4(0u, 0u, 0u, 0u), P = G;
+  uint2 QM = make_uint2(0x7F7F7F7Fu, 0x7F7F7F7Fu), QV = make_uint2(0u, 0u);
+  float am = 0.0f, av = 0.0f;
+  if (has) {
+    am = d.amax_m[blk];
+    av = d.amax_v[blk];
+    if (off + 8 <= valid) {
+      G = ld_stream16(gp + off);
+      P = ld_stream16(pp + off);
+      QM = ld_stream8(mp + off);
+      QV = ld_stream8(vp + off);
+    } else if (off < valid) {
+      uint32_t gw[4] = {0, 0, 0, 0}, pw[4] = {0, 0, 0, 0};
+      uint32_t mw[2] = {0x7F7F7F7Fu, 0x7F7F7F7Fu}, vw[2] = {0, 0};
+      for (int j = 0; j < 8 && off + j < valid; ++j) {
+        const int sh16 = 16 * (j & 1), sh8 = 8 * (j & 3);
+        gw[j >> 1] |= static_cast<uint32_t>(gp[off + j]) << sh16;
+        pw[j >> 1] |= static_cast<uint32_t>(pp[off + j]) << sh16;
+        mw[j >> 2] = (mw[j >> 2] & ~(0xFFu << sh8)) | (static_cast<uint32_t>(mp[off + j]) << sh8);
+        vw[j >> 2] |= static_cast<uint32_t>(vp[off + j]) << sh8;
+      }
+      G = make_uint4(gw[0], gw[1], gw[2], gw[3]);
+      P = make_uint4(pw[0], pw[1], pw[2], pw[3]);
+      QM = make_uint2(mw[0], mw[1]);
+      QV = make_uint2(vw[0], vw[1]);
+    }
+  }
+
+  // pass 1 (every lane, so the run reductions see all eight)
+  const float* cb_s = reinterpret_cast<const float*>(lds + kOffCbS);
+  const float* cb_u = reinterpret_cast<const float*>(lds + kOffCbU);
+  float M2[8], V2[8];
+  float mxm = 0.0f, mxv = 0.0f, mxp = 0.0f;
+  int emin = 0;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const float g = bf16_at(G, j);
+    const float m1 = cb_s[byte_at(QM, j)] * am;
+    const float v1 = cb_u[byte_at(QV, j)] * av;
+    const float m2 = sc.beta1 * m1 + sc.w1 * g;
+    const float v2 = sc.beta2 * v1 + sc.w2 * (g * g);
+    M2[j] = m2;
+    V2[j] = v2;
+    mxm = __builtin_elementwise_maximum(mxm, fabsf(m2));
+    mxv = __builtin_elementwise_maximum(mxv, v2);
+    mxp = __builtin_elementwise_maximum(mxp, fabsf(bf16_at(P, j)));
+    emin = min(min(emin, __builtin_amdgcn_frexp_expf(m2)), __builtin_amdgcn_frexp_expf(v2));
+  }
+  const bool lane_finite = (mxm <= 3.0e38f) && (mxv <= 3.0e38f) && (mxp <= 3.4028235e38f);
+  mxm = group8_max_nonneg(mxm);
+  mxv = group8_max_nonneg(mxv);
+  // the fast path's range check, per run
+  const int e_den = __builtin_amdgcn_frexp_expf(sqrtf(mxv) * sc.rbc2 + sc.eps);
+  const int e_mmax = __builtin_amdgcn_frexp_expf(mxm);
+  const int e_eps = __builtin_amdgcn_frexp_expf(sc.eps);
+  const int floor_e = max(-88, e_den - 98);
+  const bool lane_bad = !lane_finite || emin < floor_e;
+  const bool run_bad = ((__builtin_amdgcn_ballot_w64(lane_bad) >> (8 * t)) & 0xFFu) != 0;
+  const bool fast = has && range_ok && av >= 0.0f && e_den <= 100 && e_mmax - e_eps <= 100 && !run_bad;
+
+  if (fast) {
+    const float* mid_s = reinterpret_cast<const float*>(lds + kOffMidS);
+    const float* mid_u = reinterpret_cast<const float*>(lds + kOffMidU);
+    const float inv_m = mxm >= kMinNormal ? 1.0f / mxm : 0.0f;
+    const float inv_v = mxv >= kMinNormal ? 1.0f / mxv : 0.0f;
+    const uint64_t grp = (static_cast<uint64_t>(d.index_base + e0) >> 3) + static_cast<uint64_t>(i);
+    Rand4 rnd{{0, 0, 0, 0}};
+    Rand4 rm{{0, 0, 0, 0}}, rv{{0, 0, 0, 0}};
+    if constexpr (kSS && !kNearest) all_bits(grp, d.tensor_id, sc, rnd, rm, rv);
+    else if (!kNearest) rnd = group_bits(grp, 0u, d.tensor_id, sc);
+    if constexpr (kSS && kNearest) state_bits(grp, d.tensor_id, sc, rm, rv);
+    uint32_t sums[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float p = bf16_at(P, j);
+      const float den = sqrt_rn(V2[j]) * sc.rbc2 + sc.eps;
+      const float u = div_rn(M2[j], den);
+      const float pn = (p - sc.lrwd * p) - sc.step_size * u;
+      const uint32_t b = __float_as_uint(pn);
+      sums[j] = b + (kNearest ? (0x7FFFu + ((b >> 16) & 1u)) : r16_of(rnd, j));
+    }
+    uint32_t cm[2] = {0, 0}, cv[2] = {0, 0};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      uint32_t qm, qv;
+      if constexpr (kSS) {
+        qm = code_sr<true, true>(M2[j] * inv_m, lds, r16_of(rm, j));
+        qv = code_sr<false, true>(V2[j] * inv_v, lds, r16_of(rv, j));
+      } else {
+        qm = code_s(M2[j] * inv_m, lds, mid_s);
+        qv = code_u(V2[j] * inv_v, lds, mid_u);
+      }
+      cm[j >> 2] |= qm << (8 * (j & 3));
+      cv[j >> 2] |= qv << (8 * (j & 3));
+    }
+    if (off + 8 <= valid) {
+      st_stream16(pp + off, make_uint4(__builtin_amdgcn_perm(sums[1], sums[0], 0x07060302u),
+                                       __builtin_amdgcn_perm(sums[3], sums[2], 0x07060302u),
+                                       __builtin_amdgcn_perm(sums[5], sums[4], 0x07060302u),
+                                       __builtin_amdgcn_perm(sums[7], sums[6], 0x07060302u)));
+      st_stream8(mp + off, make_uint2(cm[0], cm[1]));
+      st_stream8(vp + off, make_uint2(cv[0], cv[1]));
+    } else {
+      for (int j = 0; j < 8 && off + j < valid; ++j) {
+        pp[off + j] = static_cast<uint16_t>(sums[j] >> 16);
+        mp[off + j] = static_cast<uint8_t>(cm[j >> 2] >> (8 * (j & 3)));
+        vp[off + j] = static_cast<uint8_t>(cv[j >> 2] >> (8 * (j & 3)));
+      }
+    }
+    if (i == 0) {
+      d.amax_m[blk] = mxm;
+      d.amax_v[blk] = mxv;
+    }
+  }
+
+  // the blocks whose run failed the check, one at a time by the whole wave
+  uint64_t slow = __builtin_amdgcn_ballot_w64(has && !fast && i == 0);
+  while (slow) {
+    const int src = __builtin_ctzll(slow);   // lane 8t of such a run
+    slow &= slow - 1;
+    DevTensor u;
+    const uint32_t* w = reinterpret_cast<const uint32_t*>(&d);
+    uint32_t* uw = reinterpret_cast<uint32_t*>(&u);
+#pragma unroll
+    for (int k = 0; k < static_cast<int>(sizeof(DevTensor) / 4); ++k)
+      uw[k] = __builtin_amdgcn_readlane(static_cast<int>(w[k]), src);
+    const int64_t ublk = (u.numel - 1) / kBlock;
+    block_8bit_plain<false, kSS>(u, ublk, lane, static_cast<int>(u.numel - ublk * kBlock), sc, lds);
+  }
 }
 
 // ----------------------------------------------------------------------------- bf16 state (SR)
@@ -1350,6 +1520,40 @@ step_kernel(const DevTensor* __restrict__ list, int ntensors, int64_t total_bloc
   }
 }
 
+// AdamW's short last blocks (one entry each), eight to a wave; the grid is
+// the resident count or fewer, each wave taking every nw-th set of eight.
+template <bool SS>
+__global__ void __launch_bounds__(kThreads)
+short_kernel(const DevTensor* __restrict__ list, int64_t count, StepScalars sc, int range_ok) {
+  constexpr int kLds = SS ? kTableBytesSR : kTableBytes;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kLds];
+  stage_tables<kLds>(lds);
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+  const int64_t nw = static_cast<int64_t>(gridDim.x) * kWaves;
+  for (int64_t w = static_cast<int64_t>(blockIdx.x) * kWaves + wave; w * 8 < count; w += nw) {
+    if (sc.param_round) blocks_8bit_short<true, SS>(list, w * 8, count, lane, sc, lds, range_ok != 0);
+    else blocks_8bit_short<false, SS>(list, w * 8, count, lane, sc, lds, range_ok != 0);
+  }
+}
+
+template <bool SS>
+hipError_t launch_short(const DevTensor* list, int n, const StepScalars& sc, hipStream_t stream, int resident,
+                        int range_ok) {
+  const int64_t sets = (static_cast<int64_t>(n) + 7) / 8;
+  const int64_t grid = std::max<int64_t>(1, std::min<int64_t>((sets + kWaves - 1) / kWaves, resident));
+  hipLaunchKernelGGL((short_kernel<SS>), dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0, stream, list,
+                     static_cast<int64_t>(n), sc, range_ok);
+  return hipGetLastError();
+}
+
+template <bool SS>
+int occupancy_short() {
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, short_kernel<SS>, kThreads, 0) != hipSuccess) return 1;
+  return n > 0 ? n : 1;
+}
+
 template <Kind K, int A, bool SS>
 hipError_t launch_kind(const DevTensor* list, int n, int64_t total_blocks, const StepScalars& sc,
                        hipStream_t stream, int num_cu, int resident, int range_ok, const uint32_t* map) {
@@ -1429,6 +1633,11 @@ hipError_t launch_step(Kind kind, int algo, const DevTensor* list, int n, int64_
       if (total_blocks != n) return hipErrorInvalidValue;
       return ss ? launch_algo<Kind::k8bitTail, true>(algo, list, n, total_blocks, sc, stream, num_cu, resident, range_ok, map)
                 : launch_algo<Kind::k8bitTail, false>(algo, list, n, total_blocks, sc, stream, num_cu, resident, range_ok, map);
+    case Kind::k8bitShort:
+      // AdamW only, one block per entry
+      if (algo != kAdamW || total_blocks != n) return hipErrorInvalidValue;
+      return ss ? launch_short<true>(list, n, sc, stream, resident, range_ok)
+                : launch_short<false>(list, n, sc, stream, resident, range_ok);
     case Kind::kBf16:
       return launch_algo<Kind::kBf16, false>(algo, list, n, total_blocks, sc, stream, num_cu, resident, range_ok, map);
     case Kind::kFp32:
@@ -1443,6 +1652,7 @@ int occupancy_per_cu(Kind kind, int algo, bool state_sr) {
       return state_sr ? occupancy_algo<Kind::k8bit, true>(algo) : occupancy_algo<Kind::k8bit, false>(algo);
     case Kind::k8bitTail:
       return state_sr ? occupancy_algo<Kind::k8bitTail, true>(algo) : occupancy_algo<Kind::k8bitTail, false>(algo);
+    case Kind::k8bitShort: return state_sr ? occupancy_short<true>() : occupancy_short<false>();
     case Kind::kBf16: return occupancy_algo<Kind::kBf16, false>(algo);
     case Kind::kFp32: return occupancy_algo<Kind::kFp32, false>(algo);
   }

@@ -207,6 +207,26 @@ int main() {
     for (const auto& L : g.launches) CHECK(L.num_cu == 256 && L.resident == 256 * 3 && L.algo == 0);
     expect_scalars(a.sc, h1, true);
   }
+  // partial last blocks of at most 64 elements: AdamW packs them into the short-block kernel,
+  // the one-state rules keep them with the others
+  {
+    const std::vector<opt8_tensor> tails = {tensor(7, 4097, OPT8_STATE_8BIT, 20), tensor(8, 2048 + 64, OPT8_STATE_8BIT, 21),
+                                            tensor(9, 2048 + 65, OPT8_STATE_8BIT, 22), tensor(10, 30, OPT8_STATE_8BIT, 23)};
+    g.launches.clear();
+    CHECK(step(tails, h1) == OPT8_OK);
+    CHECK(g.launches.size() == 3);
+    if (g.launches.size() == 3) {
+      CHECK(g.launches[0].kind == 0 && g.launches[0].n == 3 && g.launches[0].total_blocks == 4 && g.launches[0].ok);
+      CHECK(g.launches[1].kind == 3 && g.launches[1].n == 1 && g.launches[1].ok);           // 65 elements
+      CHECK((g.launches[1].ids == std::vector<uint32_t>{22}));
+      CHECK(g.launches[2].kind == 4 && g.launches[2].n == 3 && g.launches[2].total_blocks == 3 && g.launches[2].ok);
+      CHECK((g.launches[2].ids == std::vector<uint32_t>{20, 21, 23}));                      // 1, 64 and 30 elements
+    }
+    g.launches.clear();
+    CHECK(opt8_lion_step(tails.data(), static_cast<int32_t>(tails.size()), &h1, nullptr) == OPT8_OK);
+    CHECK(g.launches.size() == 2);
+    if (g.launches.size() == 2) CHECK(g.launches[1].kind == 3 && g.launches[1].n == 4 && g.launches[1].ok);
+  }
 
   // a list that passed is not checked again while it stays byte-identical; edited in
   // place it is checked afresh
@@ -321,8 +341,11 @@ int main() {
     g.launches.clear();
     CHECK(step(big, h1) == OPT8_OK);
     CHECK(g.mallocs > mallocs);
-    CHECK(g.launches.size() == 2 && g.launches[0].n == 1000 && g.launches[0].ok);
-    if (g.launches.size() == 2) CHECK(g.launches[1].kind == 3 && g.launches[1].n == 999);
+    CHECK(g.launches.size() == 3 && g.launches[0].n == 1000 && g.launches[0].ok);
+    if (g.launches.size() == 3) {   // last blocks of 65..999 elements, and of 1..64
+      CHECK(g.launches[1].kind == 3 && g.launches[1].n == 935 && g.launches[1].ok);
+      CHECK(g.launches[2].kind == 4 && g.launches[2].n == 64 && g.launches[2].ok);
+    }
     // an overlap far down a long list is found
     big[999].grad = reinterpret_cast<const uint16_t*>(base_of(100 + 500, 1) + 1024);
     CHECK(step(big, h1) == OPT8_E_ALIAS);
