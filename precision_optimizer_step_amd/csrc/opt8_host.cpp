@@ -297,17 +297,23 @@ struct ValidatedCache {
 };
 thread_local ValidatedCache t_validated;
 
-// FNV-1a over the list's 8-byte words (an opt8_tensor is a whole number of them).
+// A filter before the byte compare, in constant time: FNV-1a over the count and
+// the 8-byte words of the first and last four descriptors (lists that differ
+// only in between share it and are told apart by the compare).
 uint64_t list_hash(const opt8_tensor* t, int32_t n) {
   static_assert(sizeof(opt8_tensor) % sizeof(uint64_t) == 0, "descriptor size");
-  const size_t words = sizeof(opt8_tensor) / sizeof(uint64_t) * static_cast<size_t>(n);
-  const unsigned char* p = reinterpret_cast<const unsigned char*>(t);
-  uint64_t h = 0xCBF29CE484222325ull;
-  for (size_t i = 0; i < words; ++i) {
-    uint64_t w;
-    std::memcpy(&w, p + i * sizeof w, sizeof w);
-    h = (h ^ w) * 0x100000001B3ull;
-  }
+  constexpr size_t kWords = sizeof(opt8_tensor) / sizeof(uint64_t);
+  uint64_t h = (0xCBF29CE484222325ull ^ static_cast<uint64_t>(n)) * 0x100000001B3ull;
+  auto mix = [&](int32_t i) {
+    const unsigned char* p = reinterpret_cast<const unsigned char*>(t + i);
+    for (size_t k = 0; k < kWords; ++k) {
+      uint64_t w;
+      std::memcpy(&w, p + k * sizeof w, sizeof w);
+      h = (h ^ w) * 0x100000001B3ull;
+    }
+  };
+  for (int32_t i = 0; i < std::min<int32_t>(n, 4); ++i) mix(i);
+  for (int32_t i = std::max<int32_t>(4, n - 4); i < n; ++i) mix(i);
   return h;
 }
 
