@@ -174,9 +174,10 @@ int32_t opt8_default_mode(int64_t numel);
  * error (every status but OPT8_E_HIP and OPT8_E_NOMEM) nothing is queued and
  * nothing is modified; OPT8_E_NOMEM (the host could not allocate the
  * library's copy of the list) is returned before any launch, with at most a
- * descriptor upload into an unused cache slot queued.  A step is up to four kernel launches, one per kind of tensor in
+ * descriptor upload into an unused cache slot queued.  A step is up to five kernel launches, one per kind of tensor in
  * the list (8-bit full blocks, bf16 state, fp32 state, 8-bit last partial
- * blocks); if a launch fails (OPT8_E_HIP) the kinds launched before it have
+ * blocks, and for AdamW 8-bit last blocks of at most 64 elements, eight to a
+ * wave); if a launch fails (OPT8_E_HIP) the kinds launched before it have
  * been queued and will step their tensors, and the message names them.
  * n == 0 is a no-op.  Tensors of
  * different modes may be mixed.  Concurrent calls on different streams must
