@@ -176,7 +176,7 @@ int32_t opt8_default_mode(int64_t numel);
  * library's copy of the list) is returned before any launch, with at most a
  * descriptor upload into an unused cache slot queued.  A step is up to five kernel launches, one per kind of tensor in
  * the list (8-bit full blocks, bf16 state, fp32 state, 8-bit last partial
- * blocks, and for AdamW 8-bit last blocks of at most 64 elements, eight to a
+ * blocks longer than 64 elements, and those of at most 64, eight to a
  * wave); if a launch fails (OPT8_E_HIP) the kinds launched before it have
  * been queued and will step their tensors, and the message names them.
  * n == 0 is a no-op.  Tensors of

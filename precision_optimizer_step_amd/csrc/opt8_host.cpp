@@ -194,9 +194,9 @@ constexpr int kKinds = 5;
 
 // The device-side form of a tensor list: one sub-list per kernel, each with its
 // own block numbering (full blocks of 8-bit tensors, bf16-state tensors,
-// fp32-state tensors, the partial last block of 8-bit tensors, and for AdamW
-// the partial last blocks of at most kShortTail elements, which its short-block
-// kernel packs eight to a wave), in that order.
+// fp32-state tensors, the partial last block of 8-bit tensors longer than
+// kShortTail elements, and those of at most kShortTail elements, which the
+// short-block kernel packs eight to a wave), in that order.
 struct Plan {
   std::vector<DevTensor> list;
   int count[kKinds] = {};
@@ -213,13 +213,13 @@ size_t map_units(const Plan& p) {
 }
 
 // Blocks tensor `x` contributes to the sub-list of `kind` (0: not in it).
-int64_t blocks_in_kind(const opt8_tensor& x, int kind, bool two_state) {
+int64_t blocks_in_kind(const opt8_tensor& x, int kind) {
   const bool tail = kind == static_cast<int>(Kind::k8bitTail) || kind == static_cast<int>(Kind::k8bitShort);
   const int mode = tail ? OPT8_STATE_8BIT : kind;
   if (x.mode != mode) return 0;
   if (tail) {
     const int64_t rest = x.numel % kBlock;
-    const bool short_tail = two_state && rest > 0 && rest <= kShortTail;
+    const bool short_tail = rest > 0 && rest <= kShortTail;
     if (kind == static_cast<int>(Kind::k8bitShort)) return short_tail ? 1 : 0;
     return (rest > 0 && !short_tail) ? 1 : 0;
   }
@@ -234,7 +234,7 @@ void build_plan(const opt8_tensor* t, int32_t n, bool two_state, Plan& p) {
   int64_t total = 0;
   for (int32_t i = 0; i < n; ++i)
     for (int kind = 0; kind < kKinds; ++kind)
-      if (blocks_in_kind(t[i], kind, two_state)) ++p.count[kind];
+      if (blocks_in_kind(t[i], kind)) ++p.count[kind];
   for (int kind = 0; kind < kKinds; ++kind) {
     p.first[kind] = static_cast<int>(total);
     total += p.count[kind];
@@ -246,7 +246,7 @@ void build_plan(const opt8_tensor* t, int32_t n, bool two_state, Plan& p) {
     const opt8_tensor& x = t[i];
     const bool q8 = x.mode == OPT8_STATE_8BIT;
     for (int kind = 0; kind < kKinds; ++kind) {
-      const int64_t nb = blocks_in_kind(x, kind, two_state);
+      const int64_t nb = blocks_in_kind(x, kind);
       if (!nb) continue;
       DevTensor& d = p.list[pos[kind]++];
       d.param = x.param;

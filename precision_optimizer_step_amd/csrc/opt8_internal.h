@@ -85,9 +85,9 @@ static_assert(kOffPairU + 2048 <= kOffFloor + static_cast<int>(kKeyLo) &&
               kOffFloor + static_cast<int>(kKeyHi) < kOffFloor + static_cast<int>(kKeySNeg),
               "floor LUT regions overlap the pairs");
 
-// k8bitTail: the last partial block of 8-bit tensors, a wave per block;
-// k8bitShort: AdamW's last partial blocks of at most kShortTail elements,
-// eight blocks per wave (one 8-lane run each).
+// k8bitTail: the last partial blocks of 8-bit tensors longer than kShortTail
+// elements, a wave per block; k8bitShort: those of at most kShortTail
+// elements, eight blocks per wave (one 8-lane run each).
 enum class Kind : int { k8bit = 0, kBf16 = 1, kFp32 = 2, k8bitTail = 3, k8bitShort = 4 };
 constexpr int kShortTail = 64;
 

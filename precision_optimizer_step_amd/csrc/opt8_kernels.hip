@@ -551,7 +551,7 @@ __device__ __forceinline__ bool block_8bit_fast(const DevTensor& d, int64_t blk,
 }
 
 // ----------------------------------------------------------------------------- 8-bit, short last blocks
-// Last partial blocks of at most kShortTail (64) elements (AdamW): such a block fits
+// Last partial blocks of at most kShortTail (64) elements: such a block fits
 // one 8-element group per lane in eight lanes, so a wave takes eight of them at
 // once, lane run t (lanes 8t .. 8t+7) the entry first + t, its lane i holding
 // elements 8i .. 8i+7 as lane i of the one-block layout.  The arithmetic is the
@@ -1206,6 +1206,115 @@ __device__ __forceinline__ bool block_1s_8bit_fast(const DevTensor& d, int64_t b
   return true;
 }
 
+// Short last blocks of the one-state rules, eight to a wave as in
+// blocks_8bit_short: the fast path's arithmetic per lane, the run's block
+// maximum reduced in the run, and a run with a NaN result or a non-finite
+// moment stepped afterwards by the whole wave on the plain path.
+template <int A, bool kNearest, bool kSS>
+__device__ __forceinline__ void blocks_1s_8bit_short(const DevTensor* __restrict__ list, int64_t first,
+                                                     int64_t count, int lane, const StepScalars& sc,
+                                                     const uint8_t* lds) {
+  const int t = lane >> 3, i = lane & 7;
+  const int64_t entry = first + t;
+  const bool has = entry < count;
+  DevTensor d{};
+  if (has) d = list[entry];
+  const int64_t blk = has ? (d.numel - 1) / kBlock : 0;
+  const int valid = has ? static_cast<int>(d.numel - blk * kBlock) : 0;
+  const int off = 8 * i;
+  const int64_t e0 = blk * kBlock;
+  const uint16_t* gp = d.grad + e0;
+  uint16_t* pp = d.param + e0;
+  uint8_t* mp = static_cast<uint8_t*>(d.m) + e0;
+
+  uint4 G = make_uint4(0u, 0u, 0u, 0u), P = G;
+  uint2 QM = make_uint2(0x7F7F7F7Fu, 0x7F7F7F7Fu);
+  float am = 0.0f;
+  if (has) {
+    am = d.amax_m[blk];
+    if (off + 8 <= valid) {
+      G = ld_stream16(gp + off);
+      P = ld_stream16(pp + off);
+      QM = ld_stream8(mp + off);
+    } else if (off < valid) {
+      uint32_t gw[4] = {0, 0, 0, 0}, pw[4] = {0, 0, 0, 0};
+      uint32_t mw[2] = {0x7F7F7F7Fu, 0x7F7F7F7Fu};
+      for (int j = 0; j < 8 && off + j < valid; ++j) {
+        const int sh16 = 16 * (j & 1), sh8 = 8 * (j & 3);
+        gw[j >> 1] |= static_cast<uint32_t>(gp[off + j]) << sh16;
+        pw[j >> 1] |= static_cast<uint32_t>(pp[off + j]) << sh16;
+        mw[j >> 2] = (mw[j >> 2] & ~(0xFFu << sh8)) | (static_cast<uint32_t>(mp[off + j]) << sh8);
+      }
+      G = make_uint4(gw[0], gw[1], gw[2], gw[3]);
+      P = make_uint4(pw[0], pw[1], pw[2], pw[3]);
+      QM = make_uint2(mw[0], mw[1]);
+    }
+  }
+  const float* cb_s = reinterpret_cast<const float*>(lds + kOffCbS);
+  const float* mid_s = reinterpret_cast<const float*>(lds + kOffMidS);
+  const uint64_t grp = (static_cast<uint64_t>(d.index_base + e0) >> 3) + static_cast<uint64_t>(i);
+  Rand4 rnd{{0, 0, 0, 0}};
+  if (!kNearest) rnd = group_bits(grp, 0u, d.tensor_id, sc);
+  float M2[8];
+  float mxm = 0.0f;
+  bool nan = false;
+  uint32_t sums[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    float m2;
+    const float pn = update1<A>(bf16_at(P, j), bf16_at(G, j), cb_s[byte_at(QM, j)] * am, sc, m2);
+    M2[j] = m2;
+    mxm = fmaxf(mxm, fabsf(m2));
+    nan |= __builtin_isunordered(pn, m2);
+    const uint32_t b = __float_as_uint(pn);
+    sums[j] = b + (kNearest ? (0x7FFFu + ((b >> 16) & 1u)) : r16_of(rnd, j));
+  }
+  mxm = group8_max_nonneg(mxm);
+  const bool run_bad = ((__builtin_amdgcn_ballot_w64(nan) >> (8 * t)) & 0xFFu) != 0;
+  const bool fast = has && !run_bad && mxm <= 3.0e38f;
+
+  if (fast) {
+    const float inv = mxm >= kMinNormal ? 1.0f / mxm : 0.0f;
+    uint32_t cm[2] = {0, 0};
+    if constexpr (kSS) {
+      const Rand4 rm = group_bits(grp, 1u, d.tensor_id, sc);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) cm[j >> 2] |= code_sr<true>(M2[j] * inv, lds, r16_of(rm, j)) << (8 * (j & 3));
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) cm[j >> 2] |= code_s(M2[j] * inv, lds, mid_s) << (8 * (j & 3));
+    }
+    if (off + 8 <= valid) {
+      st_stream16(pp + off, make_uint4(__builtin_amdgcn_perm(sums[1], sums[0], 0x07060302u),
+                                       __builtin_amdgcn_perm(sums[3], sums[2], 0x07060302u),
+                                       __builtin_amdgcn_perm(sums[5], sums[4], 0x07060302u),
+                                       __builtin_amdgcn_perm(sums[7], sums[6], 0x07060302u)));
+      st_stream8(mp + off, make_uint2(cm[0], cm[1]));
+    } else {
+      for (int j = 0; j < 8 && off + j < valid; ++j) {
+        pp[off + j] = static_cast<uint16_t>(sums[j] >> 16);
+        mp[off + j] = static_cast<uint8_t>(cm[j >> 2] >> (8 * (j & 3)));
+      }
+    }
+    if (i == 0) d.amax_m[blk] = mxm;
+  }
+
+  // the blocks whose run failed the check, one at a time by the whole wave
+  uint64_t slow = __builtin_amdgcn_ballot_w64(has && !fast && i == 0);
+  while (slow) {
+    const int src = __builtin_ctzll(slow);   // lane 8t of such a run
+    slow &= slow - 1;
+    DevTensor u;
+    const uint32_t* w = reinterpret_cast<const uint32_t*>(&d);
+    uint32_t* uw = reinterpret_cast<uint32_t*>(&u);
+#pragma unroll
+    for (int k = 0; k < static_cast<int>(sizeof(DevTensor) / 4); ++k)
+      uw[k] = __builtin_amdgcn_readlane(static_cast<int>(w[k]), src);
+    const int64_t ublk = (u.numel - 1) / kBlock;
+    block_1s_8bit_plain<A, false, kSS>(u, ublk, lane, static_cast<int>(u.numel - ublk * kBlock), sc, lds);
+  }
+}
+
 // bf16 state of the one-state rules: plain operations with every rounding's NaN
 // rule.  Full blocks move whole 8-element groups with 16-byte accesses (the
 // random words of the parameter and the state come from one two-stream Philox
@@ -1520,9 +1629,10 @@ step_kernel(const DevTensor* __restrict__ list, int ntensors, int64_t total_bloc
   }
 }
 
-// AdamW's short last blocks (one entry each), eight to a wave; the grid is
-// the resident count or fewer, each wave taking every nw-th set of eight.
-template <bool SS>
+// The short last blocks of 8-bit tensors (one entry each), eight to a wave;
+// the grid is the resident count or fewer, each wave taking every nw-th set
+// of eight.
+template <int A, bool SS>
 __global__ void __launch_bounds__(kThreads)
 short_kernel(const DevTensor* __restrict__ list, int64_t count, StepScalars sc, int range_ok) {
   constexpr int kLds = SS ? kTableBytesSR : kTableBytes;
@@ -1532,26 +1642,52 @@ short_kernel(const DevTensor* __restrict__ list, int64_t count, StepScalars sc, 
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
   const int64_t nw = static_cast<int64_t>(gridDim.x) * kWaves;
   for (int64_t w = static_cast<int64_t>(blockIdx.x) * kWaves + wave; w * 8 < count; w += nw) {
-    if (sc.param_round) blocks_8bit_short<true, SS>(list, w * 8, count, lane, sc, lds, range_ok != 0);
-    else blocks_8bit_short<false, SS>(list, w * 8, count, lane, sc, lds, range_ok != 0);
+    if constexpr (A == kAdamW) {
+      if (sc.param_round) blocks_8bit_short<true, SS>(list, w * 8, count, lane, sc, lds, range_ok != 0);
+      else blocks_8bit_short<false, SS>(list, w * 8, count, lane, sc, lds, range_ok != 0);
+    } else {
+      if (sc.param_round) blocks_1s_8bit_short<A, true, SS>(list, w * 8, count, lane, sc, lds);
+      else blocks_1s_8bit_short<A, false, SS>(list, w * 8, count, lane, sc, lds);
+    }
   }
 }
 
-template <bool SS>
+template <int A, bool SS>
 hipError_t launch_short(const DevTensor* list, int n, const StepScalars& sc, hipStream_t stream, int resident,
                         int range_ok) {
   const int64_t sets = (static_cast<int64_t>(n) + 7) / 8;
   const int64_t grid = std::max<int64_t>(1, std::min<int64_t>((sets + kWaves - 1) / kWaves, resident));
-  hipLaunchKernelGGL((short_kernel<SS>), dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0, stream, list,
+  hipLaunchKernelGGL((short_kernel<A, SS>), dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0, stream, list,
                      static_cast<int64_t>(n), sc, range_ok);
   return hipGetLastError();
 }
 
 template <bool SS>
+hipError_t launch_short_algo(int algo, const DevTensor* list, int n, const StepScalars& sc, hipStream_t stream,
+                             int resident, int range_ok) {
+  switch (algo) {
+    case kAdamW: return launch_short<kAdamW, SS>(list, n, sc, stream, resident, range_ok);
+    case kLion: return launch_short<kLion, SS>(list, n, sc, stream, resident, range_ok);
+    case kMomentum: return launch_short<kMomentum, SS>(list, n, sc, stream, resident, range_ok);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <int A, bool SS>
 int occupancy_short() {
   int n = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, short_kernel<SS>, kThreads, 0) != hipSuccess) return 1;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, short_kernel<A, SS>, kThreads, 0) != hipSuccess) return 1;
   return n > 0 ? n : 1;
+}
+
+template <bool SS>
+int occupancy_short_algo(int algo) {
+  switch (algo) {
+    case kAdamW: return occupancy_short<kAdamW, SS>();
+    case kLion: return occupancy_short<kLion, SS>();
+    case kMomentum: return occupancy_short<kMomentum, SS>();
+  }
+  return 1;
 }
 
 template <Kind K, int A, bool SS>
@@ -1634,10 +1770,10 @@ hipError_t launch_step(Kind kind, int algo, const DevTensor* list, int n, int64_
       return ss ? launch_algo<Kind::k8bitTail, true>(algo, list, n, total_blocks, sc, stream, num_cu, resident, range_ok, map)
                 : launch_algo<Kind::k8bitTail, false>(algo, list, n, total_blocks, sc, stream, num_cu, resident, range_ok, map);
     case Kind::k8bitShort:
-      // AdamW only, one block per entry
-      if (algo != kAdamW || total_blocks != n) return hipErrorInvalidValue;
-      return ss ? launch_short<true>(list, n, sc, stream, resident, range_ok)
-                : launch_short<false>(list, n, sc, stream, resident, range_ok);
+      // one block per entry
+      if (total_blocks != n) return hipErrorInvalidValue;
+      return ss ? launch_short_algo<true>(algo, list, n, sc, stream, resident, range_ok)
+                : launch_short_algo<false>(algo, list, n, sc, stream, resident, range_ok);
     case Kind::kBf16:
       return launch_algo<Kind::kBf16, false>(algo, list, n, total_blocks, sc, stream, num_cu, resident, range_ok, map);
     case Kind::kFp32:
@@ -1652,7 +1788,7 @@ int occupancy_per_cu(Kind kind, int algo, bool state_sr) {
       return state_sr ? occupancy_algo<Kind::k8bit, true>(algo) : occupancy_algo<Kind::k8bit, false>(algo);
     case Kind::k8bitTail:
       return state_sr ? occupancy_algo<Kind::k8bitTail, true>(algo) : occupancy_algo<Kind::k8bitTail, false>(algo);
-    case Kind::k8bitShort: return state_sr ? occupancy_short<true>() : occupancy_short<false>();
+    case Kind::k8bitShort: return state_sr ? occupancy_short_algo<true>(algo) : occupancy_short_algo<false>(algo);
     case Kind::kBf16: return occupancy_algo<Kind::kBf16, false>(algo);
     case Kind::kFp32: return occupancy_algo<Kind::kFp32, false>(algo);
   }

@@ -207,8 +207,7 @@ int main() {
     for (const auto& L : g.launches) CHECK(L.num_cu == 256 && L.resident == 256 * 3 && L.algo == 0);
     expect_scalars(a.sc, h1, true);
   }
-  // partial last blocks of at most 64 elements: AdamW packs them into the short-block kernel,
-  // the one-state rules keep them with the others
+  // partial last blocks of at most 64 elements go to the short-block kernel, under every rule
   {
     const std::vector<opt8_tensor> tails = {tensor(7, 4097, OPT8_STATE_8BIT, 20), tensor(8, 2048 + 64, OPT8_STATE_8BIT, 21),
                                             tensor(9, 2048 + 65, OPT8_STATE_8BIT, 22), tensor(10, 30, OPT8_STATE_8BIT, 23)};
@@ -224,8 +223,11 @@ int main() {
     }
     g.launches.clear();
     CHECK(opt8_lion_step(tails.data(), static_cast<int32_t>(tails.size()), &h1, nullptr) == OPT8_OK);
-    CHECK(g.launches.size() == 2);
-    if (g.launches.size() == 2) CHECK(g.launches[1].kind == 3 && g.launches[1].n == 4 && g.launches[1].ok);
+    CHECK(g.launches.size() == 3);
+    if (g.launches.size() == 3) {
+      CHECK(g.launches[1].kind == 3 && g.launches[1].n == 1 && g.launches[1].algo == 1 && g.launches[1].ok);
+      CHECK(g.launches[2].kind == 4 && g.launches[2].n == 3 && g.launches[2].algo == 1 && g.launches[2].ok);
+    }
   }
 
   // a list that passed is not checked again while it stays byte-identical; edited in

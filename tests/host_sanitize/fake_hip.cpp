@@ -139,12 +139,12 @@ hipError_t launch_step(Kind kind, int algo, const DevTensor* list, int n, int64_
     if (list[i].block_begin != b) L.ok = false;
     if (list[i].nblocks == 0) L.ok = false;
     // the last-partial-block kernels read entry b for block b; the short-block
-    // kernel takes AdamW's partial blocks of at most kShortTail elements, the
+    // kernel takes the partial blocks of at most kShortTail elements, the
     // other the rest
     if ((kind == Kind::k8bitTail || kind == Kind::k8bitShort) && list[i].nblocks != 1) L.ok = false;
     const int64_t rest = list[i].numel % kBlock;
-    if (kind == Kind::k8bitShort && (algo != kAdamW || rest < 1 || rest > kShortTail)) L.ok = false;
-    if (kind == Kind::k8bitTail && (rest < 1 || (algo == kAdamW && rest <= kShortTail))) L.ok = false;
+    if (kind == Kind::k8bitShort && (rest < 1 || rest > kShortTail)) L.ok = false;
+    if (kind == Kind::k8bitTail && rest <= kShortTail) L.ok = false;
     b += list[i].nblocks;
     L.numel += list[i].numel;
     L.ids.push_back(list[i].tensor_id);
