@@ -280,7 +280,7 @@ void build_plan(const opt8_tensor* t, int32_t n, bool two_state, Plan& p) {
 // sorting 6n ranges and building 2n descriptors and the block map.
 struct ValidatedList {
   std::vector<opt8_tensor> list;
-  uint64_t hash = 0;   // of the list's bytes, compared before them
+  uint64_t hash = 0;   // list_hash of the list, compared before its bytes
   bool two_state = false;
   bool valid = false;
   uint64_t stamp = 0;
