@@ -10,7 +10,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB = os.path.join(HERE, "libopt8.so")
 SOURCES = [os.path.join(HERE, "csrc", "opt8_host.cpp"), os.path.join(HERE, "csrc", "opt8_tables.cpp"),
-           os.path.join(HERE, "csrc", "opt8_kernels.hip")]
+           os.path.join(HERE, "csrc", "opt8_kernels.hip"), os.path.join(HERE, "csrc", "opt8_map.hip")]
 # bandwidth probe used by bench.py for the attainable-bandwidth context figure
 PROBE_LIB = os.path.join(HERE, "libopt8_probe.so")
 PROBE_SOURCES = [os.path.join(HERE, "csrc", "bw_probe.hip")]
@@ -29,8 +29,9 @@ FLAGS = [
 
 
 def kernel_fingerprint() -> str:
-    """sha256 over the kernel sources, the table builder and the device compile flags (names a
-    kernel build)."""
+    """sha256 over the step kernels' sources, the table builder and the device compile flags
+    (names the build of the kernels the profiles measure; the block-map fill in opt8_map.hip,
+    a copy-sized kernel run when a list is uploaded, is not one of them)."""
     import hashlib
     h = hashlib.sha256()
     for name in ("opt8_kernels.hip", "opt8_internal.h", "opt8_exact.h", "opt8_codes.h", "opt8_launch.h", "opt8_tables.cpp"):

@@ -14,6 +14,7 @@
 #include "../../include/opt8.h"
 #include "opt8_host_limits.h"
 #include "opt8_internal.h"
+#include "opt8_map.h"
 
 namespace opt8 {
 namespace {
@@ -202,14 +203,15 @@ struct Plan {
   int count[kKinds] = {};
   int first[kKinds] = {};
   int64_t blocks[kKinds] = {};
-  // for every full 8-bit block, the entry of its sub-list that holds it (the
-  // kernels read it instead of searching the descriptors)
-  std::vector<uint32_t> map;
 };
 
-// Descriptor-sized device units that hold the block map after the descriptors.
+// Descriptor-sized device units after the descriptors that hold the block map:
+// for every full 8-bit block, the entry of its sub-list that holds it (the
+// kernels read it instead of searching the descriptors; filled on the device
+// after each upload, launch_block_map).
 size_t map_units(const Plan& p) {
-  return (p.map.size() * sizeof(uint32_t) + sizeof(DevTensor) - 1) / sizeof(DevTensor);
+  const size_t blocks = static_cast<size_t>(p.blocks[static_cast<int>(Kind::k8bit)]);
+  return (blocks * sizeof(uint32_t) + sizeof(DevTensor) - 1) / sizeof(DevTensor);
 }
 
 // Blocks tensor `x` contributes to the sub-list of `kind` (0: not in it).
@@ -230,7 +232,13 @@ int64_t blocks_in_kind(const opt8_tensor& x, int kind) {
 // Two passes over the caller's array: count each sub-list, then place every
 // descriptor at its final position.
 void build_plan(const opt8_tensor* t, int32_t n, bool two_state, Plan& p) {
-  p = Plan{};
+  // reset in place: the vector keeps its capacity for the next list
+  p.list.clear();
+  for (int kind = 0; kind < kKinds; ++kind) {
+    p.count[kind] = 0;
+    p.first[kind] = 0;
+    p.blocks[kind] = 0;
+  }
   int64_t total = 0;
   for (int32_t i = 0; i < n; ++i)
     for (int kind = 0; kind < kKinds; ++kind)
@@ -262,12 +270,6 @@ void build_plan(const opt8_tensor* t, int32_t n, bool two_state, Plan& p) {
       d.nblocks = static_cast<uint32_t>(nb);
       p.blocks[kind] += nb;
     }
-  }
-  const int k8 = static_cast<int>(Kind::k8bit);
-  p.map.resize(static_cast<size_t>(p.blocks[k8]));
-  for (int e = 0; e < p.count[k8]; ++e) {
-    const DevTensor& d = p.list[p.first[k8] + e];
-    std::fill(p.map.begin() + d.block_begin, p.map.begin() + d.block_begin + d.nblocks, static_cast<uint32_t>(e));
   }
 }
 
@@ -328,14 +330,17 @@ size_t cache_budget() {
 }
 
 size_t entry_bytes(const ValidatedList& e) {
-  return e.list.capacity() * sizeof(opt8_tensor) + e.plan.list.capacity() * sizeof(DevTensor) +
-         e.plan.map.capacity() * sizeof(uint32_t);
+  return e.list.capacity() * sizeof(opt8_tensor) + e.plan.list.capacity() * sizeof(DevTensor);
 }
 
-void drop_entry(ValidatedList& e) {
+// Invalidates an entry; with release its memory is freed (budget eviction),
+// else kept for the list that replaces it (the vectors' capacity is reused).
+void drop_entry(ValidatedList& e, bool release) {
   e.valid = false;
-  std::vector<opt8_tensor>().swap(e.list);
-  e.plan = Plan{};
+  if (release) {
+    std::vector<opt8_tensor>().swap(e.list);
+    e.plan = Plan{};
+  }
   e.slot_dev = -1;
   e.slot_index = -1;
 }
@@ -363,7 +368,7 @@ int validate_tensors_cached(const opt8_tensor* t, int32_t n, bool two_state, Val
     c.entry.emplace_back();
     victim = &c.entry.back();
   }
-  drop_entry(*victim);
+  drop_entry(*victim, false);
   victim->hash = hash;
   victim->list.assign(t, t + n);
   build_plan(t, n, two_state, victim->plan);
@@ -381,7 +386,7 @@ int validate_tensors_cached(const opt8_tensor* t, int32_t n, bool two_state, Val
       if (e.valid && &e != victim && (!lru || e.stamp < lru->stamp)) lru = &e;
     if (!lru) break;
     total -= entry_bytes(*lru);
-    drop_entry(*lru);
+    drop_entry(*lru, true);
   }
   out = victim;
   return OPT8_OK;
@@ -492,13 +497,36 @@ int acquire_slot(DeviceState& ds, const Plan& plan, hipStream_t stream, Slot*& o
     }
   }
   ++ds.clock;
-  // an unused slot, a new one while there is room, else the least recently used
+  // the descriptors, then the block map (a function of them, so the key stays the list)
+  const size_t units = list.size() + map_units(plan);
+  size_t total = 0;
+  for (const Slot& o : ds.slots) total += o.cap * sizeof(DevTensor);
+  // the slot to write: the smallest unused one that holds the list; else a new one while the
+  // count and the byte budget allow; else the least recently used of those that hold it, its
+  // buffers reused, or failing that the least recently used of all (so a loop whose lists
+  // change every step rewrites slots instead of freeing and allocating device and pinned
+  // memory, which waits for the device, on every call)
   Slot* victim = nullptr;
-  for (Slot& s : ds.slots) {
-    if (!s.used) { victim = &s; break; }
-    if (!victim || s.stamp < victim->stamp) victim = &s;
+  for (Slot& o : ds.slots)
+    if (!o.used && o.cap >= units && (!victim || o.cap < victim->cap)) victim = &o;
+  if (!victim && ds.slots.size() < static_cast<size_t>(kSlotCache) &&
+      total + units * sizeof(DevTensor) <= cache_budget()) {
+    hipEvent_t ev = nullptr;
+    const hipError_t ce = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
+    if (ce != hipSuccess) return hip_fail(ce, "hipEventCreateWithFlags");
+    ds.slots.emplace_back();
+    victim = &ds.slots.back();
+    victim->done = ev;
   }
-  if ((!victim || victim->used) && ds.slots.size() < static_cast<size_t>(kSlotCache)) {
+  if (!victim) {
+    for (Slot& o : ds.slots)
+      if (o.cap >= units && (!victim || o.stamp < victim->stamp)) victim = &o;
+  }
+  if (!victim) {
+    for (Slot& o : ds.slots)
+      if (!victim || o.stamp < victim->stamp) victim = &o;
+  }
+  if (!victim) {   // no slot yet and the list alone exceeds the budget
     hipEvent_t ev = nullptr;
     const hipError_t ce = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
     if (ce != hipSuccess) return hip_fail(ce, "hipEventCreateWithFlags");
@@ -513,12 +541,10 @@ int acquire_slot(DeviceState& ds, const Plan& plan, hipStream_t stream, Slot*& o
   hipError_t e = hipEventSynchronize(s.done);
   if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize");
   s.used = false;
-  // the descriptors, then the block map (a function of them, so the key stays the list)
-  const size_t units = list.size() + map_units(plan);
   int rc = ensure_capacity(s, units);
   if (rc != OPT8_OK) return rc;
-  // over the byte budget: free the least recently used other slots
-  size_t total = 0;
+  // over the byte budget (a slot grew): free the least recently used other slots
+  total = 0;
   for (const Slot& o : ds.slots) total += o.cap * sizeof(DevTensor);
   while (total > cache_budget()) {
     Slot* lru = nullptr;
@@ -531,10 +557,15 @@ int acquire_slot(DeviceState& ds, const Plan& plan, hipStream_t stream, Slot*& o
   }
   s.key = list;   // may throw: nothing is queued yet
   std::memcpy(s.host, list.data(), list.size() * sizeof(DevTensor));
-  if (!plan.map.empty())
-    std::memcpy(s.host + list.size(), plan.map.data(), plan.map.size() * sizeof(uint32_t));
-  e = hipMemcpyAsync(s.dev, s.host, units * sizeof(DevTensor), hipMemcpyHostToDevice, stream);
+  e = hipMemcpyAsync(s.dev, s.host, list.size() * sizeof(DevTensor), hipMemcpyHostToDevice, stream);
   if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync(descriptors)");
+  const int k8 = static_cast<int>(Kind::k8bit);
+  e = launch_block_map(s.dev + plan.first[k8], plan.count[k8], reinterpret_cast<uint32_t*>(s.dev + list.size()),
+                       stream);
+  if (e != hipSuccess) {
+    (void)hipEventRecord(s.done, stream);   // the copy above is queued: a rewrite waits for it
+    return hip_fail(e, "block map launch");
+  }
   // until the step's launches record it again, the event follows the upload
   e = hipEventRecord(s.done, stream);
   if (e != hipSuccess) return hip_fail(e, "hipEventRecord");

@@ -445,16 +445,19 @@ int main() {
   {
     std::vector<std::vector<opt8_tensor>> groups;
     for (int l = 0; l < 40; ++l) groups.push_back({tensor(6200 + l, 4096, OPT8_STATE_8BIT, 0)});
+    const long fills = g.map_fills;
     for (auto& L : groups) CHECK(step(L, h1) == OPT8_OK);
+    CHECK(g.map_fills == fills + 40);         // each upload fills its block map on the device
     const long up = g.uploads, syncs = g.event_syncs;
     for (int round = 0; round < 2; ++round)
       for (auto& L : groups) CHECK(step(L, h1) == OPT8_OK);
-    CHECK(g.uploads == up && g.event_syncs == syncs);
+    CHECK(g.uploads == up && g.event_syncs == syncs && g.map_fills == fills + 40);
   }
 
   // the byte budget (16 MiB in this run) bounds both caches whatever their counts: lists with
-  // 4 MiB block maps stay a few at a time, the oldest is dropped, its slot freed only after
-  // the launches that read it (the check on reuse_violations below), and uploaded again
+  // 4 MiB block maps stay a few at a time, the oldest is dropped (its slot rewritten only after
+  // the launches that read it: the check on reuse_violations below) and uploaded again, and the
+  // slots' device memory stays within the budget plus one list
   {
     auto huge_tensor = [](int j) {   // 2^31 elements (2^20 blocks), its buffers 8 GiB apart
       opt8_tensor t;
@@ -472,9 +475,9 @@ int main() {
     };
     std::vector<std::vector<opt8_tensor>> big;
     for (int l = 0; l < 6; ++l) big.push_back({huge_tensor(l)});
-    const long frees = g.frees;
     for (auto& L : big) CHECK(step(L, h1) == OPT8_OK);
-    CHECK(g.frees > frees);                   // slots were freed to stay within the budget
+    const size_t list_bytes = (size_t(1) << 20) * 4 + 1024;   // one list: its map and descriptor
+    CHECK(g.device_bytes <= (size_t(16) << 20) + 2 * list_bytes);
     const long up = g.uploads;
     CHECK(step(big[5], h1) == OPT8_OK);       // the newest stays
     CHECK(g.uploads == up);
@@ -483,6 +486,31 @@ int main() {
     g.launches.clear();
     CHECK(step(big[0], h1) == OPT8_OK);
     CHECK(g.uploads == up + 1 && g.launches.size() == 1 && g.launches[0].ok);
+  }
+
+  // lists whose buffers move every step (every call a miss): once the budget is full, slots are
+  // rewritten, not freed and allocated again (freeing device memory waits for the device)
+  {
+    auto moved = [](int k) {   // the same 2^31-element tensor, its gradient 16 bytes further each time
+      opt8_tensor t;
+      std::memset(&t, 0, sizeof t);
+      const uintptr_t b = (uintptr_t(1) << 45);
+      t.param = reinterpret_cast<uint16_t*>(b);
+      t.grad = reinterpret_cast<const uint16_t*>(b + (uintptr_t(1) << 33) + 16 * uintptr_t(k));
+      t.m = reinterpret_cast<void*>(b + (uintptr_t(2) << 33));
+      t.v = reinterpret_cast<void*>(b + (uintptr_t(3) << 33));
+      t.absmax_m = reinterpret_cast<float*>(b + (uintptr_t(4) << 33));
+      t.absmax_v = reinterpret_cast<float*>(b + (uintptr_t(5) << 33));
+      t.numel = int64_t(1) << 31;
+      t.mode = OPT8_STATE_8BIT;
+      return std::vector<opt8_tensor>{t};
+    };
+    for (int k = 0; k < 8; ++k) CHECK(step(moved(k), h1) == OPT8_OK);
+    const long mallocs = g.mallocs, frees = g.frees, up = g.uploads;
+    for (int k = 8; k < 24; ++k) CHECK(step(moved(k), h1) == OPT8_OK);
+    CHECK(g.uploads == up + 16);                        // every call a miss, uploaded
+    CHECK(g.mallocs == mallocs && g.frees == frees);    // into slots that are rewritten
+    CHECK(g.device_bytes <= (size_t(16) << 20) + 2 * ((size_t(1) << 22) + 1024));
   }
   CHECK(g.reuse_violations == 0);   // no staging buffer was rewritten or freed under its copy
 

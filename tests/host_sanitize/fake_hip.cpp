@@ -12,6 +12,7 @@
 #include <vector>
 
 #include "fake_hip.h"
+#include "opt8_map.h"
 
 namespace fake {
 State g;
@@ -67,10 +68,19 @@ hipError_t hipMalloc(void** ptr, size_t size) {
   if (g.fail_malloc) return hipErrorOutOfMemory;
   *ptr = std::malloc(size);
   ++g.mallocs;
+  g.device_live.emplace_back(*ptr, size);
+  g.device_bytes += size;
+  g.device_bytes_peak = std::max(g.device_bytes_peak, g.device_bytes);
   return hipSuccess;
 }
 
 hipError_t hipFree(void* ptr) {
+  for (size_t i = 0; i < g.device_live.size(); ++i)
+    if (g.device_live[i].first == ptr) {
+      g.device_bytes -= g.device_live[i].second;
+      g.device_live.erase(g.device_live.begin() + static_cast<long>(i));
+      break;
+    }
   std::free(ptr);
   ++g.frees;
   return hipSuccess;
@@ -164,6 +174,15 @@ hipError_t launch_step(Kind kind, int algo, const DevTensor* list, int n, int64_
 }
 
 int occupancy_per_cu(Kind, int, bool) { return 3; }
+
+// The block-map fill, on the host: the stand-in's device memory is host memory, so ASan
+// checks that the map fits the slot the library reserved for it.
+hipError_t launch_block_map(const DevTensor* list, int n, uint32_t* map, hipStream_t) {
+  ++g.map_fills;
+  for (int e = 0; e < n; ++e)
+    for (uint32_t i = 0; i < list[e].nblocks; ++i) map[list[e].block_begin + i] = static_cast<uint32_t>(e);
+  return hipSuccess;
+}
 
 // The stand-in for the device's descriptor scratch: a static host array of
 // the same size, so ASan checks every descriptor written into it.

@@ -24,7 +24,9 @@ struct State {
   bool capturing = false;
   bool fail_malloc = false;
   long mallocs = 0, frees = 0, uploads = 0, events = 0, event_syncs = 0, stream_waits = 0;
-  long host_mallocs = 0, scratch_queries = 0;
+  long host_mallocs = 0, scratch_queries = 0, map_fills = 0;
+  std::vector<std::pair<void*, size_t>> device_live;   // hipMalloc'd buffers not yet freed
+  size_t device_bytes = 0, device_bytes_peak = 0;
   const void* scratch_lo = nullptr;   // extent of the stand-in descriptor scratch
   const void* scratch_hi = nullptr;
   long table_uploads = 0;
