@@ -63,7 +63,7 @@ def test_group_counter_above_32_bits(algo, state_round):
     sets, states = [], []
     tid = 0
     for base in BASES:
-        for mode, n in ((M8, 3 * 2048 + 100), (MB, 2 * 2048 + 9), (MF, 1000)):
+        for mode, n in ((M8, 3 * 2048 + 100), (M8, 2048 + 40), (MB, 2 * 2048 + 9), (MF, 1000)):
             p, g = _bf16(rng, n, 0.02), _bf16(rng, n, 1e-3)
             m, v, am, av = _state(mode, n, tid, one_state)
             sets.append(DevTensorSet(mode, p, g, m, v, am, av, tensor_id=500 + tid, index_base=base))
