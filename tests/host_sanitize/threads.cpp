@@ -1,12 +1,12 @@
 // Concurrent callers of libopt8's host code, linked with the host-only HIP
 // stand-in and built with ThreadSanitizer by tests/test_host_sanitizers.py.
-// Several threads step at once, each on a stream of its own: a list they all
-// share, lists of their own that fit the caches, fresh lists every few steps
-// (cache misses, slot rewrites, growth and releases under a 1 MiB byte budget) and
-// the one-state rules; one of them also calls the entry point without
-// allocation.  Every call must succeed, every launch must carry a well-formed
-// descriptor list, and no staging buffer may be rewritten under a pending
-// copy.  Prints "all thread checks passed".
+// Several threads step at once: a list they all share, on one stream they all
+// use; on a stream of its own, each thread's lists that fit the caches under
+// all three rules, and fresh lists every few steps (cache misses, slot
+// rewrites, growth and releases under a 1 MiB byte budget); one thread also
+// calls the entry point without allocation.  Every call must succeed, every
+// launch must carry a well-formed descriptor list, and no staging buffer may
+// be rewritten under a pending copy.  Prints "all thread checks passed".
 #include <atomic>
 #include <cstdint>
 #include <cstdio>
@@ -80,12 +80,14 @@ constexpr int kSteps = 200;
 
 void worker(int t, const std::vector<opt8_tensor>* shared) {
   void* stream = reinterpret_cast<void*>(uintptr_t(0x1000) + uintptr_t(t) * 0x100);
+  void* shared_stream = reinterpret_cast<void*>(uintptr_t(0x900));
   std::vector<std::vector<opt8_tensor>> own;
   for (int k = 0; k < 6; ++k) own.push_back(make_list(1000 * (t + 1) + 10 * k, 3 + k));
   for (int s = 0; s < kSteps; ++s) {
     const opt8_hparams h = hparams(s + 1);
     const int32_t ns = static_cast<int32_t>(shared->size());
-    expect_ok(opt8_adamw_step(shared->data(), ns, &h, stream), "shared list", t, s);
+    // the shared buffers on one stream that all threads use (different streams need disjoint buffers)
+    expect_ok(opt8_adamw_step(shared->data(), ns, &h, shared_stream), "shared list", t, s);
     const auto& mine = own[s % own.size()];
     const int32_t nm = static_cast<int32_t>(mine.size());
     if (s % 3 == 1) expect_ok(opt8_lion_step(mine.data(), nm, &h, stream), "lion", t, s);
