@@ -1693,7 +1693,7 @@ int occupancy_short_algo(int algo) {
 template <Kind K, int A, bool SS>
 hipError_t launch_kind(const DevTensor* list, int n, int64_t total_blocks, const StepScalars& sc,
                        hipStream_t stream, int num_cu, int resident, int range_ok, const uint32_t* map) {
-  const int64_t grid = launch_groups<K, A>(total_blocks, num_cu, resident);
+  const int64_t grid = launch_groups<K, A, SS>(total_blocks, num_cu, resident);
   hipLaunchKernelGGL((step_kernel<K, A, SS>), dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0, stream,
                      list, n, total_blocks, sc, range_ok, map);
   return hipGetLastError();

@@ -523,6 +523,8 @@ int main() {
     CHECK((opt8::launch_groups<Kind::k8bit, opt8::kAdamW>(3251174, 256, 768) == 192 * 256));
     CHECK((opt8::launch_groups<Kind::k8bit, opt8::kLion>(3251174, 256, 512) == 96 * 256));
     CHECK((opt8::launch_groups<Kind::k8bit, opt8::kMomentum>(3251174, 256, 512) == 384 * 256));
+    CHECK((opt8::launch_groups<Kind::k8bit, opt8::kMomentum, true>(3251174, 256, 512) == 96 * 256));
+    CHECK((opt8::launch_groups<Kind::k8bit, opt8::kAdamW, true>(3251174, 256, 768) == 192 * 256));
     CHECK((opt8::launch_groups<Kind::kBf16, opt8::kAdamW>(1294710, 256, 1280) == 384 * 256));
     CHECK((opt8::launch_groups<Kind::k8bit, opt8::kAdamW>(60000, 256, 768) == 60000 / 8 / 32 * 32));
     CHECK((opt8::launch_groups<Kind::kFp32, opt8::kAdamW>(30000, 256, 1280) == 7500 / 32 * 32));
