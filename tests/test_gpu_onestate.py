@@ -31,11 +31,11 @@ def device():
     opt8.opt8_init_codebooks()
 
 
-def _hp(algo, step, seed=0x5EED, param_round=oracle.ROUND_STOCHASTIC, lr=None, wd=0.1):
+def _hp(algo, step, seed=0x5EED, param_round=oracle.ROUND_STOCHASTIC, lr=None, wd=0.1, state_round=0):
     if lr is None:
         lr = 1e-4 if algo == LION else 1e-2
     return oracle.Hparams(lr=lr, beta1=0.9, beta2=0.99, eps=1e-8, weight_decay=wd, step=step,
-                          seed=seed, param_round=param_round)
+                          seed=seed, param_round=param_round, state_round=state_round)
 
 
 def _rand_bf16(rng, n, sigma):
@@ -181,20 +181,24 @@ def test_non_finite_gradients(algo):
     assert np.array_equal(got[0][4096:], want[0][4096:])
 
 
+@pytest.mark.parametrize("state_round", [0, 1])
 @pytest.mark.parametrize("algo", ALGOS)
-def test_full_size_6p7b_sampled_blocks(algo):
+def test_full_size_6p7b_sampled_blocks(algo, state_round):
     """The 6.7B-shaped list (388 tensors, 6,658,404,352 elements, one 8-bit state) stepped in
-    one call, checked on two random blocks plus the first and last block of every tensor."""
+    one call, with the state rounded to nearest or stochastically (each rule and rounding has
+    its own launch size at this length), checked on two random blocks plus the first and last
+    block of every tensor."""
     w = shapes.get("gptneo-6.7b")
     log(f"{NAMES[algo]}: building {len(w.tensors)} tensors, {w.numel} elements on the device")
     lst = build_list(w, one_state=True)
     torch.cuda.synchronize()
     blocks = sample_blocks(lst, 2, np.random.default_rng(2))
     before = snapshot(lst, blocks)
-    hp = _hp(algo, 2, seed=w.seed)
+    hp = _hp(algo, 2, seed=w.seed, state_round=state_round)
     arr = descriptors(lst)
     fn = opt8.opt8_lion_step if algo == LION else opt8.opt8_momentum_step
-    fn(arr, opt8.make_hparams(hp.lr, hp.beta1, hp.beta2, hp.eps, hp.weight_decay, hp.step, hp.seed))
+    fn(arr, opt8.make_hparams(hp.lr, hp.beta1, hp.beta2, hp.eps, hp.weight_decay, hp.step, hp.seed,
+                              hp.param_round, hp.state_round))
     torch.cuda.synchronize()
     after = snapshot(lst, blocks)
     stats = {}
@@ -204,6 +208,7 @@ def test_full_size_6p7b_sampled_blocks(algo):
                                          tensor_id=t["tid"], index_base=b * 2048)
         compare_state(f"{NAMES[algo]}/t{t['tid']}/b{b}", [y["p"], y["m"], None, y["am"], None],
                       [want[0], want[1], None, want[2], None], t["mode"], stats)
-    log(f"{NAMES[algo]} 6.7B: {len(blocks)} sampled blocks, mismatches {sum(stats.values())}")
+    log(f"{NAMES[algo]} 6.7B, state rounding {state_round}: {len(blocks)} sampled blocks, "
+        f"mismatches {sum(stats.values())}")
     del lst, arr
     torch.cuda.empty_cache()
